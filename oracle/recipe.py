@@ -1,0 +1,86 @@
+"""Recipe defaults and validation.
+
+Oracle module (test infrastructure only; see the package docstring).
+
+From "BitDecoding-FP4 evaluation/config.py":
+
+* RECIPE turns on the two-term query, underflow-aware probability scaling
+  with c = 8 and tau = "calibrate", and key smoothing, Hadamard rotation and
+  adaptive block-scale search for keys;
+* ``recipe_additional_config`` maps that to key scale mode four_six (amax6
+  when the search is off), value and query amax6, two query terms (one when
+  the dual residual is off) and rotation hadamard (none when off);
+* ``probability_environment``: scaling disabled gives P mode amax6; c must be
+  1 or 8; tau "calibrate" is refused outside calibration; otherwise tau must
+  be a finite number in [0, 448];
+* KV_MODES ``bitdecoding-nvfp4`` keeps a 16-token BF16 sink;
+  ``bitdecoding-mxfp4`` uses mxfp4_search with the same sink, two query terms
+  and Hadamard rotation.
+
+Here tau = NaN stands for "calibrate".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+from . import quant as Q
+
+
+class RecipeError(ValueError):
+    pass
+
+
+class UncalibratedError(RecipeError):
+    pass
+
+
+@dataclass(frozen=True)
+class Recipe:
+    sink_tokens: int = 16
+    rotation: bool = True
+    key_smoothing: bool = True
+    scale_mode_k: str = Q.FOUR_SIX
+    scale_mode_v: str = Q.AMAX6
+    scale_mode_q: str = Q.AMAX6
+    scale_mode_p: str = Q.AMAX2_OR_AMAX6
+    query_terms: int = 2
+    c: int = 8
+    tau: float = float("nan")
+
+    def with_(self, **kw) -> "Recipe":
+        return replace(self, **kw)
+
+
+def nvfp4_default() -> Recipe:
+    """The bitdecoding-nvfp4 recipe, tau still to be calibrated."""
+    return Recipe()
+
+
+def mxfp4_default() -> Recipe:
+    """The bitdecoding-mxfp4 recipe, tau still to be calibrated."""
+    return Recipe(scale_mode_k=Q.MXFP4_SEARCH, scale_mode_v=Q.MXFP4_SEARCH,
+                  scale_mode_q=Q.MXFP4_SEARCH)
+
+
+def validate(r: Recipe) -> None:
+    """Raise RecipeError / UncalibratedError for recipes the method refuses."""
+    if r.scale_mode_p == Q.AMAX2_OR_AMAX6:
+        if r.c not in (1, 8):
+            raise RecipeError("the probability kernel supports c=1 or c=8")
+        if isinstance(r.tau, float) and math.isnan(r.tau):
+            raise UncalibratedError(
+                "tau must be calibrated before evaluation or throughput measurement")
+        if not isinstance(r.tau, (int, float)) or not math.isfinite(r.tau) or not 0 <= r.tau <= 448:
+            raise RecipeError("tau must be 'calibrate' or a finite number between 0 and 448")
+    elif r.scale_mode_p not in (Q.AMAX6, Q.NONE):
+        raise RecipeError(f"bad probability scale mode {r.scale_mode_p!r}")
+    if r.query_terms not in (1, 2):
+        raise RecipeError("query_terms is 1 or 2")
+    if r.sink_tokens < 0 or r.sink_tokens >= 128 or r.sink_tokens % 16:
+        raise RecipeError("sink_tokens is a multiple of 16 in [0, 112]")
+    for m, ok in ((r.scale_mode_k, (Q.FOUR_SIX, Q.AMAX6, Q.MXFP4_SEARCH, Q.NONE)),
+                  (r.scale_mode_v, (Q.AMAX6, Q.MXFP4_SEARCH, Q.NONE)),
+                  (r.scale_mode_q, (Q.AMAX6, Q.MXFP4_SEARCH, Q.NONE))):
+        if m not in ok:
+            raise RecipeError(f"bad scale mode {m!r}")
