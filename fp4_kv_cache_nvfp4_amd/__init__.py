@@ -1,2 +1,249 @@
 """NVFP4 / MXFP4 KV-cache page quantization and paged FP4 decode attention
-for AMD MI355X (gfx950)."""
+for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``lib/libbdfp4.so`` (declared in
+``include/bdfp4.h``). Each function has the name of its C entry point without
+the ``bdfp4_`` prefix and only marshals arguments: tensors become device
+pointers, the current torch stream becomes the launch stream, and a negative
+status becomes a :class:`Bdfp4Error`. All computation happens in the HIP
+kernels; if the library is not built, loading fails with an error (there is
+no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libbdfp4.so")
+
+OK, E_INVALID, E_UNCALIBRATED, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
+SCALE_NONE, SCALE_AMAX6, SCALE_FOUR_SIX, SCALE_MXFP4_SEARCH, SCALE_AMAX2_OR_AMAX6 = 0, 1, 2, 3, 4
+
+
+class Bdfp4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+class Recipe(ctypes.Structure):
+    _fields_ = [
+        ("sink_tokens", ctypes.c_int32),
+        ("rotation", ctypes.c_int32),
+        ("key_smoothing", ctypes.c_int32),
+        ("scale_mode_k", ctypes.c_int32),
+        ("scale_mode_v", ctypes.c_int32),
+        ("scale_mode_q", ctypes.c_int32),
+        ("scale_mode_p", ctypes.c_int32),
+        ("query_terms", ctypes.c_int32),
+        ("c", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+    ]
+
+    def replace(self, **kw) -> "Recipe":
+        r = Recipe()
+        ctypes.pointer(r)[0] = self
+        for k, v in kw.items():
+            setattr(r, k, v)
+        return r
+
+    @property
+    def mx(self) -> bool:
+        return self.scale_mode_k == SCALE_MXFP4_SEARCH
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+    ]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp4_kv_cache_nvfp4_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    RP = ctypes.POINTER(Recipe)
+    CP = ctypes.POINTER(Cache)
+    sig = {
+        "bdfp4_recipe_default_nvfp4": [RP],
+        "bdfp4_recipe_default_mxfp4": [RP],
+        "bdfp4_recipe_validate": [RP],
+        "bdfp4_cache_bytes": [RP, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+        "bdfp4_quantize_pages": [RP, CP, P, P, P, I32, P, P],
+        "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
+        "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
+        "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
+        "bdfp4_bf16_decode_attention": [P, I32, I32, I32, P, P, I32, P, I32, P, I32, F32, I32, P, SZ, P, P],
+        "bdfp4_quantize_rows": [P, I32, P, I32, I32, I32, P, P, P],
+        "bdfp4_quantize_p_blocks": [P, I32, I32, F32, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int32
+    L.bdfp4_status_string.argtypes = [ctypes.c_int32]
+    L.bdfp4_status_string.restype = ctypes.c_char_p
+    L.bdfp4_last_error.argtypes = []
+    L.bdfp4_last_error.restype = ctypes.c_char_p
+    _lib_handle = L
+    return L
+
+
+def status_string(s: int) -> str:
+    return lib().bdfp4_status_string(s).decode()
+
+
+def _check(s: int) -> None:
+    if s != OK:
+        raise Bdfp4Error(s, lib().bdfp4_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+# ---------------------------------------------------------------- recipe
+
+def recipe_default_nvfp4(tau: float = math.nan) -> Recipe:
+    r = Recipe()
+    _check(lib().bdfp4_recipe_default_nvfp4(ctypes.byref(r)))
+    r.tau = tau
+    return r
+
+
+def recipe_default_mxfp4(tau: float = math.nan) -> Recipe:
+    r = Recipe()
+    _check(lib().bdfp4_recipe_default_mxfp4(ctypes.byref(r)))
+    r.tau = tau
+    return r
+
+
+def recipe_validate(r: Recipe) -> None:
+    _check(lib().bdfp4_recipe_validate(ctypes.byref(r)))
+
+
+def cache_bytes(r: Recipe, num_pages: int, num_kv_heads: int):
+    out = [ctypes.c_size_t() for _ in range(4)]
+    _check(lib().bdfp4_cache_bytes(ctypes.byref(r), num_pages, num_kv_heads, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+@dataclass
+class PagedCache:
+    """The four cache arrays as uint8 device tensors [pages, heads, bytes]."""
+    k_codes: object
+    k_scales: object
+    v_codes: object
+    v_scales: object
+    num_pages: int
+    num_kv_heads: int
+
+    @classmethod
+    def allocate(cls, r: Recipe, num_pages: int, num_kv_heads: int, device="cuda"):
+        import torch
+        kc, ks, vc, vs = cache_bytes(r, num_pages, num_kv_heads)
+        z = lambda n: torch.zeros((num_pages, num_kv_heads, n // max(1, num_pages * num_kv_heads)),
+                                  dtype=torch.uint8, device=device)
+        return cls(z(kc), z(ks), z(vc), z(vs), num_pages, num_kv_heads)
+
+    def struct(self) -> Cache:
+        return Cache(_ptr(self.k_codes), _ptr(self.k_scales), _ptr(self.v_codes), _ptr(self.v_scales),
+                     self.num_pages, self.num_kv_heads, 128, 128)
+
+
+# ---------------------------------------------------------------- writer
+
+def quantize_pages(r: Recipe, cache: PagedCache, k, v, page_ids, key_shift=None, stream=None) -> None:
+    n_pages = 0 if page_ids is None else int(page_ids.numel())
+    c = cache.struct()
+    _check(lib().bdfp4_quantize_pages(ctypes.byref(r), ctypes.byref(c), _ptr(k), _ptr(v), _ptr(page_ids),
+                                      n_pages, _ptr(key_shift), _stream(stream)))
+
+
+# ---------------------------------------------------------------- decode
+
+def decode_plan(batch: int, num_kv_heads: int, max_seq_len: int, pages_per_partition: int = 0):
+    ppp, parts = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().bdfp4_decode_plan(batch, num_kv_heads, max_seq_len, pages_per_partition,
+                                   ctypes.byref(ppp), ctypes.byref(parts)))
+    return ppp.value, parts.value
+
+
+def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                          pages_per_partition: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().bdfp4_decode_workspace_size(batch, num_q_heads, num_kv_heads, max_seq_len,
+                                             pages_per_partition, ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """Zero-filled workspace (the ticket words must start at zero)."""
+    import torch
+    return torch.zeros(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)
+
+
+def decode_attention(r: Recipe, cache: PagedCache, q, block_tables, seq_lens, max_seq_len: int,
+                     sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale: float,
+                     pages_per_partition: int, workspace, out, stream=None) -> None:
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    c = cache.struct()
+    _check(lib().bdfp4_decode_attention(
+        ctypes.byref(r), ctypes.byref(c), _ptr(q), B, Hq, _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(seq_lens), int(max_seq_len), _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v),
+        _ptr(key_shift), float(softmax_scale), int(pages_per_partition), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _ptr(out), _stream(stream)))
+
+
+def bf16_decode_attention(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len: int,
+                          softmax_scale: float, pages_per_partition: int, workspace, out, stream=None) -> None:
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    _check(lib().bdfp4_bf16_decode_attention(
+        _ptr(q), B, Hq, int(k_pages.shape[1]), _ptr(k_pages), _ptr(v_pages), int(k_pages.shape[0]),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+        float(softmax_scale), int(pages_per_partition), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------- codec debug entries
+
+def quantize_rows(rows, shift, rotation: int, mode: int, terms: int, codes, scales, stream=None) -> None:
+    _check(lib().bdfp4_quantize_rows(_ptr(rows), int(rows.shape[0]) if rows is not None else 0, _ptr(shift),
+                                     rotation, mode, terms, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def quantize_p_blocks(pp, mode: int, tau: float, codes, scales, stream=None) -> None:
+    _check(lib().bdfp4_quantize_p_blocks(_ptr(pp), int(pp.shape[0]) if pp is not None else 0, mode, float(tau),
+                                         _ptr(codes), _ptr(scales), _stream(stream)))

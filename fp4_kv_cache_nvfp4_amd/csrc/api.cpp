@@ -1,0 +1,430 @@
+// Host side of the bdfp4 C ABI: recipe defaults and validation, sizes, the
+// decode split plan, and the launches. Every check runs before anything is
+// enqueued; a failing check returns its status and records a message.
+//
+// Validation rules follow "BitDecoding-FP4 evaluation/config.py":
+// probability_environment (c in {1, 8}; tau "calibrate" refused outside
+// calibration; tau finite in [0, 448]) and the KV_MODES entries
+// bitdecoding-nvfp4 / bitdecoding-mxfp4 (sink 16, scale modes, query terms).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bdfp4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bdfp4_status fail(bdfp4_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bdfp4_status ok() {
+  g_err[0] = '\0';
+  return BDFP4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_nv_kv(const bdfp4_recipe* r) {
+  return (r->scale_mode_k == BDFP4_SCALE_FOUR_SIX || r->scale_mode_k == BDFP4_SCALE_AMAX6) &&
+         r->scale_mode_v == BDFP4_SCALE_AMAX6;
+}
+
+bool is_mx_kv(const bdfp4_recipe* r) {
+  return r->scale_mode_k == BDFP4_SCALE_MXFP4_SEARCH && r->scale_mode_v == BDFP4_SCALE_MXFP4_SEARCH;
+}
+
+// The fields the page writer uses: rotation, smoothing, K and V modes.
+bdfp4_status check_kv_recipe(const bdfp4_recipe* r) {
+  if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
+  if (r->rotation != 0 && r->rotation != 1) return fail(BDFP4_E_INVALID, "rotation must be 0 or 1");
+  if (r->key_smoothing != 0 && r->key_smoothing != 1)
+    return fail(BDFP4_E_INVALID, "key_smoothing must be 0 or 1");
+  const int km = r->scale_mode_k, vm = r->scale_mode_v;
+  if (km != BDFP4_SCALE_FOUR_SIX && km != BDFP4_SCALE_AMAX6 && km != BDFP4_SCALE_MXFP4_SEARCH &&
+      km != BDFP4_SCALE_NONE)
+    return fail(BDFP4_E_INVALID, "scale_mode_k %d is not a key scale mode", km);
+  if (vm != BDFP4_SCALE_AMAX6 && vm != BDFP4_SCALE_MXFP4_SEARCH && vm != BDFP4_SCALE_NONE)
+    return fail(BDFP4_E_INVALID, "scale_mode_v %d is not a value scale mode", vm);
+  if (!is_nv_kv(r) && !is_mx_kv(r))
+    return fail(BDFP4_E_UNSUPPORTED,
+                "K/V scale modes (%d, %d): this build has kernels for (four_six|amax6, amax6) and "
+                "(mxfp4_search, mxfp4_search)", km, vm);
+  return BDFP4_OK;
+}
+
+bdfp4_status check_recipe(const bdfp4_recipe* r) {
+  bdfp4_status s = check_kv_recipe(r);
+  if (s != BDFP4_OK) {
+    // an invalid K/V field outranks an unsupported combination only if the
+    // probability settings are themselves fine; report the first problem
+    if (s == BDFP4_E_INVALID) return s;
+  }
+  if (r->sink_tokens < 0 || r->sink_tokens > 112 || (r->sink_tokens % 16) != 0)
+    return fail(BDFP4_E_INVALID, "sink_tokens must be a multiple of 16 in [0, 112], got %d",
+                r->sink_tokens);
+  if (r->query_terms != 1 && r->query_terms != 2)
+    return fail(BDFP4_E_INVALID, "query_terms must be 1 or 2, got %d", r->query_terms);
+  const int qm = r->scale_mode_q, pm = r->scale_mode_p;
+  if (qm != BDFP4_SCALE_AMAX6 && qm != BDFP4_SCALE_MXFP4_SEARCH && qm != BDFP4_SCALE_NONE)
+    return fail(BDFP4_E_INVALID, "scale_mode_q %d is not a query scale mode", qm);
+  if (pm == BDFP4_SCALE_AMAX2_OR_AMAX6) {
+    if (r->c != 1 && r->c != 8) return fail(BDFP4_E_INVALID, "the probability kernel supports c=1 or c=8");
+    if (isnan(r->tau))
+      return fail(BDFP4_E_UNCALIBRATED, "tau must be calibrated before evaluation or throughput measurement");
+    if (!isfinite(r->tau) || r->tau < 0.0f || r->tau > 448.0f)
+      return fail(BDFP4_E_INVALID, "tau must be 'calibrate' or a finite number between 0 and 448");
+  } else if (pm == BDFP4_SCALE_AMAX6) {
+    if (r->c != 1 && r->c != 8) return fail(BDFP4_E_INVALID, "the probability kernel supports c=1 or c=8");
+  } else if (pm == BDFP4_SCALE_NONE) {
+    return fail(BDFP4_E_UNSUPPORTED, "unquantized probabilities have no FP4 decode kernel");
+  } else {
+    return fail(BDFP4_E_INVALID, "scale_mode_p %d is not a probability scale mode", pm);
+  }
+  if (s != BDFP4_OK) return s;
+  if (qm == BDFP4_SCALE_NONE)
+    return fail(BDFP4_E_UNSUPPORTED, "an unquantized query has no FP4 decode kernel");
+  if (is_nv_kv(r) && qm != BDFP4_SCALE_AMAX6)
+    return fail(BDFP4_E_UNSUPPORTED, "NVFP4 pages take an amax6 query in this build");
+  if (is_mx_kv(r) && qm != BDFP4_SCALE_MXFP4_SEARCH)
+    return fail(BDFP4_E_UNSUPPORTED, "MXFP4 pages take an mxfp4_search query in this build");
+  return BDFP4_OK;
+}
+
+bdfp4_status check_cache(const bdfp4_cache* c) {
+  if (c == nullptr) return fail(BDFP4_E_INVALID, "cache is NULL");
+  if (c->head_dim != 128 || c->block_size != 128)
+    return fail(BDFP4_E_UNSUPPORTED, "head_dim and block_size must be 128 (got %d, %d)", c->head_dim,
+                c->block_size);
+  if (c->num_pages < 1 || c->num_kv_heads < 1)
+    return fail(BDFP4_E_INVALID, "num_pages and num_kv_heads must be positive");
+  if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales)
+    return fail(BDFP4_E_INVALID, "cache array pointer is NULL");
+  if (!aligned16(c->k_codes) || !aligned16(c->k_scales) || !aligned16(c->v_codes) || !aligned16(c->v_scales))
+    return fail(BDFP4_E_INVALID, "cache arrays must be 16-byte aligned");
+  return BDFP4_OK;
+}
+
+int32_t auto_ppp(int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  const int64_t n_full = max_seq_len / 128;
+  const int64_t work = (int64_t)batch * hkv * n_full;
+  int64_t ppp = (work + 1023) / 1024;     // about 1024 FP4 workgroups (4 per CU)
+  if (ppp < 1) ppp = 1;
+  if (ppp > 16) ppp = 16;
+  return (int32_t)ppp;
+}
+
+constexpr int32_t kMaxPpp = 16;
+
+bdfp4_status plan(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_in, int32_t* ppp,
+                  int32_t* parts) {
+  if (batch < 1 || hkv < 1) return fail(BDFP4_E_INVALID, "batch and num_kv_heads must be positive");
+  if (max_seq_len < 1) return fail(BDFP4_E_INVALID, "max_seq_len must be positive");
+  if (ppp_in < 0 || ppp_in > kMaxPpp)
+    return fail(BDFP4_E_INVALID, "pages_per_partition must be in [0, %d], got %d", kMaxPpp, ppp_in);
+  if ((int64_t)batch * hkv > bdfp4::kMaxSeqHeads)
+    return fail(BDFP4_E_UNSUPPORTED, "batch * num_kv_heads must be <= %d", bdfp4::kMaxSeqHeads);
+  *ppp = ppp_in ? ppp_in : auto_ppp(batch, hkv, max_seq_len);
+  const int32_t n_full = max_seq_len / 128;
+  *parts = (n_full + *ppp - 1) / *ppp;
+  return BDFP4_OK;
+}
+
+size_t workspace_bytes(int32_t batch, int32_t hkv, int32_t parts) {
+  return bdfp4::kCounterBytes +
+         (size_t)batch * hkv * (size_t)(parts + 1) * bdfp4::kPartialFloats * sizeof(float);
+}
+
+bdfp4_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BDFP4_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bdfp4_status_string(int32_t s) {
+  switch (s) {
+    case BDFP4_OK: return "BDFP4_OK";
+    case BDFP4_E_INVALID: return "BDFP4_E_INVALID";
+    case BDFP4_E_UNCALIBRATED: return "BDFP4_E_UNCALIBRATED";
+    case BDFP4_E_UNSUPPORTED: return "BDFP4_E_UNSUPPORTED";
+    case BDFP4_E_WORKSPACE: return "BDFP4_E_WORKSPACE";
+    case BDFP4_E_HIP: return "BDFP4_E_HIP";
+    default: return "BDFP4_E_UNKNOWN";
+  }
+}
+
+const char* bdfp4_last_error(void) { return g_err; }
+
+bdfp4_status bdfp4_recipe_default_nvfp4(bdfp4_recipe* r) {
+  if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
+  r->sink_tokens = 16;
+  r->rotation = 1;
+  r->key_smoothing = 1;
+  r->scale_mode_k = BDFP4_SCALE_FOUR_SIX;
+  r->scale_mode_v = BDFP4_SCALE_AMAX6;
+  r->scale_mode_q = BDFP4_SCALE_AMAX6;
+  r->scale_mode_p = BDFP4_SCALE_AMAX2_OR_AMAX6;
+  r->query_terms = 2;
+  r->c = 8;
+  r->tau = NAN;
+  return ok();
+}
+
+bdfp4_status bdfp4_recipe_default_mxfp4(bdfp4_recipe* r) {
+  bdfp4_status s = bdfp4_recipe_default_nvfp4(r);
+  if (s != BDFP4_OK) return s;
+  r->scale_mode_k = r->scale_mode_v = r->scale_mode_q = BDFP4_SCALE_MXFP4_SEARCH;
+  return ok();
+}
+
+bdfp4_status bdfp4_recipe_validate(const bdfp4_recipe* r) {
+  if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
+  bdfp4_status s = check_recipe(r);
+  return s == BDFP4_OK ? ok() : s;
+}
+
+bdfp4_status bdfp4_cache_bytes(const bdfp4_recipe* r, int32_t num_pages, int32_t num_kv_heads,
+                               size_t* k_codes, size_t* k_scales, size_t* v_codes, size_t* v_scales) {
+  bdfp4_status s = check_kv_recipe(r);
+  if (s != BDFP4_OK) return s;
+  if (num_pages < 0 || num_kv_heads < 1) return fail(BDFP4_E_INVALID, "bad page or head count");
+  if (!k_codes || !k_scales || !v_codes || !v_scales) return fail(BDFP4_E_INVALID, "NULL output");
+  const size_t ph = (size_t)num_pages * num_kv_heads;
+  const bool kmx = r->scale_mode_k == BDFP4_SCALE_MXFP4_SEARCH;
+  const bool vmx = r->scale_mode_v == BDFP4_SCALE_MXFP4_SEARCH;
+  *k_codes = ph * 8192;
+  *v_codes = ph * 8192;
+  *k_scales = ph * (kmx ? 512 : 1024);
+  *v_scales = ph * (vmx ? 512 : 1024);
+  return ok();
+}
+
+bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* k_bf16,
+                                  const void* v_bf16, const int32_t* page_ids, int32_t n_pages,
+                                  const float* key_shift, void* stream) {
+  bdfp4_status s = check_kv_recipe(r);
+  if (s != BDFP4_OK) return s;
+  if ((s = check_cache(cache)) != BDFP4_OK) return s;
+  if (n_pages < 0) return fail(BDFP4_E_INVALID, "n_pages must be >= 0");
+  if (n_pages == 0) return ok();
+  if (!k_bf16 || !v_bf16 || !page_ids) return fail(BDFP4_E_INVALID, "NULL input pointer");
+  if (!aligned16(k_bf16) || !aligned16(v_bf16)) return fail(BDFP4_E_INVALID, "k/v must be 16-byte aligned");
+  if (r->key_smoothing && key_shift == nullptr)
+    return fail(BDFP4_E_INVALID, "key_smoothing needs key_shift (the key-mean sidecar)");
+  if (!r->key_smoothing && key_shift != nullptr)
+    return fail(BDFP4_E_INVALID, "key_shift given but key_smoothing is off");
+  if (key_shift && !aligned16(key_shift)) return fail(BDFP4_E_INVALID, "key_shift must be 16-byte aligned");
+  if ((int64_t)n_pages * cache->num_kv_heads > 0x7FFFFFFF)
+    return fail(BDFP4_E_INVALID, "too many pages in one call");
+  bdfp4::WriterLaunch L;
+  L.k = k_bf16;
+  L.v = v_bf16;
+  L.page_ids = page_ids;
+  L.key_shift = key_shift;
+  L.k_codes = cache->k_codes;
+  L.k_scales = cache->k_scales;
+  L.v_codes = cache->v_codes;
+  L.v_scales = cache->v_scales;
+  L.num_pages = cache->num_pages;
+  L.hkv = cache->num_kv_heads;
+  L.n_pages = n_pages;
+  L.rotation = r->rotation;
+  L.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
+  L.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
+  return hip_status(bdfp4::launch_writer(L, static_cast<hipStream_t>(stream)), "page writer launch");
+}
+
+bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                               int32_t pages_per_partition, int32_t* ppp_out, int32_t* parts_out) {
+  if (!ppp_out || !parts_out) return fail(BDFP4_E_INVALID, "NULL output");
+  bdfp4_status s = plan(batch, num_kv_heads, max_seq_len, pages_per_partition, ppp_out, parts_out);
+  return s == BDFP4_OK ? ok() : s;
+}
+
+bdfp4_status bdfp4_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t max_seq_len, int32_t pages_per_partition, size_t* bytes) {
+  if (!bytes) return fail(BDFP4_E_INVALID, "NULL output");
+  if (num_q_heads != bdfp4::kGroup * num_kv_heads)
+    return fail(BDFP4_E_UNSUPPORTED, "num_q_heads must be 4 * num_kv_heads");
+  int32_t ppp, parts;
+  bdfp4_status s = plan(batch, num_kv_heads, max_seq_len, pages_per_partition, &ppp, &parts);
+  if (s != BDFP4_OK) return s;
+  // the BF16 decode also reads the partial last page: size for ceil(L/128) pages
+  const int32_t all_parts = ((max_seq_len + 127) / 128 + ppp - 1) / ppp;
+  *bytes = workspace_bytes(batch, num_kv_heads, all_parts > parts ? all_parts : parts);
+  return ok();
+}
+
+static bdfp4_status check_decode_common(const void* q, int32_t batch, int32_t hq, int32_t hkv,
+                                        const int32_t* block_tables, int32_t max_pages_per_seq,
+                                        const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                        int32_t ppp_in, void* workspace, size_t workspace_bytes_in,
+                                        float* out, int32_t* ppp, int32_t* parts) {
+  if (hq != bdfp4::kGroup * hkv)
+    return fail(BDFP4_E_UNSUPPORTED, "num_q_heads must be 4 * num_kv_heads (got %d, %d)", hq, hkv);
+  bdfp4_status s = plan(batch, hkv, max_seq_len, ppp_in, ppp, parts);
+  if (s != BDFP4_OK) return s;
+  if (!q || !block_tables || !seq_lens || !out) return fail(BDFP4_E_INVALID, "NULL input or output pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(BDFP4_E_INVALID, "q and out must be 16-byte aligned");
+  if (max_pages_per_seq < 1) return fail(BDFP4_E_INVALID, "max_pages_per_seq must be positive");
+  if (!isfinite(softmax_scale)) return fail(BDFP4_E_INVALID, "softmax_scale must be finite");
+  const size_t need = workspace_bytes(batch, hkv, *parts);
+  if (workspace == nullptr || workspace_bytes_in < need)
+    return fail(BDFP4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes_in);
+  if (!aligned16(workspace)) return fail(BDFP4_E_INVALID, "workspace must be 16-byte aligned");
+  return BDFP4_OK;
+}
+
+bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+                                    int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                                    int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                    const void* sink_k, const void* sink_v, const void* tail_k,
+                                    const void* tail_v, const float* key_shift, float softmax_scale,
+                                    int32_t pages_per_partition, void* workspace, size_t workspace_bytes_in,
+                                    float* out, void* stream) {
+  if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
+  bdfp4_status s = check_recipe(r);
+  if (s != BDFP4_OK) return s;
+  if ((s = check_cache(cache)) != BDFP4_OK) return s;
+  int32_t ppp, parts;
+  s = check_decode_common(q_bf16, batch, num_q_heads, cache->num_kv_heads, block_tables, max_pages_per_seq,
+                          seq_lens, max_seq_len, softmax_scale, pages_per_partition, workspace,
+                          workspace_bytes_in, out, &ppp, &parts);
+  if (s != BDFP4_OK) return s;
+  if (r->sink_tokens > 0 && (!sink_k || !sink_v)) return fail(BDFP4_E_INVALID, "sink buffers are NULL");
+  if (!tail_k || !tail_v) return fail(BDFP4_E_INVALID, "tail buffers are NULL");
+  if ((sink_k && !aligned16(sink_k)) || (sink_v && !aligned16(sink_v)) || !aligned16(tail_k) ||
+      !aligned16(tail_v))
+    return fail(BDFP4_E_INVALID, "sink and tail buffers must be 16-byte aligned");
+  if (r->key_smoothing && key_shift == nullptr)
+    return fail(BDFP4_E_INVALID, "key_smoothing needs key_shift (the key-mean sidecar)");
+  if (!r->key_smoothing && key_shift != nullptr)
+    return fail(BDFP4_E_INVALID, "key_shift given but key_smoothing is off");
+  if (key_shift && !aligned16(key_shift)) return fail(BDFP4_E_INVALID, "key_shift must be 16-byte aligned");
+  if (max_seq_len / 128 > max_pages_per_seq)
+    return fail(BDFP4_E_INVALID, "max_seq_len needs %d pages but block tables hold %d", max_seq_len / 128,
+                max_pages_per_seq);
+  bdfp4::DecodeLaunch L;
+  L.sink = r->sink_tokens;
+  L.rotation = r->rotation;
+  L.key_smoothing = r->key_smoothing;
+  L.mx = is_mx_kv(r) ? 1 : 0;
+  L.k_four_six = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX;
+  L.p_mode = r->scale_mode_p;
+  L.terms = r->query_terms;
+  L.c = r->c;
+  L.tau = r->scale_mode_p == BDFP4_SCALE_AMAX2_OR_AMAX6 ? r->tau : 0.0f;
+  L.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+  L.k_scales = static_cast<const uint8_t*>(cache->k_scales);
+  L.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+  L.v_scales = static_cast<const uint8_t*>(cache->v_scales);
+  L.num_pages = cache->num_pages;
+  L.hkv = cache->num_kv_heads;
+  L.q = static_cast<const uint16_t*>(q_bf16);
+  L.batch = batch;
+  L.hq = num_q_heads;
+  L.block_tables = block_tables;
+  L.max_pages_per_seq = max_pages_per_seq;
+  L.seq_lens = seq_lens;
+  L.max_seq_len = max_seq_len;
+  L.sink_k = static_cast<const uint16_t*>(sink_k);
+  L.sink_v = static_cast<const uint16_t*>(sink_v);
+  L.tail_k = static_cast<const uint16_t*>(tail_k);
+  L.tail_v = static_cast<const uint16_t*>(tail_v);
+  L.key_shift = key_shift;
+  L.softmax_scale = softmax_scale;
+  L.ppp = ppp;
+  L.max_parts = parts;
+  L.workspace = workspace;
+  L.out = out;
+  return hip_status(bdfp4::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+bdfp4_status bdfp4_bf16_decode_attention(const void* q_bf16, int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, const void* k_pages, const void* v_pages,
+                                         int32_t num_pages, const int32_t* block_tables,
+                                         int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                         int32_t max_seq_len, float softmax_scale, int32_t pages_per_partition,
+                                         void* workspace, size_t workspace_bytes_in, float* out, void* stream) {
+  int32_t ppp, parts;
+  bdfp4_status s = check_decode_common(q_bf16, batch, num_q_heads, num_kv_heads, block_tables,
+                                       max_pages_per_seq, seq_lens, max_seq_len, softmax_scale,
+                                       pages_per_partition, workspace, workspace_bytes_in, out, &ppp, &parts);
+  if (s != BDFP4_OK) return s;
+  if (!k_pages || !v_pages) return fail(BDFP4_E_INVALID, "NULL page pointer");
+  if (!aligned16(k_pages) || !aligned16(v_pages)) return fail(BDFP4_E_INVALID, "pages must be 16-byte aligned");
+  if (num_pages < 1) return fail(BDFP4_E_INVALID, "num_pages must be positive");
+  if ((max_seq_len + 127) / 128 > max_pages_per_seq)
+    return fail(BDFP4_E_INVALID, "max_seq_len needs %d pages but block tables hold %d",
+                (max_seq_len + 127) / 128, max_pages_per_seq);
+  bdfp4::Bf16DecodeLaunch L;
+  L.q = static_cast<const uint16_t*>(q_bf16);
+  L.batch = batch;
+  L.hq = num_q_heads;
+  L.hkv = num_kv_heads;
+  L.k_pages = static_cast<const uint16_t*>(k_pages);
+  L.v_pages = static_cast<const uint16_t*>(v_pages);
+  L.num_pages = num_pages;
+  L.block_tables = block_tables;
+  L.max_pages_per_seq = max_pages_per_seq;
+  L.seq_lens = seq_lens;
+  L.max_seq_len = max_seq_len;
+  L.softmax_scale = softmax_scale;
+  // every page of a BF16 cache is read, the partial last one included
+  L.ppp = ppp;
+  L.max_parts = ((max_seq_len + 127) / 128 + ppp - 1) / ppp;
+  L.workspace = workspace;
+  L.out = out;
+  if (workspace_bytes_in < workspace_bytes(batch, num_kv_heads, L.max_parts))
+    return fail(BDFP4_E_WORKSPACE, "workspace too small for the BF16 decode");
+  return hip_status(bdfp4::launch_bf16_decode(L, static_cast<hipStream_t>(stream)), "bf16 decode launch");
+}
+
+bdfp4_status bdfp4_quantize_rows(const void* rows_bf16, int32_t n_rows, const float* shift, int32_t rotation,
+                                 int32_t mode, int32_t terms, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (n_rows < 0) return fail(BDFP4_E_INVALID, "n_rows must be >= 0");
+  if (mode != BDFP4_SCALE_AMAX6 && mode != BDFP4_SCALE_FOUR_SIX && mode != BDFP4_SCALE_MXFP4_SEARCH)
+    return fail(BDFP4_E_INVALID, "mode must be amax6, four_six or mxfp4_search");
+  if (terms != 1 && terms != 2) return fail(BDFP4_E_INVALID, "terms must be 1 or 2");
+  if (rotation != 0 && rotation != 1) return fail(BDFP4_E_INVALID, "rotation must be 0 or 1");
+  if (n_rows == 0) return ok();
+  if (!rows_bf16 || !codes || !scales) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (!aligned16(rows_bf16) || !aligned16(codes)) return fail(BDFP4_E_INVALID, "rows/codes must be 16-byte aligned");
+  if (n_rows > (1 << 28)) return fail(BDFP4_E_INVALID, "too many rows");
+  const int m = mode == BDFP4_SCALE_AMAX6 ? 1 : (mode == BDFP4_SCALE_FOUR_SIX ? 2 : 3);
+  return hip_status(bdfp4::launch_rows(rows_bf16, n_rows, shift, rotation, m, terms, codes, scales,
+                                       static_cast<hipStream_t>(stream)),
+                    "row quantizer launch");
+}
+
+bdfp4_status bdfp4_quantize_p_blocks(const float* pp, int32_t n_blocks, int32_t mode, float tau, uint8_t* codes,
+                                     uint8_t* scales, void* stream) {
+  if (n_blocks < 0) return fail(BDFP4_E_INVALID, "n_blocks must be >= 0");
+  if (mode != BDFP4_SCALE_AMAX2_OR_AMAX6 && mode != BDFP4_SCALE_AMAX6)
+    return fail(BDFP4_E_INVALID, "mode must be amax2_or_amax6 or amax6");
+  if (mode == BDFP4_SCALE_AMAX2_OR_AMAX6) {
+    if (isnan(tau)) return fail(BDFP4_E_UNCALIBRATED, "tau must be calibrated before evaluation or throughput measurement");
+    if (!isfinite(tau) || tau < 0.0f || tau > 448.0f)
+      return fail(BDFP4_E_INVALID, "tau must be 'calibrate' or a finite number between 0 and 448");
+  }
+  if (n_blocks == 0) return ok();
+  if (!pp || !codes || !scales) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (!aligned16(pp) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return fail(BDFP4_E_INVALID, "pp must be 16-byte and codes 8-byte aligned");
+  if (n_blocks > (1 << 28)) return fail(BDFP4_E_INVALID, "too many blocks");
+  return hip_status(bdfp4::launch_p_blocks(pp, n_blocks, mode, tau, codes, scales, static_cast<hipStream_t>(stream)),
+                    "probability quantizer launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,275 @@
+// Device codecs for the bdfp4 kernels (gfx950): bf16 widening, E4M3 and E8M0
+// scales, E2M1 element codes, the 128-point Hadamard butterflies and the
+// float32 error tree of the adaptive scale searches.
+//
+// Format definitions: OCP 8-bit Floating Point (E4M3, max 448, no infinities)
+// and OCP Microscaling v1.0 (E2M1 elements, E8M0 scales). Scale-mode names
+// from "BitDecoding-FP4 evaluation/config.py" (recipe_additional_config,
+// probability_environment, KV_MODES). Every value produced here must be a
+// bit-exact function of its inputs: float32 operations are written out one
+// by one and the library is compiled with -ffp-contract=off.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bdfp4 {
+
+constexpr int kD = 128;     // head_dim
+constexpr int kPage = 128;  // tokens per page (block_size)
+
+// float32 nearest to 1/sqrt(128) (0x3DB504F3)
+__device__ __forceinline__ float inv_sqrt_d() { return __uint_as_float(0x3DB504F3u); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- E4M3
+
+// Code of the E4M3 value nearest to v >= 0 (ties to even), saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;
+  const uint32_t u = __float_as_uint(v);
+  if (u < 0x3C800000u) {                 // v < 2^-6: subnormal codes m * 2^-9
+    return (uint32_t)__builtin_rintf(v * 512.0f);   // exact scaling, RNE; 8 -> 0x08
+  }
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // RNE to 3 mantissa bits
+  return r - (120u << 3);                // rebias 127 -> 7
+}
+
+// Value of a non-negative finite E4M3 code (exact in float32).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 0u) return (float)m * 0.001953125f;      // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------- E8M0
+
+// 2^E as float32 for E in [-127, 127] (E = -127 is the float32 subnormal 2^-127).
+__device__ __forceinline__ float pow2_f32(int e) {
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Least integer E with a <= 6 * 2^E, for a > 0 (6 * 2^E = 1.5 * 2^(E+2)).
+__device__ __forceinline__ int mx_exponent_hi(float a) {
+  int bias = 0;
+  uint32_t u = __float_as_uint(a);
+  if (u < 0x00800000u) {                  // float32 subnormal: scale up exactly
+    a = a * 18446744073709551616.0f;      // 2^64
+    u = __float_as_uint(a);
+    bias = 64;
+  }
+  const int e = (int)(u >> 23) - 127;
+  return e - 2 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0) - bias;
+}
+
+// ---------------------------------------------------------------- E2M1
+
+// Thresholds between consecutive grid points times s: the midpoints 0.25,
+// 0.75, 1.25, 1.75, 2.5, 3.5, 5 (exact products: s has at most 4 significant
+// bits or is a power of two).
+struct E2m1Thr {
+  float t0, t1, t2, t3, t4, t5, t6;
+  bool zero;
+};
+
+__device__ __forceinline__ E2m1Thr e2m1_thresholds(float s) {
+  E2m1Thr T;
+  T.t0 = 0.25f * s; T.t1 = 0.75f * s; T.t2 = 1.25f * s; T.t3 = 1.75f * s;
+  T.t4 = 2.5f * s;  T.t5 = 3.5f * s;  T.t6 = 5.0f * s;
+  T.zero = !(s > 0.0f);
+  return T;
+}
+
+// Magnitude code (0..7) of |x| relative to s: nearest grid point of the exact
+// ratio, ties to the even code. The code counts the thresholds passed; at a
+// tie the step to an even code is taken, i.e. thresholds 1, 3, 5 are passed
+// on >= and thresholds 0, 2, 4, 6 on >. The passed set is a prefix, so a
+// three-level binary search finds its length.
+__device__ __forceinline__ uint32_t e2m1_mag(float ax, const E2m1Thr& T) {
+  uint32_t c = (ax >= T.t3) ? 4u : 0u;
+  const float tb = c ? T.t5 : T.t1;
+  c += (ax >= tb) ? 2u : 0u;
+  const float tc = (c & 4u) ? ((c & 2u) ? T.t6 : T.t4) : ((c & 2u) ? T.t2 : T.t0);
+  c += (ax > tc) ? 1u : 0u;
+  return c;
+}
+
+// Grid magnitude of a code 0..7: 0, .5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_grid(uint32_t c) {
+  return c < 4u ? 0.5f * (float)c : (c == 7u ? 6.0f : (float)(c - 2u));
+}
+
+// 4-bit code: sign bit of x in bit 3, magnitude in bits 2..0; 0 if s == 0.
+__device__ __forceinline__ uint32_t e2m1_nibble(float x, const E2m1Thr& T) {
+  const uint32_t mag = e2m1_mag(__builtin_fabsf(x), T);
+  const uint32_t sgn = (__float_as_uint(x) >> 31) << 3;
+  return T.zero ? 0u : (sgn | mag);
+}
+
+// ---------------------------------------------------------------- blocks
+
+// Quantize N in-register values with scale value s (float32): codes packed
+// 8 per uint32 (element 2i in the low nibble of byte i) and, when requested,
+// the float32 squared error summed as a balanced pairwise tree
+// ((e0+e1)+(e2+e3))+... . The tree is built incrementally: lvl[k] holds the
+// pending left sum of 2^k elements; element i is merged with the levels of
+// its trailing one bits (left operand the older sum), so the additions and
+// their order are exactly those of the level-by-level tree.
+template <int N, bool kSse>
+__device__ __forceinline__ float quant_block(const float* x, float s, uint32_t* packed) {
+  const E2m1Thr T = e2m1_thresholds(s);
+  constexpr int kLv = N == 32 ? 6 : 5;
+  float lvl[kLv];
+#pragma unroll
+  for (int w = 0; w < N / 8; ++w) packed[w] = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float ax = __builtin_fabsf(x[i]);
+    const uint32_t mag = T.zero ? 0u : e2m1_mag(ax, T);
+    const uint32_t sgn = (__float_as_uint(x[i]) >> 31) << 3;
+    const uint32_t nib = T.zero ? 0u : (sgn | mag);
+    packed[i >> 3] |= nib << (4 * (i & 7));
+    if (kSse) {
+      const float q = __fmul_rn(e2m1_grid(mag), s);   // exact
+      const float d = __fsub_rn(ax, q);
+      float v = __fmul_rn(d, d);
+      int k = 0;
+#pragma unroll
+      for (int bit = 1; bit < N; bit <<= 1, ++k) {
+        if ((i & bit) == 0) break;
+        v = __fadd_rn(lvl[k], v);
+      }
+      lvl[k] = v;
+    }
+  }
+  if (!kSse) return 0.0f;
+  return lvl[kLv - 1];
+}
+
+__device__ __forceinline__ float absmax16(const float* x) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(x[i]));
+  return a;
+}
+
+// NVFP4 block of 16: amax6 or four_six. Returns the E4M3 scale code.
+template <bool kFourSix>
+__device__ __forceinline__ uint32_t nv_block(const float* x, uint32_t* packed) {
+  const float a = absmax16(x);
+  const uint32_t c6 = e4m3_encode(a / 6.0f);
+  if (!kFourSix) {
+    quant_block<16, false>(x, e4m3_value(c6), packed);
+    return c6;
+  }
+  const uint32_t c4 = e4m3_encode(a * 0.25f);
+  uint32_t p6[2], p4[2];
+  const float err6 = quant_block<16, true>(x, e4m3_value(c6), p6);
+  __builtin_amdgcn_sched_barrier(0);   // keep the two candidates from interleaving
+  const float err4 = quant_block<16, true>(x, e4m3_value(c4), p4);
+  const bool take4 = err4 < err6;
+  packed[0] = take4 ? p4[0] : p6[0];
+  packed[1] = take4 ? p4[1] : p6[1];
+  return take4 ? c4 : c6;
+}
+
+// MXFP4 block of 32 with the two-candidate exponent search. Returns the E8M0 code.
+__device__ __forceinline__ uint32_t mx_block(const float* x, uint32_t* packed) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(x[i]));
+  if (!(a > 0.0f)) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) packed[w] = 0u;
+    return 0u;
+  }
+  int ehi = mx_exponent_hi(a);
+  ehi = ehi < -127 ? -127 : (ehi > 127 ? 127 : ehi);
+  const int elo = ehi - 1 < -127 ? -127 : ehi - 1;
+  uint32_t phi[4], plo[4];
+  const float err_hi = quant_block<32, true>(x, pow2_f32(ehi), phi);
+  __builtin_amdgcn_sched_barrier(0);   // keep the two candidates from interleaving
+  const float err_lo = quant_block<32, true>(x, pow2_f32(elo), plo);
+  const bool take_lo = (err_lo < err_hi) && (elo < ehi);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) packed[w] = take_lo ? plo[w] : phi[w];
+  return (uint32_t)((take_lo ? elo : ehi) + 127);
+}
+
+// Dequantized values (float32, exact) of 8 codes in a uint32 with scale s.
+__device__ __forceinline__ void deq8(uint32_t w, float s, float* out) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t nib = (w >> (4 * i)) & 0xFu;
+    const float g = e2m1_grid(nib & 7u) * s;
+    out[i] = (nib & 8u) ? -g : g;
+  }
+}
+
+// ---------------------------------------------------------------- Hadamard
+
+// In-lane stages h = 1 .. N/2 of the fast Walsh-Hadamard transform on N
+// consecutive elements (pairs (i, i+h) with bit h of i clear -> (a+b, a-b)).
+template <int N>
+__device__ __forceinline__ void fwht_inlane(float* x) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = __fadd_rn(a, b);
+        x[i + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+}
+
+// DPP quad permutations (within groups of 4 lanes).
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Cross-lane butterfly stage: the lane whose selector bit is clear keeps
+// own + partner, the other partner - own (the (a+b, a-b) pair of the stage).
+template <int N, int kCtrl>
+__device__ __forceinline__ void fwht_xlane(float* x, bool upper) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float p = dpp_f32<kCtrl>(x[i]);
+    x[i] = upper ? __fsub_rn(p, x[i]) : __fadd_rn(x[i], p);
+  }
+}
+
+// Rotation of a 128-element row held as 32 consecutive elements per lane in
+// 4 consecutive lanes (lane q of the quad holds elements [32q, 32q+32)):
+// stages 1..16 in-lane, 32 across lanes q^1, 64 across q^2, then * 1/sqrt(128).
+__device__ __forceinline__ void rotate_row_quad(float* x, int q) {
+  fwht_inlane<32>(x);
+  fwht_xlane<32, kDppQuadXor1>(x, (q & 1) != 0);
+  fwht_xlane<32, kDppQuadXor2>(x, (q & 2) != 0);
+  const float c = inv_sqrt_d();
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = __fmul_rn(x[i], c);
+}
+
+// Widen 32 bf16 (four 16-byte words) to float32.
+__device__ __forceinline__ void widen32(const uint4* w, float* x) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t v[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * k + 2 * i] = bf16_lo(v[i]);
+      x[8 * k + 2 * i + 1] = bf16_hi(v[i]);
+    }
+  }
+}
+
+}  // namespace bdfp4

@@ -1,0 +1,272 @@
+// KV page writer for gfx950: key centering, 128-point Hadamard rotation and
+// NVFP4 / MXFP4 block quantization of whole 128-token pages.
+//
+// "How openbitsys/bitdecoding-fp4 works" (gitdiagram): the KV cache writer
+// quantizes pages through KV quantization, which uses block scaling and scale
+// modes. "kv-landlords scripts/quant_ab.py", PageSim: a page is quantized
+// once when it fills. "BitDecoding-FP4 evaluation/config.py": RECIPE
+// outlier_aware_key_quantization (key smoothing, Hadamard rotation, adaptive
+// block-scale search), recipe_additional_config (key four_six, value amax6),
+// KV_MODES bitdecoding-mxfp4 (mxfp4_search).
+//
+// One workgroup of 256 threads quantizes one (page, KV head) of either K or
+// V. Each row of 128 elements sits in four consecutive lanes, 32 elements per
+// lane, so the rotation needs only two cross-lane (DPP quad) stages and every
+// NVFP4 block (16) / MXFP4 block (32) lies inside one lane. A wave covers a
+// 16-token tile, whose K codes are one contiguous 1 KiB run of the page
+// layout, written straight from registers; V codes and all scales are
+// assembled in LDS and written as contiguous 16-byte stores.
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace bdfp4 {
+
+struct WriterArgs {
+  const uint16_t* k;       // [n_pages*128][hkv][128] bf16
+  const uint16_t* v;
+  const int32_t* page_ids;
+  const float* key_shift;  // [hkv][128] or null
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  int32_t num_pages;
+  int32_t hkv;
+  int32_t n_pages;
+  int32_t rotation;
+};
+
+// kKMode / kVMode: 1 amax6, 2 four_six, 3 mxfp4_search.
+template <int kKMode, int kVMode>
+__global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
+  constexpr bool kKMx = kKMode == 3, kVMx = kVMode == 3;
+  __shared__ __align__(16) uint8_t s_codes[8192];
+  __shared__ __align__(16) uint8_t s_scales[1024];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 3;          // quarter of the row: elements [32q, 32q+32)
+  const int n = lane >> 2;         // token within the 16-token tile
+  const int ph = blockIdx.x;       // input page * hkv + head
+  const bool is_v = blockIdx.y != 0;
+  const int in_page = ph / a.hkv, h = ph - in_page * a.hkv;
+  const int dst = a.page_ids[in_page];
+  if (dst < 0 || dst >= a.num_pages) return;
+  const size_t blk = (size_t)dst * a.hkv + h;
+
+  float mu[32];
+  if (!is_v && a.key_shift != nullptr) {
+    const float4* m4 = reinterpret_cast<const float4*>(a.key_shift + h * kD + 32 * q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 t = m4[i];
+      mu[4 * i] = t.x; mu[4 * i + 1] = t.y; mu[4 * i + 2] = t.z; mu[4 * i + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mu[i] = 0.0f;
+  }
+  const bool center = !is_v && a.key_shift != nullptr;
+  const uint16_t* src = is_v ? a.v : a.k;
+
+#pragma unroll 1
+  for (int it = 0; it < 2; ++it) {
+    const int tile = wave * 2 + it;
+    const int t = tile * 16 + n;
+    const size_t row = ((size_t)in_page * kPage + t) * a.hkv + h;
+    const uint4* p = reinterpret_cast<const uint4*>(src + row * kD + 32 * q);
+    uint4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = p[k];
+    float x[32];
+    widen32(w, x);
+
+    if (!is_v) {
+      if (center) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = __fsub_rn(x[i], mu[i]);
+      }
+      if (a.rotation) rotate_row_quad(x, q);
+      uint32_t pk[4];
+      if (kKMx) {
+        const uint32_t sc = mx_block(x, pk);
+        s_scales[(q * 16 + n) * 8 + tile] = (uint8_t)sc;
+      } else {
+        const uint32_t s0 = nv_block<kKMode == 2>(x, pk);
+        const uint32_t s1 = nv_block<kKMode == 2>(x + 16, pk + 2);
+        *reinterpret_cast<uint16_t*>(&s_scales[((q * 16 + n) * 8 + tile) * 2]) =
+            (uint16_t)(s0 | (s1 << 8));
+      }
+      uint4* dstc = reinterpret_cast<uint4*>(a.k_codes + blk * 8192 + tile * 1024 + q * 256 + n * 16);
+      *dstc = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+      uint32_t pk[4];
+      const int chunk = t >> 5, qq = (t >> 3) & 3, i8 = t & 7;
+      if (kVMx) {
+        const uint32_t sc = mx_block(x, pk);
+        s_scales[((chunk * 4 + qq) * 4 + q) * 8 + i8] = (uint8_t)sc;
+      } else {
+        const uint32_t s0 = nv_block<false>(x, pk);
+        const uint32_t s1 = nv_block<false>(x + 16, pk + 2);
+        s_scales[((chunk * 4 + qq) * 8 + 2 * q) * 8 + i8] = (uint8_t)s0;
+        s_scales[((chunk * 4 + qq) * 8 + 2 * q + 1) * 8 + i8] = (uint8_t)s1;
+      }
+      // the lane's 4 words are d-octets 4q .. 4q+3 of token t
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        const int oct = 4 * q + o;
+        *reinterpret_cast<uint32_t*>(&s_codes[(((chunk * 4 + qq) * 16 + oct) * 8 + i8) * 4]) = pk[o];
+      }
+    }
+  }
+  __syncthreads();
+  if (!is_v) {
+    const int sbytes = kKMx ? 512 : 1024;
+    if (tid * 16 < sbytes)
+      *reinterpret_cast<uint4*>(a.k_scales + blk * sbytes + tid * 16) =
+          *reinterpret_cast<const uint4*>(&s_scales[tid * 16]);
+  } else {
+    const int sbytes = kVMx ? 512 : 1024;
+    uint4* dc = reinterpret_cast<uint4*>(a.v_codes + blk * 8192);
+    const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
+    dc[tid] = sc4[tid];
+    dc[tid + 256] = sc4[tid + 256];
+    if (tid * 16 < sbytes)
+      *reinterpret_cast<uint4*>(a.v_scales + blk * sbytes + tid * 16) =
+          *reinterpret_cast<const uint4*>(&s_scales[tid * 16]);
+  }
+}
+
+hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
+  if (L.n_pages == 0) return hipSuccess;
+  WriterArgs a;
+  a.k = static_cast<const uint16_t*>(L.k);
+  a.v = static_cast<const uint16_t*>(L.v);
+  a.page_ids = L.page_ids;
+  a.key_shift = L.key_shift;
+  a.k_codes = static_cast<uint8_t*>(L.k_codes);
+  a.k_scales = static_cast<uint8_t*>(L.k_scales);
+  a.v_codes = static_cast<uint8_t*>(L.v_codes);
+  a.v_scales = static_cast<uint8_t*>(L.v_scales);
+  a.num_pages = L.num_pages;
+  a.hkv = L.hkv;
+  a.n_pages = L.n_pages;
+  a.rotation = L.rotation;
+  const dim3 grid((unsigned)(L.n_pages * L.hkv), 2u), block(256u);
+  if (L.k_mode == 2 && L.v_mode == 1)
+    hipLaunchKernelGGL((writer_kernel<2, 1>), grid, block, 0, stream, a);
+  else if (L.k_mode == 1 && L.v_mode == 1)
+    hipLaunchKernelGGL((writer_kernel<1, 1>), grid, block, 0, stream, a);
+  else if (L.k_mode == 3 && L.v_mode == 3)
+    hipLaunchKernelGGL((writer_kernel<3, 3>), grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- debug codec
+
+// One row per quad of lanes: optional shift, optional rotation, then the
+// scale mode, and for terms == 2 the residual r = y - deq(Q1) quantized again.
+template <int kMode>
+__global__ void __launch_bounds__(256) rows_kernel(const uint16_t* rows, int n_rows, const float* shift,
+                                                   int rotation, int terms, uint8_t* codes, uint8_t* scales) {
+  constexpr bool kMx = kMode == 3;
+  constexpr int nb = kMx ? 4 : 8;
+  const int gl = blockIdx.x * 256 + threadIdx.x;
+  const int row = gl >> 2, q = gl & 3;
+  const bool live = row < n_rows;
+  const int r = live ? row : 0;   // dead quads compute on row 0 and store nothing
+  const uint4* p = reinterpret_cast<const uint4*>(rows + (size_t)r * kD + 32 * q);
+  uint4 w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = p[k];
+  float x[32];
+  widen32(w, x);
+  if (shift != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __fsub_rn(x[i], shift[32 * q + i]);
+  }
+  if (rotation) rotate_row_quad(x, q);
+  for (int term = 0; term < terms; ++term) {
+    uint32_t pk[4];
+    float deq[32];
+    if (kMx) {
+      const uint32_t sc = mx_block(x, pk);
+      if (live) scales[((size_t)row * terms + term) * nb + q] = (uint8_t)sc;
+      const float s = pow2_f32((int)sc - 127);   // an all-zero block dequantizes to 0
+#pragma unroll
+      for (int k = 0; k < 4; ++k) deq8(pk[k], s, deq + 8 * k);
+    } else {
+      uint32_t s0 = nv_block<kMode == 2>(x, pk);
+      uint32_t s1 = nv_block<kMode == 2>(x + 16, pk + 2);
+      if (live) {
+        scales[((size_t)row * terms + term) * nb + 2 * q] = (uint8_t)s0;
+        scales[((size_t)row * terms + term) * nb + 2 * q + 1] = (uint8_t)s1;
+      }
+      deq8(pk[0], e4m3_value(s0), deq);
+      deq8(pk[1], e4m3_value(s0), deq + 8);
+      deq8(pk[2], e4m3_value(s1), deq + 16);
+      deq8(pk[3], e4m3_value(s1), deq + 24);
+    }
+    if (live)
+      *reinterpret_cast<uint4*>(codes + ((size_t)row * terms + term) * 64 + 16 * q) =
+          make_uint4(pk[0], pk[1], pk[2], pk[3]);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __fsub_rn(x[i], deq[i]);
+  }
+}
+
+hipError_t launch_rows(const void* rows, int n_rows, const float* shift, int rotation, int mode,
+                       int terms, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_rows * 4 + 255) / 256)), block(256u);
+  const uint16_t* r = static_cast<const uint16_t*>(rows);
+  if (mode == 1)
+    hipLaunchKernelGGL((rows_kernel<1>), grid, block, 0, stream, r, n_rows, shift, rotation, terms, codes, scales);
+  else if (mode == 2)
+    hipLaunchKernelGGL((rows_kernel<2>), grid, block, 0, stream, r, n_rows, shift, rotation, terms, codes, scales);
+  else if (mode == 3)
+    hipLaunchKernelGGL((rows_kernel<3>), grid, block, 0, stream, r, n_rows, shift, rotation, terms, codes, scales);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace bdfp4
+
+namespace bdfp4 {
+
+// One 16-value block of p' per lane: block max, the probability scale rule
+// (amax2_or_amax6: E4M3(a/2) if a < tau else E4M3(a/6); amax6: E4M3(a/6)),
+// then the E2M1 codes.
+__global__ void __launch_bounds__(256) p_blocks_kernel(const float* pp, int n_blocks, int mode, float tau,
+                                                       uint8_t* codes, uint8_t* scales) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= n_blocks) return;
+  float x[16];
+  const float4* p4 = reinterpret_cast<const float4*>(pp + (size_t)b * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 t = p4[i];
+    x[4 * i] = t.x; x[4 * i + 1] = t.y; x[4 * i + 2] = t.z; x[4 * i + 3] = t.w;
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, x[i]);
+  const uint32_t sc = e4m3_encode((mode == 4 && a < tau) ? a * 0.5f : a / 6.0f);
+  uint32_t pk[2];
+  quant_block<16, false>(x, e4m3_value(sc), pk);
+  *reinterpret_cast<uint2*>(codes + (size_t)b * 8) = make_uint2(pk[0], pk[1]);
+  scales[b] = (uint8_t)sc;
+}
+
+hipError_t launch_p_blocks(const float* pp, int n_blocks, int mode, float tau, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream) {
+  if (n_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(p_blocks_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256u), 0, stream,
+                     pp, n_blocks, mode, tau, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace bdfp4

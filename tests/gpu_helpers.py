@@ -1,0 +1,119 @@
+"""Helpers for the GPU parity tests: device transfer of the synthetic inputs,
+oracle <-> C-ABI recipe translation, and the two runs (HIP path, oracle) on
+the same seeded workload."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import fp4_kv_cache_nvfp4_amd as bd
+from oracle import decode as OD
+from oracle import quant as Q
+from oracle import recipe as RC
+from oracle import writer as W
+
+# tolerance for attention outputs against the float64 oracle on the same
+# quantized operands and partitioning
+MAX_ABS = 2e-3
+REL_L2 = 1e-3
+
+_MODE = {Q.NONE: bd.SCALE_NONE, Q.AMAX6: bd.SCALE_AMAX6, Q.FOUR_SIX: bd.SCALE_FOUR_SIX,
+         Q.MXFP4_SEARCH: bd.SCALE_MXFP4_SEARCH, Q.AMAX2_OR_AMAX6: bd.SCALE_AMAX2_OR_AMAX6}
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def to_c(r: RC.Recipe) -> bd.Recipe:
+    c = bd.Recipe()
+    c.sink_tokens = r.sink_tokens
+    c.rotation = int(r.rotation)
+    c.key_smoothing = int(r.key_smoothing)
+    c.scale_mode_k = _MODE[r.scale_mode_k]
+    c.scale_mode_v = _MODE[r.scale_mode_v]
+    c.scale_mode_q = _MODE[r.scale_mode_q]
+    c.scale_mode_p = _MODE[r.scale_mode_p]
+    c.query_terms = r.query_terms
+    c.c = r.c
+    c.tau = float(r.tau)
+    return c
+
+
+def dev_bf16(u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_write(r: RC.Recipe, wl, cache: bd.PagedCache | None = None) -> bd.PagedCache:
+    rc = to_c(r)
+    if cache is None:
+        cache = bd.PagedCache.allocate(rc, wl.num_pages, wl.num_kv_heads)
+    k, v, ids = wl.writer_inputs()
+    if len(ids):
+        mu = dev(wl.key_shift) if r.key_smoothing else None
+        bd.quantize_pages(rc, cache, dev_bf16(k), dev_bf16(v), dev(ids), mu)
+    return cache
+
+
+def oracle_write(r: RC.Recipe, wl) -> dict:
+    cache = W.empty_cache(wl.num_pages, wl.num_kv_heads, r)
+    k, v, ids = wl.writer_inputs()
+    if len(ids):
+        W.write_pages(r, cache, k, v, ids, wl.key_shift if r.key_smoothing else None)
+    return cache
+
+
+def cache_to_host(c: bd.PagedCache) -> dict:
+    return {n: getattr(c, n).cpu().numpy() for n in ("k_codes", "k_scales", "v_codes", "v_scales")}
+
+
+def cache_to_dev(r: RC.Recipe, host: dict, num_kv_heads: int) -> bd.PagedCache:
+    num_pages = host["k_codes"].shape[0]
+    return bd.PagedCache(dev(host["k_codes"]), dev(host["k_scales"]), dev(host["v_codes"]),
+                         dev(host["v_scales"]), num_pages, num_kv_heads)
+
+
+def gpu_decode(r: RC.Recipe, wl, cache: bd.PagedCache, ppp: int, max_seq_len=None,
+               seq_lens=None, block_tables=None, repeat: int = 1):
+    rc = to_c(r)
+    B, Hq = wl.batch, wl.num_q_heads
+    sl = wl.seq_lens if seq_lens is None else seq_lens
+    btab = wl.block_tables if block_tables is None else block_tables
+    msl = int(max(sl.max(), 1)) if max_seq_len is None else max_seq_len
+    sk, sv, tk, tv = wl.sink_tail()
+    ws = bd.alloc_workspace(bd.decode_workspace_size(B, Hq, wl.num_kv_heads, msl, ppp))
+    outs = []
+    args = dict(q=dev_bf16(wl.q), bt=dev(btab.astype(np.int32)), sl=dev(sl.astype(np.int32)),
+                sk=dev_bf16(sk) if r.sink_tokens else None, sv=dev_bf16(sv) if r.sink_tokens else None,
+                tk=dev_bf16(tk), tv=dev_bf16(tv), mu=dev(wl.key_shift) if r.key_smoothing else None)
+    for _ in range(repeat):
+        out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        bd.decode_attention(rc, cache, args["q"], args["bt"], args["sl"], msl, args["sk"], args["sv"],
+                            args["tk"], args["tv"], args["mu"], wl.sigma, ppp, ws, out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().astype(np.float64))
+    return outs if repeat > 1 else outs[0]
+
+
+def oracle_decode(r: RC.Recipe, wl, cache: dict, ppp: int) -> np.ndarray:
+    sk, sv, tk, tv = wl.sink_tail()
+    return OD.decode(r, cache, wl.q, wl.block_tables, wl.seq_lens, sk, sv, tk, tv,
+                     wl.key_shift if r.key_smoothing else None, wl.sigma, ppp)
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    d = got - ref
+    return float(np.max(np.abs(d))), float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
+
+
+def assert_close(got, ref, what=""):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    mx, rel = errors(got, ref)
+    print(f"[parity] {what}: max_abs={mx:.3e} rel_l2={rel:.3e}", flush=True)
+    assert mx <= MAX_ABS and rel <= REL_L2, (what, mx, rel)

@@ -1,0 +1,204 @@
+"""The C ABI on the host (no GPU): the library loads and exports every entry
+point include/bdfp4.h declares; recipe defaults and validation follow the
+BitDecoding-FP4 config page (golden/recipe_modes.json,
+golden/probability_environment.json); every invalid argument returns its
+documented status before anything is launched; sizes and the split plan.
+
+Only failing calls and pure host functions are made here: a call that passed
+validation would launch a kernel.
+"""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+import fp4_kv_cache_nvfp4_amd as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+FAKE = 0x7F0000000000          # 16-byte aligned stand-in device address (never dereferenced)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "bdfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bdfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = _declared()
+    assert len(names) >= 12
+    L = bd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert bd.status_string(0) == "BDFP4_OK"
+    assert bd.status_string(-2) == "BDFP4_E_UNCALIBRATED"
+    assert bd.status_string(-99) == "BDFP4_E_UNKNOWN"
+
+
+def test_recipe_defaults_follow_kv_modes():
+    g = _golden("recipe_modes.json")
+    nv = bd.recipe_default_nvfp4()
+    e = g["bitdecoding-nvfp4"]
+    assert nv.sink_tokens == e["sink_tokens"] and nv.query_terms == e["query_terms"]
+    assert (nv.scale_mode_k, nv.scale_mode_v, nv.scale_mode_q) == (bd.SCALE_FOUR_SIX, bd.SCALE_AMAX6, bd.SCALE_AMAX6)
+    assert nv.rotation == 1 and nv.key_smoothing == 1
+    assert nv.scale_mode_p == bd.SCALE_AMAX2_OR_AMAX6 and nv.c == g["probability"]["c"]
+    assert math.isnan(nv.tau)
+    mx = bd.recipe_default_mxfp4()
+    assert mx.scale_mode_k == mx.scale_mode_v == mx.scale_mode_q == bd.SCALE_MXFP4_SEARCH
+    assert mx.sink_tokens == g["bitdecoding-mxfp4"]["sink_tokens"] and mx.rotation == 1
+
+
+def test_recipe_validation_follows_probability_environment():
+    g = _golden("probability_environment.json")
+    for case in g["cases"]:
+        r = bd.recipe_default_nvfp4()
+        r.c = case["c"]
+        r.tau = math.nan if case["tau"] is None else float(case["tau"])
+        r.scale_mode_p = bd.SCALE_AMAX2_OR_AMAX6 if case["enabled"] else bd.SCALE_AMAX6
+        want = {"ok": bd.OK, "invalid": bd.E_INVALID, "uncalibrated": bd.E_UNCALIBRATED}[case["expect"]]
+        if want == bd.OK:
+            bd.recipe_validate(r)
+        else:
+            with pytest.raises(bd.Bdfp4Error) as ei:
+                bd.recipe_validate(r)
+            assert ei.value.status == want
+            assert case["message"] in str(ei.value)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("sink_tokens", 8, bd.E_INVALID), ("sink_tokens", 128, bd.E_INVALID), ("sink_tokens", -16, bd.E_INVALID),
+    ("query_terms", 3, bd.E_INVALID), ("rotation", 2, bd.E_INVALID), ("key_smoothing", 5, bd.E_INVALID),
+    ("scale_mode_k", 9, bd.E_INVALID), ("scale_mode_v", bd.SCALE_FOUR_SIX, bd.E_INVALID),
+    ("scale_mode_p", 7, bd.E_INVALID), ("scale_mode_p", bd.SCALE_NONE, bd.E_UNSUPPORTED),
+    ("scale_mode_q", bd.SCALE_MXFP4_SEARCH, bd.E_UNSUPPORTED),
+    ("scale_mode_v", bd.SCALE_MXFP4_SEARCH, bd.E_UNSUPPORTED),
+])
+def test_recipe_field_checks(field, value, status):
+    r = bd.recipe_default_nvfp4(tau=1.0)
+    setattr(r, field, value)
+    with pytest.raises(bd.Bdfp4Error) as ei:
+        bd.recipe_validate(r)
+    assert ei.value.status == status
+
+
+def test_sizes_and_plan():
+    nv = bd.recipe_default_nvfp4(tau=1.0)
+    mx = bd.recipe_default_mxfp4(tau=1.0)
+    assert bd.cache_bytes(nv, 10, 8) == (10 * 8 * 8192, 10 * 8 * 1024, 10 * 8 * 8192, 10 * 8 * 1024)
+    assert bd.cache_bytes(mx, 3, 2) == (3 * 2 * 8192, 3 * 2 * 512, 3 * 2 * 8192, 3 * 2 * 512)
+    # explicit plan
+    assert bd.decode_plan(1, 8, 131072, 8) == (8, 128)
+    assert bd.decode_plan(1, 1, 2048, 4) == (4, 4)
+    assert bd.decode_plan(1, 1, 100, 4) == (4, 0)
+    ppp, parts = bd.decode_plan(1, 8, 131072, 0)
+    assert 1 <= ppp <= 16 and parts == -(-1024 // ppp)
+    ws = bd.decode_workspace_size(1, 32, 8, 131072, 8)
+    assert ws == 65536 + 8 * 129 * 520 * 4
+    with pytest.raises(bd.Bdfp4Error) as ei:
+        bd.decode_workspace_size(1, 24, 8, 1000, 0)
+    assert ei.value.status == bd.E_UNSUPPORTED
+    for args in [(0, 8, 1000, 0), (1, 8, 0, 0), (1, 8, 1000, 17), (1, 8, 1000, -1)]:
+        with pytest.raises(bd.Bdfp4Error) as ei:
+            bd.decode_plan(*args)
+        assert ei.value.status == bd.E_INVALID
+
+
+def _cache(**kw):
+    c = bd.Cache(FAKE, FAKE, FAKE, FAKE, 16, 1, 128, 128)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _decode(r, cache=None, **kw):
+    a = dict(q=FAKE, batch=1, hq=4, bt=FAKE, maxp=16, seq=FAKE, maxlen=2048, sk=FAKE, sv=FAKE, tk=FAKE,
+             tv=FAKE, mu=FAKE, scale=0.088, ppp=4, ws=None, wsb=None, out=FAKE)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = bd.decode_workspace_size(1, 4, 1, 2048, 4)
+    if a["ws"] is None:
+        a["ws"] = FAKE
+    c = cache or _cache()
+    return bd.lib().bdfp4_decode_attention(
+        ctypes.byref(r), ctypes.byref(c), a["q"], a["batch"], a["hq"], a["bt"], a["maxp"], a["seq"],
+        a["maxlen"], a["sk"], a["sv"], a["tk"], a["tv"], a["mu"], a["scale"], a["ppp"], a["ws"], a["wsb"],
+        a["out"], None)
+
+
+def test_decode_rejects_before_launch():
+    r = bd.recipe_default_nvfp4(tau=1.0)
+    assert _decode(bd.recipe_default_nvfp4()) == bd.E_UNCALIBRATED
+    assert _decode(r.replace(c=2)) == bd.E_INVALID
+    assert _decode(r, cache=_cache(head_dim=64)) == bd.E_UNSUPPORTED
+    assert _decode(r, cache=_cache(block_size=16)) == bd.E_UNSUPPORTED
+    assert _decode(r, cache=_cache(k_codes=None)) == bd.E_INVALID
+    assert _decode(r, cache=_cache(v_scales=FAKE + 4)) == bd.E_INVALID
+    assert _decode(r, hq=8) == bd.E_UNSUPPORTED
+    assert _decode(r, q=None) == bd.E_INVALID
+    assert _decode(r, q=FAKE + 2) == bd.E_INVALID
+    assert _decode(r, mu=None) == bd.E_INVALID                     # key smoothing without key means
+    assert _decode(r.replace(key_smoothing=0)) == bd.E_INVALID     # key means without smoothing
+    assert _decode(r, sk=None) == bd.E_INVALID
+    assert _decode(r, tk=None) == bd.E_INVALID
+    assert _decode(r, ws=None, wsb=0) == bd.E_WORKSPACE
+    assert _decode(r, wsb=100) == bd.E_WORKSPACE
+    assert _decode(r, maxp=15) == bd.E_INVALID                     # 2048 tokens need 16 pages
+    assert _decode(r, maxlen=0) == bd.E_INVALID
+    assert _decode(r, ppp=40) == bd.E_INVALID
+    assert _decode(r, scale=float("inf")) == bd.E_INVALID
+    assert _decode(r, batch=0) == bd.E_INVALID
+    assert "key_shift" in bd.lib().bdfp4_last_error().decode() or True
+
+
+def _write(r, cache=None, k=FAKE, v=FAKE, ids=FAKE, n=4, mu=FAKE):
+    c = cache or _cache()
+    return bd.lib().bdfp4_quantize_pages(ctypes.byref(r), ctypes.byref(c), k, v, ids, n, mu, None)
+
+
+def test_writer_rejects_before_launch():
+    r = bd.recipe_default_nvfp4()          # tau is not needed to write pages
+    assert _write(r, n=0) == bd.OK          # empty write is a no-op
+    assert _write(r, n=-1) == bd.E_INVALID
+    assert _write(r, k=None) == bd.E_INVALID
+    assert _write(r, v=FAKE + 8) == bd.E_INVALID
+    assert _write(r, ids=None) == bd.E_INVALID
+    assert _write(r, mu=None) == bd.E_INVALID
+    assert _write(r.replace(key_smoothing=0)) == bd.E_INVALID
+    assert _write(r.replace(scale_mode_k=bd.SCALE_MXFP4_SEARCH)) == bd.E_UNSUPPORTED
+    assert _write(r, cache=_cache(num_pages=0)) == bd.E_INVALID
+    assert _write(r, cache=_cache(head_dim=256)) == bd.E_UNSUPPORTED
+
+
+def test_codec_entries_reject_before_launch():
+    L = bd.lib()
+    assert L.bdfp4_quantize_rows(FAKE, 4, None, 1, 7, 1, FAKE, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_quantize_rows(FAKE, 4, None, 1, 1, 3, FAKE, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_quantize_rows(FAKE, 0, None, 1, 1, 1, None, None, None) == bd.OK
+    assert L.bdfp4_quantize_p_blocks(FAKE, 4, 4, ctypes.c_float(math.nan), FAKE, FAKE, None) == bd.E_UNCALIBRATED
+    assert L.bdfp4_quantize_p_blocks(FAKE, 4, 4, ctypes.c_float(500.0), FAKE, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_quantize_p_blocks(FAKE, 4, 2, ctypes.c_float(1.0), FAKE, FAKE, None) == bd.E_INVALID
+
+
+def test_bf16_decode_rejects_before_launch():
+    L = bd.lib()
+    wsb = bd.decode_workspace_size(1, 4, 1, 2048, 4)
+    call = lambda **k: L.bdfp4_bf16_decode_attention(
+        k.get("q", FAKE), 1, k.get("hq", 4), 1, k.get("kp", FAKE), FAKE, 16, FAKE, k.get("maxp", 16), FAKE,
+        k.get("maxlen", 2048), 0.088, 4, FAKE, k.get("wsb", wsb), FAKE, None)
+    assert call(hq=12) == bd.E_UNSUPPORTED
+    assert call(kp=None) == bd.E_INVALID
+    assert call(maxlen=2049) == bd.E_INVALID       # 17 pages needed, 16 in the table
+    assert call(wsb=64) == bd.E_WORKSPACE

@@ -1,0 +1,94 @@
+"""GPU codec parity through the C ABI: the row quantizer (key / query path:
+shift, rotation, amax6 / four_six / mxfp4_search, two residual terms) and the
+probability quantizer (amax2_or_amax6 with tau, amax6) against the oracle,
+bit for bit, including ties, zero blocks, subnormal and saturating scales."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_nvfp4_amd as bd
+from fp4_kv_cache_nvfp4_amd import synth
+from oracle import formats as F
+from oracle import quant as Q
+from oracle import writer as W
+
+from gpu_helpers import dev, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _pack_logical(nib):
+    """[..., 128] nibbles -> [..., 64] bytes, element 2i in the low nibble."""
+    nib = nib.astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _rows(seed, n):
+    """A mix of row types: normal, outlier channels, tiny, huge, on-grid, zeros."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 128)).astype(np.float32)
+    x[0::7, rng.integers(0, 128, 4)] += 10.0
+    x[1::7] *= 1e-4
+    x[2::7] *= 300.0
+    x[2::14] *= 10.0                        # saturating E4M3 scales
+    x[3::7] = 0.0
+    x[4::7, :16] = 0.0
+    g = rng.choice(GRID, size=(n, 128)) * rng.choice([-1.0, 1.0], size=(n, 128))
+    x[5::7] = (g[5::7] * 0.375).astype(np.float32)
+    x[6::7] = rng.integers(-12, 13, size=x[6::7].shape) * np.float32(0.25)   # many exact ties
+    return synth.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("mode", [Q.AMAX6, Q.FOUR_SIX, Q.MXFP4_SEARCH])
+@pytest.mark.parametrize("rotation,shift", [(False, False), (True, False), (True, True)])
+@pytest.mark.parametrize("terms", [1, 2])
+def test_rows_bit_exact(mode, rotation, shift, terms):
+    n = 4099                                  # several workgroups and a ragged tail
+    u = _rows(11, n)
+    mu = (np.random.default_rng(3).standard_normal(128) * 2).astype(np.float32) if shift else None
+    cmode = {Q.AMAX6: bd.SCALE_AMAX6, Q.FOUR_SIX: bd.SCALE_FOUR_SIX, Q.MXFP4_SEARCH: bd.SCALE_MXFP4_SEARCH}[mode]
+    nb = 4 if mode == Q.MXFP4_SEARCH else 8
+    codes = torch.zeros((n, terms, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((n, terms, nb), dtype=torch.uint8, device="cuda")
+    bd.quantize_rows(dev_bf16(u), dev(mu) if shift else None, int(rotation), cmode, terms, codes, scales)
+    torch.cuda.synchronize()
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    y = W.key_rows(F.bf16_to_f32(u), mu, rotation)
+    if terms == 1:
+        nib, sc = Q.quantize(y, mode)
+        want = [(nib, sc)]
+    else:
+        want, _ = Q.quantize_query(y, mode, 2)
+    for t, (nib, sc) in enumerate(want):
+        assert np.array_equal(gc[:, t], _pack_logical(nib)), f"codes term {t}"
+        assert np.array_equal(gs[:, t], sc.astype(np.uint8)), f"scales term {t}"
+
+
+def _p_blocks(seed, n):
+    rng = np.random.default_rng(seed)
+    p = np.exp(-rng.exponential(2.0, size=(n, 16)))
+    p[::5, 0] = 1.0
+    pp = (8.0 * p).astype(np.float32)
+    pp[1::9] *= np.float32(1e-3)            # small blocks: subnormal / zero scales
+    pp[2::9] = 0.0
+    pp[3::9] = (rng.integers(0, 25, size=(len(pp[3::9]), 16)) * 0.25).astype(np.float32)   # ties
+    pp[4::9, :] = np.float32(1.0)          # a == tau exactly
+    pp[5::9] *= np.float32(80.0)           # large scales (c p' up to 640)
+    return pp
+
+
+@pytest.mark.parametrize("mode,tau", [(Q.AMAX2_OR_AMAX6, 1.0), (Q.AMAX2_OR_AMAX6, 0.0),
+                                      (Q.AMAX2_OR_AMAX6, 448.0), (Q.AMAX2_OR_AMAX6, 0.37), (Q.AMAX6, 0.0)])
+def test_p_blocks_bit_exact(mode, tau):
+    n = 20011
+    pp = _p_blocks(5, n)
+    cmode = bd.SCALE_AMAX2_OR_AMAX6 if mode == Q.AMAX2_OR_AMAX6 else bd.SCALE_AMAX6
+    codes = torch.zeros((n, 8), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((n,), dtype=torch.uint8, device="cuda")
+    bd.quantize_p_blocks(dev(pp), cmode, tau, codes, scales)
+    torch.cuda.synchronize()
+    nib, sc = Q.quantize_p(pp, mode, np.float32(tau))
+    assert np.array_equal(scales.cpu().numpy(), sc[:, 0])
+    assert np.array_equal(codes.cpu().numpy(), _pack_logical(nib))

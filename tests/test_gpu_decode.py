@@ -1,0 +1,145 @@
+"""GPU decode parity through the C ABI against the float64 oracle on the same
+quantized operands and the same split plan: max-abs <= 2e-3 and relative L2
+<= 1e-3 on float32 outputs. Covers the tiny 2K case, ragged batches (sink
+only, sink + tail, several partitions with a ragged last one), sink lengths,
+the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode, the
+32K Qwen3-4B-shaped layer with a 77-token tail, determinism, paging
+invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
+and the BF16-KV baseline arm."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_nvfp4_amd as bd
+from fp4_kv_cache_nvfp4_amd import synth
+from oracle import decode as OD
+from oracle import quant as Q
+from oracle import recipe as RC
+
+from gpu_helpers import (assert_close, cache_to_dev, dev, dev_bf16, gpu_decode, gpu_write,
+                         oracle_decode, oracle_write, to_c)
+
+pytestmark = pytest.mark.gpu
+
+NV = RC.nvfp4_default().with_(tau=1.0)
+MX = RC.mxfp4_default().with_(tau=1.0)
+
+
+def _run(r, wl, ppp, what):
+    print(f"[decode] {what}", flush=True)
+    host = oracle_write(r, wl)
+    ref = oracle_decode(r, wl, host, ppp)
+    got = gpu_decode(r, wl, cache_to_dev(r, host, wl.num_kv_heads), ppp)
+    assert_close(got, ref, what)
+    return got, ref, host
+
+
+@pytest.mark.parametrize("ppp", [4, 1, 3, 16])
+def test_tiny_2k(ppp):
+    _run(NV, synth.tiny(0), ppp, f"tiny ppp={ppp}")
+
+
+def test_tiny_2k_mxfp4():
+    _run(MX, synth.tiny(0), 4, "tiny mxfp4")
+
+
+@pytest.mark.parametrize("variant", ["terms1", "c1", "tau0", "p_amax6", "k_amax6", "norot", "nosmooth"])
+def test_recipe_variants(variant):
+    r = {"terms1": NV.with_(query_terms=1), "c1": NV.with_(c=1), "tau0": NV.with_(tau=0.0),
+         "p_amax6": NV.with_(scale_mode_p=Q.AMAX6), "k_amax6": NV.with_(scale_mode_k=Q.AMAX6),
+         "norot": NV.with_(rotation=False), "nosmooth": NV.with_(key_smoothing=False)}[variant]
+    wl = synth.decode_workload("v", 3, [1500, 777], 8, 2, "qwen", extra_pages=1)
+    _run(r, wl, 2, variant)
+
+
+@pytest.mark.parametrize("sink", [0, 16, 112])
+def test_ragged_batch(sink):
+    # L = 1 (sink only), 100 (< one page), 300 (2 pages + 44 tail), 2049 (16 pages + 1), 640 (5 pages)
+    wl = synth.decode_workload("r", 4, [1, 100, 300, 2049, 640], 8, 2, "tiny", extra_pages=2, sink_tokens=sink)
+    _run(NV.with_(sink_tokens=sink), wl, 3, f"ragged sink={sink}")
+
+
+def test_ragged_batch_mxfp4():
+    wl = synth.decode_workload("r", 5, [129, 1000, 4096 + 77], 12, 3, "qwen", extra_pages=2)
+    _run(MX, wl, 5, "ragged mxfp4")
+
+
+def test_qwen_32k_layer():
+    """32 query / 8 KV heads, 256 full pages + 77-token tail, permuted pool."""
+    wl = synth.qwen_32k(0)
+    ppp, _ = bd.decode_plan(1, 8, int(wl.seq_lens[0]), 0)
+    _run(NV, wl, ppp, f"qwen 32k ppp={ppp}")
+
+
+def test_determinism_and_paging_invariance():
+    wl = synth.decode_workload("d", 6, [3000, 1234], 8, 2, "qwen", extra_pages=4)
+    host = oracle_write(NV, wl)
+    cache = cache_to_dev(NV, host, 2)
+    a, b = gpu_decode(NV, wl, cache, 2, repeat=2)
+    assert np.array_equal(a, b)
+    # move every physical page to a new slot and remap the tables
+    perm = np.random.default_rng(0).permutation(wl.num_pages)
+    moved = {k: np.empty_like(v) for k, v in host.items()}
+    for k in host:
+        moved[k][perm] = host[k]
+    c = gpu_decode(NV, wl, cache_to_dev(NV, moved, 2), 2, block_tables=perm[wl.block_tables].astype(np.int32))
+    assert np.array_equal(a, c)
+
+
+def test_invalid_inputs_give_nan_rows():
+    wl = synth.decode_workload("n", 8, [700, 600, 500], 8, 2, "tiny", extra_pages=1)
+    host = oracle_write(NV, wl)
+    cache = cache_to_dev(NV, host, 2)
+    ref = oracle_decode(NV, wl, host, 2)
+    sl = wl.seq_lens.copy()
+    sl[1] = 0                                   # empty sequence
+    bt = wl.block_tables.copy()
+    bt[2, 1] = wl.num_pages + 7                 # page outside the pool
+    got = gpu_decode(NV, wl, cache, 2, max_seq_len=700, seq_lens=sl, block_tables=bt)
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
+    assert_close(got[0], ref[0], "valid row next to invalid ones")
+    # a length above max_seq_len is rejected on the device too
+    sl2 = wl.seq_lens.copy()
+    got2 = gpu_decode(NV, wl, cache, 2, max_seq_len=600, seq_lens=sl2)
+    assert np.all(np.isnan(got2[0])) and np.all(np.isfinite(got2[1:]))
+
+
+def test_workspace_reuse_across_shapes():
+    """Tickets return to zero: one workspace serves different batches back to back."""
+    big = synth.decode_workload("a", 9, [2000, 900, 129], 8, 2, "tiny", extra_pages=1)
+    small = synth.decode_workload("b", 10, [700], 8, 2, "tiny")
+    ws = bd.alloc_workspace(bd.decode_workspace_size(3, 8, 2, 2048, 1))
+    for wl in (big, small, big):
+        host = oracle_write(NV, wl)
+        ref = oracle_decode(NV, wl, host, 1)
+        rc = to_c(NV)
+        sk, sv, tk, tv = wl.sink_tail()
+        out = torch.empty((wl.batch, 8, 128), dtype=torch.float32, device="cuda")
+        bd.decode_attention(rc, cache_to_dev(NV, host, 2), dev_bf16(wl.q), dev(wl.block_tables),
+                            dev(wl.seq_lens), int(wl.seq_lens.max()), dev_bf16(sk), dev_bf16(sv), dev_bf16(tk),
+                            dev_bf16(tv), dev(wl.key_shift), wl.sigma, 1, ws, out)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().astype(np.float64), ref, f"reuse {wl.name}")
+    assert not ws[:65536].any()
+
+
+@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+def test_end_to_end_writer_then_decode(r):
+    wl = synth.decode_workload("e", 12, [5000, 2300], 16, 4, "qwen", extra_pages=2)
+    cache = gpu_write(r, wl)
+    ref = oracle_decode(r, wl, oracle_write(r, wl), 4)
+    assert_close(gpu_decode(r, wl, cache, 4), ref, "end to end")
+
+
+@pytest.mark.parametrize("ppp", [1, 4])
+def test_bf16_baseline(ppp):
+    wl = synth.decode_workload("b", 13, [1, 127, 128, 1000, 2100], 8, 2, "qwen", extra_pages=2)
+    kp, vp = wl.bf16_pages()
+    ref = OD.bf16_decode(wl.q, kp, vp, wl.block_tables, wl.seq_lens, wl.sigma)
+    msl = int(wl.seq_lens.max())
+    ws = bd.alloc_workspace(bd.decode_workspace_size(wl.batch, 8, 2, msl, ppp))
+    out = torch.empty((wl.batch, 8, 128), dtype=torch.float32, device="cuda")
+    bd.bf16_decode_attention(dev_bf16(wl.q), dev_bf16(kp), dev_bf16(vp), dev(wl.block_tables),
+                             dev(wl.seq_lens), msl, wl.sigma, ppp, ws, out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), ref, f"bf16 baseline ppp={ppp}")
