@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 decode hot path on one MI355X.
+
+Workload (the 128K long-context decode): batch 1, Qwen3-4B shapes (32 query
+/ 8 KV heads, head_dim 128), 131,072-token context paged at block_size 128
+through a permuted block table, 16-token BF16 sink, no tail; 36 layers with
+independent seeded K/V/Q/key means (seed = layer); bitdecoding-nvfp4 recipe
+(Hadamard rotation, key centering, K four_six, V/Q amax6, two-term query,
+P amax2_or_amax6, c = 8, tau = 1.0). Inputs are synthetic, drawn on the
+device, and every layer's pages are written by the HIP page writer before
+timing; all inputs are resident in HBM when the timed region starts.
+
+A step is one decode token through all 36 layers: 36 launches of
+bdfp4_decode_attention (each: two-term query quantization, QK^T over the FP4
+pages, partition softmax, P quantization, PV, BF16 sink partition and the
+split-K merge). The MXFP4 and BF16-KV arms and the page writer (131,072
+tokens x 8 heads prefill write) are timed the same way and reported beside it.
+
+Prints one JSON line; run `python bench.py --help` for options.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "FP4 decode-attention µs/step + achieved HBM GB/s (% of peak) at 128K ctx"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--context", type=int, default=131072)
+    ap.add_argument("--ppp", type=int, default=0, help="pages per partition (0 = library plan)")
+    ap.add_argument("--arms", default="nvfp4,mxfp4,bf16")
+    ap.add_argument("--no-writer", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration) and exit")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- algorithmic bytes
+
+def decode_bytes(seq_len: int, hq: int, hkv: int, sink: int, mx: bool) -> int:
+    """Bytes one decode launch must move: FP4 K/V codes + scales of tokens
+    [sink, 128 n), BF16 sink/tail tokens, query, key means, block table, output."""
+    n_full = seq_len // 128
+    fp4_tok = max(0, 128 * n_full - sink) if n_full else 0
+    bf16_tok = min(sink, seq_len) + max(0, seq_len - max(sink, 128 * n_full))
+    per_tok = 2 * (64 + (4 if mx else 8))
+    return (fp4_tok * hkv * per_tok + bf16_tok * hkv * 512 + hq * 256 + hkv * 512 + 4 * n_full + hq * 512)
+
+
+def bf16_decode_bytes(seq_len: int, hq: int, hkv: int) -> int:
+    return seq_len * hkv * 512 + hq * 256 + 4 * (-(-seq_len // 128)) + hq * 512
+
+
+def writer_bytes(tokens: int, hkv: int, mx: bool) -> int:
+    read = tokens * hkv * 128 * 2 * 2 + hkv * 512 + 4 * (tokens // 128)
+    write = tokens * hkv * 2 * (64 + (4 if mx else 8))
+    return read + write
+
+
+# ----------------------------------------------------------------- timing
+
+def time_launches(fns, steps: int, warmup: int, graph: bool = False):
+    """Run `warmup` untimed steps, then exactly `steps` timed steps of the
+    launches in `fns` on the current stream. Returns (ms per step, mean ms per
+    launch from per-launch events in a second pass over the same launches)."""
+    import torch
+
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        if g is not None:
+            g.replay()
+        else:
+            for f in fns:
+                f()
+    end.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms_step = start.elapsed_time(end) / steps
+    # per-launch durations: events around each launch, same stream
+    n_ev = min(steps, 5)
+    evs = []
+    torch.cuda.synchronize()
+    for _ in range(n_ev):
+        for f in fns:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return ms_step, float(np.mean(per)), wall, float(np.median(per))
+
+
+# ----------------------------------------------------------------- setup
+
+def build_layers(args, arms):
+    import torch
+
+    import fp4_kv_cache_nvfp4_amd as bd
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    rec = {"nvfp4": bd.recipe_default_nvfp4(tau=1.0), "mxfp4": bd.recipe_default_mxfp4(tau=1.0)}
+    L = args.context
+    ppp, parts = bd.decode_plan(1, 8, L, args.ppp)
+    layers = {a: [] for a in arms}
+    ws = {a: bd.alloc_workspace(bd.decode_workspace_size(1, 32, 8, L, ppp)) for a in arms}
+    outs = {a: torch.empty((1, 32, 128), dtype=torch.float32, device="cuda") for a in arms}
+    for layer in range(args.layers):
+        d = synth.torch_decode_layer(layer, seq_len=L)
+        for a in arms:
+            if a in rec:
+                r = rec[a]
+                cache = bd.PagedCache.allocate(r, d["num_pages"], 8)
+                bd.quantize_pages(r, cache, d["k"], d["v"], d["page_ids"], d["key_shift"])
+                call = bd.DecodeCall(r, cache, d["q"], d["block_tables"], d["seq_lens"], L, d["sink_k"],
+                                     d["sink_v"], d["tail_k"], d["tail_v"], d["key_shift"], d["sigma"], ppp,
+                                     ws[a], outs[a])
+            else:
+                kp = synth.bf16_pages_from_tokens(d["k"], d["block_tables"], d["num_pages"])
+                vp = synth.bf16_pages_from_tokens(d["v"], d["block_tables"], d["num_pages"])
+                call = bd.Bf16DecodeCall(d["q"], kp, vp, d["block_tables"], d["seq_lens"], L, d["sigma"], ppp,
+                                         ws[a], outs[a])
+            layers[a].append(call)
+        del d
+        torch.cuda.synchronize()
+    return layers, outs, ppp, parts
+
+
+def bench_writer(args, mx: bool):
+    import torch
+
+    import fp4_kv_cache_nvfp4_amd as bd
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    w = synth.torch_write_rows(0)
+    r = bd.recipe_default_mxfp4(tau=1.0) if mx else bd.recipe_default_nvfp4(tau=1.0)
+    cache = bd.PagedCache.allocate(r, w["num_pages"], 8)
+    fn = lambda: bd.quantize_pages(r, cache, w["k"], w["v"], w["page_ids"], w["key_shift"])
+    ms, per, _, med = time_launches([fn], max(args.steps, 10), 3)
+    nbytes = writer_bytes(w["tokens"], 8, mx)
+    del w, cache
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "us_kernel_events": per * 1e3, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def cpu_baseline(args):
+    """The oracle (numpy) decode on a bounded sample of the same workload:
+    one layer, 2 of the 8 KV heads (8 query heads), the full 131,072-token
+    context, pages quantized by the oracle writer beforehand (untimed)."""
+    from fp4_kv_cache_nvfp4_amd import synth
+    from oracle import decode as OD
+    from oracle import recipe as RC
+    from oracle import writer as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    L = args.context
+    wl = synth.decode_workload("qwen3_4b_128k_sample", 0, [L], 8, 2, "qwen")
+    r = RC.nvfp4_default().with_(tau=1.0)
+    cache = W.empty_cache(wl.num_pages, 2, r)
+    k, v, ids = wl.writer_inputs()
+    W.write_pages(r, cache, k, v, ids, wl.key_shift)
+    sk, sv, tk, tv = wl.sink_tail()
+    ppp = 8
+    t0 = time.perf_counter()
+    OD.decode(r, cache, wl.q, wl.block_tables, wl.seq_lens, sk, sv, tk, tv, wl.key_shift, wl.sigma, ppp)
+    dt = time.perf_counter() - t0
+    nbytes = decode_bytes(L, 8, 2, 16, False)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": f"oracle float64 decode of 1 layer x 2 of 8 KV heads (8 query heads) over the full {L}-token "
+                      f"context on oracle-written NVFP4 pages ({nbytes} algorithmic bytes) in {dt:.2f} s; "
+                      f"{cores} host cores visible, BLAS threads {blas_threads}",
+            "seconds": dt}
+
+
+def copy_calibration():
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms, "GBps_rw": 2 * n / (ms * 1e-3) / 1e9}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of the decode is described in DESIGN.md, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    arms = [a for a in args.arms.split(",") if a]
+    assert arms and arms[0] == "nvfp4", "the first arm is the headline NVFP4 decode"
+    print(f"[bench] building {args.layers} layers x {args.context} tokens, arms {arms}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    layers, outs, ppp, parts = build_layers(args, arms)
+    print(f"[bench] setup {time.perf_counter() - t0:.1f} s; pages/partition {ppp}, partitions {parts}",
+          file=sys.stderr, flush=True)
+    res = {}
+    for a in arms:
+        ms, per, wall, med = time_launches(layers[a], args.steps, args.warmup, graph=args.graph)
+        if not torch.isfinite(outs[a]).all():
+            raise RuntimeError(f"{a}: non-finite decode output")
+        nb = (bf16_decode_bytes(args.context, 32, 8) if a == "bf16"
+              else decode_bytes(args.context, 32, 8, 16, a == "mxfp4"))
+        res[a] = {"ms_per_step": ms, "us_per_layer": ms * 1e3 / args.layers, "us_kernel_events": per * 1e3,
+                  "us_kernel_events_median": med * 1e3, "wall_ms_per_step": wall,
+                  "bytes_per_layer": nb, "GBps": nb * args.layers / (ms * 1e-3) / 1e9,
+                  "kernel_GBps": nb / (per * 1e-3) / 1e9}
+        print(f"[bench] {a}: {ms * 1e3:.1f} us/step, {res[a]['GBps']:.0f} GB/s, kernel "
+              f"{per * 1e3:.2f} us ({res[a]['kernel_GBps']:.0f} GB/s)", file=sys.stderr, flush=True)
+    del layers
+    torch.cuda.empty_cache()
+    writer = {}
+    if not args.no_writer:
+        for mx in (False, True):
+            writer["mxfp4" if mx else "nvfp4"] = bench_writer(args, mx)
+            print(f"[bench] writer {'mxfp4' if mx else 'nvfp4'}: {writer['mxfp4' if mx else 'nvfp4']['us']:.1f} us",
+                  file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args)
+    h = res["nvfp4"]
+    achieved = h["bytes_per_layer"] / (h["us_kernel_events"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(h["GBps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 4),
+        "us_per_step": round(h["ms_per_step"] * 1e3, 1),
+        "frac_of_hbm_peak": round(h["GBps"] / PEAK_HBM_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1 codes, f16 MFMA operands, fp32 accumulate",
+        "data": "synthetic (seeded, drawn on device; no model weights)",
+        "config": {"workload": "qwen3_4b_shapes_128k_ctx_36_layer_nvfp4_decode", "batch": 1,
+                   "context": args.context, "layers": args.layers, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
+                   "block_size": 128, "sink_tokens": 16, "recipe": "bitdecoding-nvfp4 (tau=1.0, c=8)",
+                   "pages_per_partition": ppp, "partitions": parts, "graph": bool(args.graph)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "bdfp4::decode_kernel<false,2,true>",
+                     "bytes_per_launch": h["bytes_per_layer"], "us_per_launch": round(h["us_kernel_events"], 3)},
+        "cpu_baseline": cpu,
+        "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
+        "writer_131072x8": writer,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -247,3 +247,41 @@ def quantize_rows(rows, shift, rotation: int, mode: int, terms: int, codes, scal
 def quantize_p_blocks(pp, mode: int, tau: float, codes, scales, stream=None) -> None:
     _check(lib().bdfp4_quantize_p_blocks(_ptr(pp), int(pp.shape[0]) if pp is not None else 0, mode, float(tau),
                                          _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+class DecodeCall:
+    """bdfp4_decode_attention with its arguments marshalled once; calling it
+    launches on the given (or current) stream. For tight loops and graph
+    capture, where per-call Python work would otherwise dominate."""
+
+    def __init__(self, r: Recipe, cache: PagedCache, q, block_tables, seq_lens, max_seq_len: int,
+                 sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale: float,
+                 pages_per_partition: int, workspace, out):
+        self._keep = (q, block_tables, seq_lens, sink_k, sink_v, tail_k, tail_v, key_shift, workspace, out, cache)
+        self._r = r.replace()
+        self._c = cache.struct()
+        self._fn = lib().bdfp4_decode_attention
+        self._args = [ctypes.byref(self._r), ctypes.byref(self._c), _ptr(q), int(q.shape[0]), int(q.shape[1]),
+                      _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                      _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v), _ptr(key_shift),
+                      float(softmax_scale), int(pages_per_partition), _ptr(workspace),
+                      int(workspace.numel() * workspace.element_size()), _ptr(out)]
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+class Bf16DecodeCall:
+    """bdfp4_bf16_decode_attention with pre-marshalled arguments."""
+
+    def __init__(self, q, k_pages, v_pages, block_tables, seq_lens, max_seq_len: int, softmax_scale: float,
+                 pages_per_partition: int, workspace, out):
+        self._keep = (q, k_pages, v_pages, block_tables, seq_lens, workspace, out)
+        self._fn = lib().bdfp4_bf16_decode_attention
+        self._args = [_ptr(q), int(q.shape[0]), int(q.shape[1]), int(k_pages.shape[1]), _ptr(k_pages),
+                      _ptr(v_pages), int(k_pages.shape[0]), _ptr(block_tables), int(block_tables.shape[1]),
+                      _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(pages_per_partition),
+                      _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out)]
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))

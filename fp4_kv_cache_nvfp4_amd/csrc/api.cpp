@@ -116,7 +116,7 @@ bdfp4_status check_cache(const bdfp4_cache* c) {
 int32_t auto_ppp(int32_t batch, int32_t hkv, int32_t max_seq_len) {
   const int64_t n_full = max_seq_len / 128;
   const int64_t work = (int64_t)batch * hkv * n_full;
-  int64_t ppp = (work + 1023) / 1024;     // about 1024 FP4 workgroups (4 per CU)
+  int64_t ppp = (work + 511) / 512;       // about 512 FP4 workgroups: 2 resident per CU
   if (ppp < 1) ppp = 1;
   if (ppp > 16) ppp = 16;
   return (int32_t)ppp;

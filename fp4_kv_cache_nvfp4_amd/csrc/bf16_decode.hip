@@ -190,12 +190,12 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
   float* part = partial_slot(C, bh, s);
   const bool poisoned = sm.flag != 0;
   const float nan = __builtin_nanf("");
-  *reinterpret_cast<float2*>(part + head * kD + d) = poisoned ? make_float2(nan, nan) : make_float2(o0, o1);
+  pstore2(part + head * kD + d, poisoned ? nan : o0, poisoned ? nan : o1);
   if (tid < 4) {
-    part[512 + tid] = poisoned ? 0.0f : m[tid];
-    part[516 + tid] = poisoned ? 1.0f : sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid];
+    pstore(part + 512 + tid, poisoned ? 0.0f : m[tid]);
+    pstore(part + 516 + tid, poisoned ? 1.0f : sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid]);
   }
-  publish_and_merge(C, &sm.ticket, b, h, nparts);
+  publish_and_merge(C, &sm.ticket, &sm.red[0][0], sm.logit, kMaxTokB * 4, b, h, nparts);
 }
 
 }  // namespace

@@ -27,21 +27,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // ---------------------------------------------------------------- E4M3
 
 // Code of the E4M3 value nearest to v >= 0 (ties to even), saturating at 448.
+// Branch-free: both the normal and the subnormal encodings are formed and one
+// is selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  if (!(v < 448.0f)) return 0x7Eu;
   const uint32_t u = __float_as_uint(v);
-  if (u < 0x3C800000u) {                 // v < 2^-6: subnormal codes m * 2^-9
-    return (uint32_t)__builtin_rintf(v * 512.0f);   // exact scaling, RNE; 8 -> 0x08
-  }
-  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // RNE to 3 mantissa bits
-  return r - (120u << 3);                // rebias 127 -> 7
+  const uint32_t r_norm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);  // RNE to 3 mantissa bits
+  const uint32_t r_sub = (uint32_t)__builtin_rintf(v * 512.0f);   // v < 2^-6: m * 2^-9, exact scaling; 8 -> 0x08
+  const uint32_t r = u < 0x3C800000u ? r_sub : r_norm;
+  return v < 448.0f ? r : 0x7Eu;
 }
 
 // Value of a non-negative finite E4M3 code (exact in float32).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  if (e == 0u) return (float)m * 0.001953125f;      // m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0.001953125f;                      // m * 2^-9
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0u ? sub : nrm;
 }
 
 // ---------------------------------------------------------------- E8M0
@@ -120,7 +121,7 @@ __device__ __forceinline__ uint32_t e2m1_nibble(float x, const E2m1Thr& T) {
 template <int N, bool kSse>
 __device__ __forceinline__ float quant_block(const float* x, float s, uint32_t* packed) {
   const E2m1Thr T = e2m1_thresholds(s);
-  constexpr int kLv = N == 32 ? 6 : 5;
+  constexpr int kLv = N == 32 ? 6 : (N == 16 ? 5 : (N == 8 ? 4 : 3));
   float lvl[kLv];
 #pragma unroll
   for (int w = 0; w < N / 8; ++w) packed[w] = 0u;
@@ -227,13 +228,33 @@ __device__ __forceinline__ void fwht_inlane(float* x) {
   }
 }
 
-// DPP quad permutations (within groups of 4 lanes).
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+// DPP lane permutations: quad_perm within groups of 4 lanes, mirrors
+// within 8 and 16 lanes.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Maximum / sum over aligned groups of 8 or 16 lanes (every lane gets it).
+__device__ __forceinline__ float max8(float v) {
+  v = __builtin_fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  return __builtin_fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+}
+__device__ __forceinline__ float max16(float v) {
+  v = max8(v);
+  return __builtin_fmaxf(v, dpp_f32<kDppRowMirror>(v));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  return v + dpp_f32<kDppRowMirror>(v);
 }
 
 // Cross-lane butterfly stage: the lane whose selector bit is clear keeps

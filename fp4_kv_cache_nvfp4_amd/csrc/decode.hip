@@ -19,26 +19,35 @@
 // (sequence, KV head) merges all partials and resets the ticket.
 //
 // FP4 partition, per workgroup:
-//  * prologue: the 4 query rows are rotated (128-point Hadamard, float32) and
-//    quantized as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32); the
-//    dequantized terms are exact in 16 bits and become the A operands of
-//    v_mfma_f32_16x16x32_{f16,bf16} (rows 0..3 = heads, 12 zero rows); q . mu
-//    is formed from the raw float32 query.
-//  * pass 1 (QK^T): each wave streams whole pages: per 16-token tile one
-//    coalesced 1 KiB run of K codes (16 B per lane) plus one 16 B load of the
-//    page's scales per lane; codes are converted with their block scale
-//    (exactly, see deq_pair) and fed to 4 MFMAs per query term.
-//    Logits sigma * (q_hat . k_hat + q . mu) go to LDS; masked (sink) slots
-//    get -inf.
+//  * the page ids are staged in LDS and each wave starts loading its first K
+//    page before the query prologue;
+//  * prologue: wave g rotates (128-point Hadamard, float32) and quantizes
+//    query row g as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32), 16 lanes
+//    of 8 elements; the dequantized terms are exact in 16 bits and become the
+//    A operands of v_mfma_f32_16x16x32_{f16,bf16} (rows 0..3 = heads, 12 zero
+//    rows). q . mu (raw float32 query, key means) seeds the accumulator.
+//  * pass 1 (QK^T): each wave streams whole pages, the next page in flight
+//    while the current one is used; per 16-token tile a lane holds 16 code
+//    bytes (one coalesced 1 KiB run per wave) and the page's scales come in
+//    one 16-byte load per lane. Logits sigma (q . mu + q_hat . k_hat) go to
+//    LDS [head][token]; sink slots of the first page get -inf.
 //  * partition max over the 4 waves.
 //  * pass 2 (softmax, P quantization, PV): per 32-token chunk the 4 x 32
-//    probabilities p = exp(t - m) are formed two per lane, l accumulates the
-//    unquantized p, p' = c p is quantized per aligned 16-token block
-//    (amax2_or_amax6 with tau, or amax6), and s * e2m1 (exact in 16 bits) is
-//    staged in LDS as the A operand; V codes, stored so that a lane's 32 bytes
-//    hold 8 tokens of one 8-channel group, are converted and permuted
-//    into the B operand of 8 MFMAs (one per output column slab).
+//    probabilities p = exp(t - m) are formed two per lane; l accumulates the
+//    unquantized p; p' = c p is quantized per aligned 16-token block
+//    (amax2_or_amax6 with tau, or amax6) and s * e2m1 (exact in 16 bits) is
+//    staged in LDS as the A operand. V codes come as B operands of 8 MFMAs
+//    (one per output channel slab).
 //  * the 4 waves' o and l are summed in LDS; o is divided by c.
+//
+// Operand construction. The scaled FP4 converts of gfx950 apply only the
+// exponent of their float32 scale. MXFP4 scales are powers of two and convert
+// exactly to bf16 in one step. For NVFP4 the codes are converted with scale 1
+// to f16 and multiplied, two at a time, by their E4M3 scales converted to f16
+// by the hardware E4M3 convert; the product has at most 6 significant bits and
+// lies in [2^-10, 2688], so it is exact in f16. The NVFP4 V page stores tokens
+// t, t+1 of one channel in a byte, so a converted pair is directly one 32-bit
+// word of the PV B operand.
 #include "codec.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -62,15 +71,7 @@ struct DecArgs {
   float* partials;
 };
 
-// ------------------------------------------------------------ small helpers
-
-// The scaled FP4 converts of gfx950 apply only the exponent of their float32
-// scale (an E8M0 scale). MXFP4 scales are powers of two and convert exactly
-// to bf16. An E4M3 scale s = mant * 2^e is split: the codes are converted to
-// f16 with 2^e, then multiplied by mant (at most 4 significant bits) in
-// packed f16; the product has at most 6 significant bits and lies in
-// [2^-10, 2688], so it is exact in f16. NVFP4 operands are therefore f16,
-// MXFP4 operands bf16.
+// ------------------------------------------------------------ converts
 
 __device__ __forceinline__ uint32_t cvt_bf16_pair(uint32_t w, float s, int byte) {
   bf16x2_t r;
@@ -83,54 +84,23 @@ __device__ __forceinline__ uint32_t cvt_bf16_pair(uint32_t w, float s, int byte)
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ f16x2_t cvt_f16_pair(uint32_t w, float s, int byte) {
+// E2M1 codes of byte `byte` of w as an f16 pair (grid values, exact).
+__device__ __forceinline__ f16x2_t grid_f16_pair(uint32_t w, int byte) {
   switch (byte) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3);
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
   }
 }
 
-// An element scale as (power of two for the convert, multiplier pair).
-struct ElemScale {
-  float p2;
-  f16x2_t mant;
-};
-
-__device__ __forceinline__ ElemScale elem_scale(uint32_t code, bool mx) {
-  ElemScale r;
-  if (mx) {
-    r.p2 = pow2_f32((int)code - 127);
-    r.mant = (f16x2_t){(_Float16)1.0f, (_Float16)1.0f};
-    return r;
-  }
-  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
-  const float mf = e == 0u ? (float)m * 0.125f : 1.0f + (float)m * 0.125f;   // exact
-  r.p2 = e == 0u ? 0.015625f : __uint_as_float((e + 120u) << 23);           // 2^-6 or 2^(e-7)
-  const _Float16 mh = (_Float16)mf;                                          // exact
-  r.mant = (f16x2_t){mh, mh};
-  return r;
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) as an exact f16 pair.
+__device__ __forceinline__ f16x2_t e4m3_pair_f16(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
 }
 
-// Dequantized pair (elements 2 byte, 2 byte + 1 of word w) as two 16-bit values.
-template <bool kMx>
-__device__ __forceinline__ uint32_t deq_pair(uint32_t w, const ElemScale& sc, int byte) {
-  if (kMx) return cvt_bf16_pair(w, sc.p2, byte);
-  const f16x2_t v = cvt_f16_pair(w, sc.p2, byte) * sc.mant;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// 8 codes of one word (element 2i in the low nibble of byte i), dequantized.
-template <bool kMx>
-__device__ __forceinline__ u32x4_t deq_word(uint32_t w, const ElemScale& sc) {
-  u32x4_t r;
-  r[0] = deq_pair<kMx>(w, sc, 0);
-  r[1] = deq_pair<kMx>(w, sc, 1);
-  r[2] = deq_pair<kMx>(w, sc, 2);
-  r[3] = deq_pair<kMx>(w, sc, 3);
-  return r;
-}
+__device__ __forceinline__ uint32_t u32_of(f16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
 // D += A B on 16x16x32 tiles: bf16 operands for MXFP4, f16 for NVFP4.
 template <bool kMx>
@@ -149,28 +119,26 @@ __device__ __forceinline__ uint32_t op16(float v) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
-__device__ __forceinline__ uint8_t byte_of(const uint4& v, int i) {
-  const uint32_t w = i < 4 ? v.x : (i < 8 ? v.y : (i < 12 ? v.z : v.w));
-  return (uint8_t)(w >> (8 * (i & 3)));
-}
-
 // ------------------------------------------------------------ shared memory
 
 struct Smem {
-  float logit[kMaxTok * 4];                 // [token][head], reused for o reduction
-  uint16_t qhat[2][4][kD];                  // bf16 bits of the dequantized terms
-  float q[4][kD];                           // raw float32 query
+  float logit[4 * kMaxTok];                 // [head][token]; reused for the o reduction
+  uint16_t qhat[2][4][kD];                  // 16-bit dequantized query terms
+  float q[4][kD];                           // raw float32 query (BF16 partition)
   float qmu[4];
-  uint16_t p[4][4][32];                     // per wave: bf16 P_hat staging [head][token]
+  uint16_t p[4][4][32];                     // per wave: P_hat staging [head][token]
   float red[4][4];                          // per wave, per head
-  float m[4];
   float lsum[4][4];
-  int flag;                                 // invalid page seen
+  int page[kMaxPpp];                        // physical pages of the partition (-1: invalid)
   int ticket;
 };
 
@@ -193,6 +161,9 @@ __device__ __forceinline__ float* partial_ptr(const DecArgs& A, int bh, int s) {
 
 // ------------------------------------------------------------ BF16 partition
 
+// Tokens [0, min(S, L)) from the sink buffer and [max(S, 128 n), L) from the
+// tail page: exact float32 attention of the raw query, thread = token for the
+// logits, thread = (head, channel pair) for o.
 __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x;
@@ -201,7 +172,6 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
   const int tail_lo = S > kPage * n_full ? S : kPage * n_full;
   const int ntail = L > tail_lo ? L - tail_lo : 0;
   const int nb = nsink + ntail;                      // <= 112 + 127 < 256
-  // raw query
   for (int i = tid; i < 4 * kD; i += 256) {
     const int g = i >> 7, d = i & 127;
     sm.q[g][d] = bf16_lo(P.q[((size_t)b * P.hq + h * kGroup + g) * kD + d]);
@@ -217,8 +187,12 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
       krow = P.tail_k + (((size_t)b * P.hkv + h) * kPage + (tail_lo - kPage * n_full) + (tok - nsink)) * kD;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const uint4* k4 = reinterpret_cast<const uint4*>(krow);
+    uint4 kw[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) kw[c] = k4[c];      // the whole row in flight at once
+#pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const uint4 w = k4[c];
+      const uint4 w = kw[c];
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -231,7 +205,6 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
 #pragma unroll
     for (int g = 0; g < 4; ++g) t[g] = P.softmax_scale * acc[g];
   }
-  // max per head
   float mx[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -249,7 +222,6 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
 #pragma unroll
   for (int g = 0; g < 4; ++g)
     m[g] = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
-  // probabilities into LDS [token][head]
   float ls[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -264,9 +236,9 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
 #pragma unroll
     for (int g = 0; g < 4; ++g) sm.lsum[wave][g] = ls[g];
   }
-  // o[head][d] = sum_tok p v ; thread = (head, channel pair)
   const int head = tid >> 6, d = (tid & 63) * 2;
   float o0 = 0.f, o1 = 0.f;
+#pragma unroll 16
   for (int j = 0; j < nb; ++j) {
     const uint16_t* vrow;
     if (j < nsink)
@@ -280,67 +252,181 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
   }
   __syncthreads();
   float* part = partial_ptr(A, b * P.hkv + h, 0);
-  *reinterpret_cast<float2*>(part + head * kD + d) = make_float2(o0, o1);
+  pstore2(part + head * kD + d, o0, o1);
   if (tid < 4) {
-    part[512 + tid] = nb > 0 ? m[tid] : kNegInf;
-    part[516 + tid] = sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid];
+    pstore(part + 512 + tid, nb > 0 ? m[tid] : kNegInf);
+    pstore(part + 516 + tid, sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid]);
+  }
+}
+
+// ------------------------------------------------------------ query prologue
+
+// DPP row controls (16-lane rows): shift left / right by 4, rotate by 8.
+constexpr int kDppRowShl4 = 0x104;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowRor8 = 0x128;
+
+// Butterfly stages with partner lane ^ 4 and lane ^ 8 inside a 16-lane row.
+__device__ __forceinline__ void fwht_xlane_4_8(float* x, int i) {
+  const bool up4 = (i & 4) != 0, up8 = (i & 8) != 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float p = shfl_xor(x[k], 4);
+    x[k] = up4 ? __fsub_rn(p, x[k]) : __fadd_rn(x[k], p);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float p = shfl_xor(x[k], 8);
+    x[k] = up8 ? __fsub_rn(p, x[k]) : __fadd_rn(x[k], p);
+  }
+}
+
+// The raw query elements and key means of lane i of row g (loaded first, so
+// their latency overlaps the page-id staging and the first page loads).
+struct QueryIn {
+  uint4 q;
+  float4 mu0, mu1;
+};
+
+__device__ __forceinline__ QueryIn query_load(const DecodeLaunch& P, int b, int h, int g, int i) {
+  QueryIn in;
+  in.q = *reinterpret_cast<const uint4*>(P.q + ((size_t)b * P.hq + h * kGroup + g) * kD + 8 * i);
+  if (P.key_smoothing) {
+    const float4* mu4 = reinterpret_cast<const float4*>(P.key_shift + h * kD + 8 * i);
+    in.mu0 = mu4[0];
+    in.mu1 = mu4[1];
+  } else {
+    in.mu0 = in.mu1 = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  return in;
+}
+
+// Query row g of the group on 16 lanes (lane i holds elements [8i, 8i+8)):
+// q . mu, the Hadamard rotation (stages 1, 2, 4 in-lane, 8 .. 64 across
+// lanes by DPP), then Q1 and the residual Q2, dequantized into LDS. The same
+// float32 operations in the same order as the page writer's key path and the
+// row quantizer, so the codes are identical.
+template <bool kMx, int kTerms>
+__device__ __forceinline__ void query_row(const DecodeLaunch& P, const QueryIn& in, Smem& sm, int g, int i) {
+  float x[8];
+  const uint32_t ww[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16_lo(ww[k]);
+    x[2 * k + 1] = bf16_hi(ww[k]);
+  }
+  const float mu[8] = {in.mu0.x, in.mu0.y, in.mu0.z, in.mu0.w, in.mu1.x, in.mu1.y, in.mu1.z, in.mu1.w};
+  float dot = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dot = fmaf(x[k], mu[k], dot);
+  dot = sum16(dot);
+  if (i == 0) sm.qmu[g] = dot;
+  if (P.rotation) {
+    fwht_inlane<8>(x);
+    fwht_xlane<8, kDppQuadXor1>(x, (i & 1) != 0);
+    fwht_xlane<8, kDppQuadXor2>(x, (i & 2) != 0);
+    fwht_xlane_4_8(x, i);
+    const float c = inv_sqrt_d();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], c);
+  }
+#pragma unroll
+  for (int term = 0; term < kTerms; ++term) {
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = __builtin_fmaxf(a, __builtin_fabsf(x[k]));
+    float s;
+    uint32_t pk;
+    if (kMx) {
+      // 32-element block = this quad of lanes; candidates E_hi, E_hi - 1
+      a = __builtin_fmaxf(a, dpp_f32<kDppQuadXor1>(a));
+      a = __builtin_fmaxf(a, dpp_f32<kDppQuadXor2>(a));
+      int ehi = a > 0.0f ? mx_exponent_hi(a) : -127;
+      ehi = ehi < -127 ? -127 : (ehi > 127 ? 127 : ehi);
+      const int elo = ehi - 1 < -127 ? -127 : ehi - 1;
+      uint32_t phi, plo;
+      float ehi_err = quant_block<8, true>(x, pow2_f32(ehi), &phi);
+      float elo_err = quant_block<8, true>(x, pow2_f32(elo), &plo);
+      // the 32-element tree: ((t0 + t1) + (t2 + t3)) over the quad's subtrees
+      ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppQuadXor1>(ehi_err));
+      ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppQuadXor2>(ehi_err));
+      elo_err = __fadd_rn(elo_err, dpp_f32<kDppQuadXor1>(elo_err));
+      elo_err = __fadd_rn(elo_err, dpp_f32<kDppQuadXor2>(elo_err));
+      const bool take_lo = (elo_err < ehi_err) && (elo < ehi) && a > 0.0f;
+      s = a > 0.0f ? pow2_f32(take_lo ? elo : ehi) : 0.0f;
+      pk = a > 0.0f ? (take_lo ? plo : phi) : 0u;
+    } else {
+      // 16-element block = this pair of lanes
+      a = __builtin_fmaxf(a, dpp_f32<kDppQuadXor1>(a));
+      s = e4m3_value(e4m3_encode(a / 6.0f));
+      quant_block<8, false>(x, s, &pk);
+    }
+    float deq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t nib = (pk >> (4 * k)) & 0xFu;
+      const float gv = __fmul_rn(e2m1_grid(nib & 7u), s);
+      deq[k] = (nib & 8u) ? -gv : gv;
+    }
+    uint4 o;
+    o.x = op16<kMx>(deq[0]) | (op16<kMx>(deq[1]) << 16);
+    o.y = op16<kMx>(deq[2]) | (op16<kMx>(deq[3]) << 16);
+    o.z = op16<kMx>(deq[4]) | (op16<kMx>(deq[5]) << 16);
+    o.w = op16<kMx>(deq[6]) | (op16<kMx>(deq[7]) << 16);
+    *reinterpret_cast<uint4*>(&sm.qhat[term][g][8 * i]) = o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = __fsub_rn(x[k], deq[k]);
+  }
+}
+
+// ------------------------------------------------------------ page loads
+
+// One page of K for one wave: lane l holds the 16 code bytes of tile t at
+// t * 1024 + 16 l (token l & 15, channels 32 (l >> 4) .. +32) and the scales
+// of its (token, channel group) for all 8 tiles (16 B NVFP4 / 8 B MXFP4).
+struct KPage {
+  uint4 code[8];
+  uint4 sc;
+};
+
+// One page of V for one wave: chunk c (32 tokens) of lane l is the 32 bytes at
+// c * 2048 + 32 l (tokens 8 (l >> 4) .. +8 of the chunk, channels 8 (l & 15)
+// .. +8) and its 8 token scales.
+struct VPage {
+  uint4 code[8];
+  uint2 sc[4];
+};
+
+template <bool kMx>
+__device__ __forceinline__ void load_k(KPage& k, const DecodeLaunch& P, size_t blk, int lane) {
+  const uint4* kc = reinterpret_cast<const uint4*>(P.k_codes + blk * 8192) + lane;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) k.code[t] = kc[t * 64];
+  if (kMx) {
+    const uint2 t2 = *reinterpret_cast<const uint2*>(P.k_scales + blk * 512 + lane * 8);
+    k.sc = make_uint4(t2.x, t2.y, 0u, 0u);
+  } else {
+    k.sc = *reinterpret_cast<const uint4*>(P.k_scales + blk * 1024 + lane * 16);
+  }
+}
+
+template <bool kMx>
+__device__ __forceinline__ void load_v(VPage& v, const DecodeLaunch& P, size_t blk, int lane) {
+  const uint4* vc = reinterpret_cast<const uint4*>(P.v_codes + blk * 8192 + lane * 32);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v.code[2 * c] = vc[c * 128];
+    v.code[2 * c + 1] = vc[c * 128 + 1];
+  }
+  const int kg = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int sidx = kMx ? ((c * 4 + kg) * 4 + (n >> 2)) * 8 : ((c * 4 + kg) * 8 + (n >> 1)) * 8;
+    v.sc[c] = *reinterpret_cast<const uint2*>(P.v_scales + blk * (kMx ? 512 : 1024) + sidx);
   }
 }
 
 // ------------------------------------------------------------ FP4 partition
-
-// Query prologue, run by lanes 0..15 of wave 0 (row g = tid >> 2, quarter q =
-// tid & 3): q . mu from the raw query, then the rotated row quantized as Q1
-// and the residual as Q2; the dequantized terms (exact in bf16) go to LDS.
-template <bool kMx, int kTerms>
-__device__ __forceinline__ void query_prologue(const DecodeLaunch& P, Smem& sm, int b, int h, int tid) {
-  const int g = tid >> 2, q = tid & 3;
-  const uint16_t* qrow = P.q + ((size_t)b * P.hq + h * kGroup + g) * kD;
-  const uint4* q4 = reinterpret_cast<const uint4*>(qrow + 32 * q);
-  uint4 w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = q4[k];
-  float x[32];
-  widen32(w, x);
-  float dot = 0.0f;
-  if (P.key_smoothing) {
-    const float* mu = P.key_shift + h * kD + 32 * q;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) dot = fmaf(x[i], mu[i], dot);
-  }
-  dot += dpp_f32<kDppQuadXor1>(dot);
-  dot += dpp_f32<kDppQuadXor2>(dot);
-  if (q == 0) sm.qmu[g] = P.key_smoothing ? dot : 0.0f;
-  if (P.rotation) rotate_row_quad(x, q);
-#pragma unroll
-  for (int term = 0; term < 2; ++term) {
-    uint32_t pk[4];
-    float deq[32];
-    if (term < kTerms) {
-      if (kMx) {
-        const uint32_t sc = mx_block(x, pk);
-        const float sv = pow2_f32((int)sc - 127);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) deq8(pk[k], sv, deq + 8 * k);
-      } else {
-        const uint32_t s0 = nv_block<false>(x, pk);
-        const uint32_t s1 = nv_block<false>(x + 16, pk + 2);
-        deq8(pk[0], e4m3_value(s0), deq);
-        deq8(pk[1], e4m3_value(s0), deq + 8);
-        deq8(pk[2], e4m3_value(s1), deq + 16);
-        deq8(pk[3], e4m3_value(s1), deq + 24);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) deq[i] = 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      sm.qhat[term][g][32 * q + i] = (uint16_t)op16<kMx>(deq[i]);   // exact
-      x[i] = __fsub_rn(x[i], deq[i]);
-    }
-  }
-}
 
 template <bool kMx, int kTerms, bool kUnder>
 __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, int L, int n_full) {
@@ -350,18 +436,27 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   const int p1 = min(n_full, s * P.ppp);
   const int npg = p1 - p0;
   const int lo = max(P.sink, kPage * p0);
-  const int sbytes = kMx ? 512 : 1024;
   const size_t hkv = P.hkv;
-  const int32_t* bt = P.block_tables + (size_t)b * P.max_pages_per_seq + p0;
+  QueryIn qin;
+  if (lane < 16) qin = query_load(P, b, h, wave, lane);
 
-  if (tid == 0) sm.flag = 0;
+  if (tid < npg) {
+    const int ph = P.block_tables[(size_t)b * P.max_pages_per_seq + p0 + tid];
+    sm.page[tid] = (ph < 0 || ph >= P.num_pages) ? -1 : ph;
+  }
+  __syncthreads();
+  auto blk_of = [&](int pi) -> size_t {
+    const int ph = sm.page[pi];
+    return (size_t)(ph < 0 ? 0 : ph) * hkv + h;
+  };
 
-  // ---- prologue: query rows -> rotated, two-term quantized, bf16 staging
-  if (tid < 16) query_prologue<kMx, kTerms>(P, sm, b, h, tid);
+  KPage kcur, knxt;
+  if (wave < npg) load_k<kMx>(kcur, P, blk_of(wave), lane);
+  if (lane < 16) query_row<kMx, kTerms>(P, qin, sm, wave, lane);
   __syncthreads();
 
-  // ---- A operands: lane (row = lane & 15, k-group kg = lane >> 4); MFMA c
-  // covers d = 32 kg + 8 c + [0, 8)
+  // A operands: lane (row = lane & 15, k-group kg = lane >> 4); MFMA c covers
+  // channels 32 kg + 8 c + [0, 8)
   const int row = lane & 15, kg = lane >> 4;
   u32x4_t aq[2][4];
 #pragma unroll
@@ -376,43 +471,39 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
       aq[term][c] = v;
     }
   }
-  float qmu[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) qmu[g] = sm.qmu[g];
+  const f32x4_t acc0 = {sm.qmu[0], sm.qmu[1], sm.qmu[2], sm.qmu[3]};
   const float sigma = P.softmax_scale;
+  float* logit = sm.logit;
 
   // ---- pass 1: logits
   float mrun[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-  bool bad = false;
   for (int pi = wave; pi < npg; pi += 4) {
-    int phys = bt[pi];
-    if (phys < 0 || phys >= P.num_pages) { bad = true; phys = 0; }
-    const size_t blk = (size_t)phys * hkv + h;
-    const uint4* kc = reinterpret_cast<const uint4*>(P.k_codes + blk * 8192) + lane;
-    uint4 code[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) code[t] = kc[t * 64];
-    uint4 sc4;
-    if (kMx) {
-      const uint2 t2 = *reinterpret_cast<const uint2*>(P.k_scales + blk * sbytes + lane * 8);
-      sc4 = make_uint4(t2.x, t2.y, 0u, 0u);
-    } else {
-      sc4 = *reinterpret_cast<const uint4*>(P.k_scales + blk * sbytes + lane * 16);
-    }
+    if (pi + 4 < npg) load_k<kMx>(knxt, P, blk_of(pi + 4), lane);
+    const bool has_sink = kPage * (p0 + pi) < lo;          // uniform per page
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      ElemScale s_lo, s_hi;
-      if (kMx) {
-        s_lo = s_hi = elem_scale(byte_of(sc4, t), true);
-      } else {
-        s_lo = elem_scale(byte_of(sc4, 2 * t), false);
-        s_hi = elem_scale(byte_of(sc4, 2 * t + 1), false);
-      }
-      const uint32_t cw[4] = {code[t].x, code[t].y, code[t].z, code[t].w};
       u32x4_t bk[4];
+      if (kMx) {
+        const uint32_t sb = (word_of(kcur.sc, t >> 2) >> (8 * (t & 3))) & 0xFFu;
+        const float sv = pow2_f32((int)sb - 127);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bk[c] = deq_word<kMx>(cw[c], c < 2 ? s_lo : s_hi);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t cw = word_of(kcur.code[t], c);
+          bk[c] = (u32x4_t){cvt_bf16_pair(cw, sv, 0), cvt_bf16_pair(cw, sv, 1), cvt_bf16_pair(cw, sv, 2),
+                            cvt_bf16_pair(cw, sv, 3)};
+        }
+      } else {
+        const f16x2_t sp = e4m3_pair_f16(word_of(kcur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
+        const f16x2_t slo = {sp[0], sp[0]}, shi = {sp[1], sp[1]};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t cw = word_of(kcur.code[t], c);
+          const f16x2_t sc = c < 2 ? slo : shi;
+          bk[c] = (u32x4_t){u32_of(grid_f16_pair(cw, 0) * sc), u32_of(grid_f16_pair(cw, 1) * sc),
+                            u32_of(grid_f16_pair(cw, 2) * sc), u32_of(grid_f16_pair(cw, 3) * sc)};
+        }
+      }
+      f32x4_t acc = acc0;
 #pragma unroll
       for (int term = 0; term < kTerms; ++term) {
 #pragma unroll
@@ -420,27 +511,26 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
       }
       if (lane < 16) {
         const int local = pi * kPage + t * 16 + lane;        // token - 128 p0
-        const bool live = kPage * p0 + local >= lo;
-        float4 lg;
-        lg.x = live ? sigma * (acc[0] + qmu[0]) : kNegInf;
-        lg.y = live ? sigma * (acc[1] + qmu[1]) : kNegInf;
-        lg.z = live ? sigma * (acc[2] + qmu[2]) : kNegInf;
-        lg.w = live ? sigma * (acc[3] + qmu[3]) : kNegInf;
-        *reinterpret_cast<float4*>(&sm.logit[local * 4]) = lg;
-        mrun[0] = fmaxf(mrun[0], lg.x);
-        mrun[1] = fmaxf(mrun[1], lg.y);
-        mrun[2] = fmaxf(mrun[2], lg.z);
-        mrun[3] = fmaxf(mrun[3], lg.w);
+        float lg[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) lg[g] = sigma * acc[g];
+        if (has_sink && kPage * p0 + local < lo) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) lg[g] = kNegInf;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          logit[g * kMaxTok + local] = lg[g];
+          mrun[g] = fmaxf(mrun[g], lg[g]);
+        }
       }
     }
+    kcur = knxt;
   }
-  if (bad) sm.flag = 1;
+  VPage vcur, vnxt;
+  if (wave < npg) load_v<kMx>(vcur, P, blk_of(wave), lane);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float v = mrun[g];
-    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
-    mrun[g] = v;
-  }
+  for (int g = 0; g < 4; ++g) mrun[g] = max16(mrun[g]);
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) sm.red[wave][g] = mrun[g];
@@ -454,82 +544,82 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   // ---- pass 2: P, PV
   const int ph = lane >> 4;          // head of this lane in the P step
   const int pj = lane & 15;          // token pair within the 32-token chunk
-  const float mh = m[ph];
+  const float mh = ph == 0 ? m[0] : (ph == 1 ? m[1] : (ph == 2 ? m[2] : m[3]));
   const float cf = (float)P.c;
   const float tau = P.tau;
+  const float* lrow = logit + ph * kMaxTok;
   float lacc = 0.0f;
   f32x4_t acco[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acco[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  const int n = lane & 15;           // V: 8-channel group (d = 8n .. 8n+7)
   for (int pi = wave; pi < npg; pi += 4) {
-    int phys = bt[pi];
-    if (phys < 0 || phys >= P.num_pages) phys = 0;
-    const size_t blk = (size_t)phys * hkv + h;
-    const uint8_t* vcb = P.v_codes + blk * 8192;
-    const uint8_t* vsb = P.v_scales + blk * sbytes;
-#pragma unroll 1
+    if (pi + 4 < npg) load_v<kMx>(vnxt, P, blk_of(pi + 4), lane);
+#pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-      // V loads for this chunk (issued first)
-      const uint4* vc = reinterpret_cast<const uint4*>(vcb + ch * 2048 + lane * 32);
-      const uint4 v0 = vc[0], v1 = vc[1];
-      const int sidx = kMx ? ((ch * 4 + kg) * 4 + (n >> 2)) * 8 : ((ch * 4 + kg) * 8 + (n >> 1)) * 8;
-      const uint2 vs = *reinterpret_cast<const uint2*>(vsb + sidx);
       // probabilities of tokens (2 pj, 2 pj + 1), head ph
       const int local = pi * kPage + ch * 32 + 2 * pj;
-      const float t0 = sm.logit[local * 4 + ph];
-      const float t1 = sm.logit[(local + 1) * 4 + ph];
-      const float e0 = (mh == kNegInf) ? 0.0f : __expf(t0 - mh);
-      const float e1 = (mh == kNegInf) ? 0.0f : __expf(t1 - mh);
+      const float2 tt = *reinterpret_cast<const float2*>(lrow + local);
+      const float e0 = (mh == kNegInf) ? 0.0f : __expf(tt.x - mh);
+      const float e1 = (mh == kNegInf) ? 0.0f : __expf(tt.y - mh);
       lacc += e0 + e1;
       const float q0 = cf * e0, q1 = cf * e1;
-      float a = fmaxf(q0, q1);
-      a = fmaxf(a, shfl_xor(a, 1));
-      a = fmaxf(a, shfl_xor(a, 2));
-      a = fmaxf(a, shfl_xor(a, 4));
+      const float a = max8(fmaxf(q0, q1));     // the aligned 16-token block is 8 lanes
       const uint32_t scode = e4m3_encode((kUnder && a < tau) ? a * 0.5f : a / 6.0f);
       const float sv = e4m3_value(scode);
       const E2m1Thr T = e2m1_thresholds(sv);
       const float g0 = T.zero ? 0.0f : __fmul_rn(e2m1_grid(e2m1_mag(q0, T)), sv);
       const float g1 = T.zero ? 0.0f : __fmul_rn(e2m1_grid(e2m1_mag(q1, T)), sv);
-      const uint32_t pair = op16<kMx>(g0) | (op16<kMx>(g1) << 16);
-      *reinterpret_cast<uint32_t*>(&sm.p[wave][ph][2 * pj]) = pair;
+      *reinterpret_cast<uint32_t*>(&sm.p[wave][ph][2 * pj]) = op16<kMx>(g0) | (op16<kMx>(g1) << 16);
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging visible to the wave
       __builtin_amdgcn_wave_barrier();
-      u32x4_t av = {0u, 0u, 0u, 0u};
+      u32x4_t ap = {0u, 0u, 0u, 0u};
       if (row < 4) {
         const uint4 t = *reinterpret_cast<const uint4*>(&sm.p[wave][row][8 * kg]);
-        av[0] = t.x; av[1] = t.y; av[2] = t.z; av[3] = t.w;
+        ap[0] = t.x; ap[1] = t.y; ap[2] = t.z; ap[3] = t.w;
       }
-      const u32x4_t ap = av;
-      // V operand: token i = 8 kg + ii of the chunk, channels 8n .. 8n+7
+      const uint4 v0 = vcur.code[2 * ch], v1 = vcur.code[2 * ch + 1];
+      const uint2 vs = vcur.sc[ch];
       const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      uint32_t x[8][4];   // x[ii][b] = bf16 pair (channels 8n+2b, 8n+2b+1) of token ii
+      if (kMx) {
+        // element pairs per byte: vw[ii] = token 8 kg + ii, channels 8n .. 8n+7
+        uint32_t x[8][4];
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const uint32_t sb = (ii < 4 ? (vs.x >> (8 * ii)) : (vs.y >> (8 * (ii - 4)))) & 0xFFu;
-        const ElemScale svv = elem_scale(sb, kMx);
+        for (int ii = 0; ii < 8; ++ii) {
+          const uint32_t sb = (ii < 4 ? (vs.x >> (8 * ii)) : (vs.y >> (8 * (ii - 4)))) & 0xFFu;
+          const float svv = pow2_f32((int)sb - 127);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) x[ii][bb] = deq_pair<kMx>(vw[ii], svv, bb);
-      }
+          for (int bb = 0; bb < 4; ++bb) x[ii][bb] = cvt_bf16_pair(vw[ii], svv, bb);
+        }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int bb = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t bv;
+        for (int j = 0; j < 8; ++j) {
+          const int bb = j >> 1;
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          u32x4_t bv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bv[r] = __builtin_amdgcn_perm(x[2 * r + 1][bb], x[2 * r][bb], sel);
-        acco[j] = mfma<kMx>(ap, bv, acco[j]);
+          for (int r = 0; r < 4; ++r) bv[r] = __builtin_amdgcn_perm(x[2 * r + 1][bb], x[2 * r][bb], sel);
+          acco[j] = mfma<kMx>(ap, bv, acco[j]);
+        }
+      } else {
+        // token pairs per byte: byte r of vw[j] = tokens 8 kg + 2r, +1 at channel 8n + j
+        const f16x2_t sp[4] = {e4m3_pair_f16(vs.x, false), e4m3_pair_f16(vs.x, true),
+                               e4m3_pair_f16(vs.y, false), e4m3_pair_f16(vs.y, true)};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x4_t bv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bv[r] = u32_of(grid_f16_pair(vw[j], r) * sp[r]);
+          acco[j] = mfma<kMx>(ap, bv, acco[j]);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
+    vcur = vnxt;
   }
-  // l per head: lanes of one head are a 16-lane row
-  for (int o = 8; o >= 1; o >>= 1) lacc += shfl_xor(lacc, o);
+  lacc = sum16(lacc);                // lanes of one head are a 16-lane row
   if (pj == 0) sm.lsum[wave][ph] = lacc;
-  __syncthreads();   // all waves done with logits: reuse it for o
-  float* so = sm.logit;   // [wave][head][128]
+  __syncthreads();                   // all waves done with the logits: reuse for o
+  float* so = sm.logit;              // [wave][head][128]
   if (lane < 16) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -540,21 +630,21 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   }
   __syncthreads();
   const int head = tid >> 6, d = (tid & 63) * 2;
-  const float invc = 1.0f / cf;    // exact (c is a power of two)
+  const float invc = 1.0f / cf;      // exact (c is a power of two)
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     o0 += so[(w * 4 + head) * kD + d];
     o1 += so[(w * 4 + head) * kD + d + 1];
   }
+  bool poisoned = false;
+  for (int i = 0; i < npg; ++i) poisoned |= sm.page[i] < 0;
   float* part = partial_ptr(A, b * P.hkv + h, s);
-  const bool poisoned = sm.flag != 0;
   const float nan = __builtin_nanf("");
-  *reinterpret_cast<float2*>(part + head * kD + d) =
-      poisoned ? make_float2(nan, nan) : make_float2(o0 * invc, o1 * invc);
+  pstore2(part + head * kD + d, poisoned ? nan : o0 * invc, poisoned ? nan : o1 * invc);
   if (tid < 4) {
-    part[512 + tid] = poisoned ? 0.0f : m[tid];
-    part[516 + tid] = poisoned ? 1.0f : sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid];
+    pstore(part + 512 + tid, poisoned ? 0.0f : m[tid]);
+    pstore(part + 516 + tid, poisoned ? 1.0f : sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid]);
   }
 }
 
@@ -578,7 +668,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     bf16_partition(A, sm, b, h, L, n_full);
   else
     fp4_partition<kMx, kTerms, kUnder>(A, sm, b, h, s, L, n_full);
-  publish_and_merge(merge_ctx(A), &sm.ticket, b, h, nparts + 1);
+  publish_and_merge(merge_ctx(A), &sm.ticket, &sm.red[0][0], sm.logit, 4 * kMaxTok, b, h, nparts + 1);
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {

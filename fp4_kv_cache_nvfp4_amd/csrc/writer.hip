@@ -111,11 +111,39 @@ __global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
         s_scales[((chunk * 4 + qq) * 8 + 2 * q) * 8 + i8] = (uint8_t)s0;
         s_scales[((chunk * 4 + qq) * 8 + 2 * q + 1) * 8 + i8] = (uint8_t)s1;
       }
-      // the lane's 4 words are d-octets 4q .. 4q+3 of token t
+      if (kVMx) {
+        // element pairs per byte: the lane's 4 words are d-octets 4q .. 4q+3 of token t
 #pragma unroll
-      for (int o = 0; o < 4; ++o) {
-        const int oct = 4 * q + o;
-        *reinterpret_cast<uint32_t*>(&s_codes[(((chunk * 4 + qq) * 16 + oct) * 8 + i8) * 4]) = pk[o];
+        for (int o = 0; o < 4; ++o) {
+          const int oct = 4 * q + o;
+          *reinterpret_cast<uint32_t*>(&s_codes[(((chunk * 4 + qq) * 16 + oct) * 8 + i8) * 4]) = pk[o];
+        }
+      } else {
+        // token pairs per byte: tokens t (even) and t + 1 live in lanes l and
+        // l ^ 4; the even lane writes channels [32q, 32q+16), the odd lane
+        // [32q+16, 32q+32), low nibble = even token
+        uint32_t other[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) other[w] = (uint32_t)__shfl_xor((int)pk[w], 4, 64);
+        const bool odd = (t & 1) != 0;
+        const int te = t & ~1;
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const int w = odd ? 2 + w2 : w2;
+          const uint32_t mine = odd ? pk[2 + w2] : pk[w2];          // static indices only
+          const uint32_t theirs = odd ? other[2 + w2] : other[w2];
+          const uint32_t lo_tok = odd ? theirs : mine;
+          const uint32_t hi_tok = odd ? mine : theirs;
+          const uint32_t even_b = (lo_tok & 0x0F0F0F0Fu) | ((hi_tok & 0x0F0F0F0Fu) << 4);   // elements 0,2,4,6
+          const uint32_t odd_b = ((lo_tok >> 4) & 0x0F0F0F0Fu) | (hi_tok & 0xF0F0F0F0u);    // elements 1,3,5,7
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = 32 * q + 8 * w + e;
+            const uint32_t byte = ((e & 1) ? odd_b : even_b) >> (8 * (e >> 1));
+            s_codes[(te >> 5) * 2048 + (((te >> 3) & 3) * 16 + (d >> 3)) * 32 + (d & 7) * 4 + ((te & 7) >> 1)] =
+                (uint8_t)byte;
+          }
+        }
       }
     }
   }

@@ -232,3 +232,87 @@ def write_workload(seed: int = 0, tokens: int = 131072, num_kv_heads: int = 8,
     ids = rng.permutation(n) if shuffle else np.arange(n)
     mu = bf16_to_f32(k).astype(np.float64).mean(axis=0).astype(np.float32)
     return WriteWorkload("prefill_write_128k_8kv", seed, k, v, ids.astype(np.int32), n, mu)
+
+
+def torch_decode_layer(layer: int, seq_len: int = 131072, num_q_heads: int = 32, num_kv_heads: int = 8,
+                       sink_tokens: int = 16, device="cuda"):
+    """One layer of the long-context decode drawn on the device with torch's
+    generator (seed = layer): same recipe as ``decode_workload(..., "qwen")``
+    (K, V, Q ~ N(0,1) in bf16; Student-t(3) offsets, formed as Z / sqrt(chi2_3 / 3),
+    on 6 seeded key channels per KV head; mu = float32(mean of K in float64);
+    one sequence; random permutation of a pool of ceil(L/128) pages).
+    Returns a dict of device tensors."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_000 + layer)
+    hkv = num_kv_heads
+    ch = torch.stack([torch.randperm(D, generator=g, device=device)[:6] for _ in range(hkv)])
+    z = torch.randn((hkv, 6), generator=g, device=device)
+    chi = (torch.randn((hkv, 6, 3), generator=g, device=device) ** 2).sum(-1)
+    off = z / torch.sqrt(chi / 3.0)
+    k = torch.randn((seq_len, hkv, D), generator=g, device=device)
+    kf = k.view(seq_len, hkv, D)
+    for h in range(hkv):
+        kf[:, h, ch[h]] += off[h]
+    k = kf.to(torch.bfloat16)
+    v = torch.randn((seq_len, hkv, D), generator=g, device=device).to(torch.bfloat16)
+    q = torch.randn((1, num_q_heads, D), generator=g, device=device).to(torch.bfloat16)
+    n_pages = -(-seq_len // PAGE)
+    perm = torch.randperm(n_pages, generator=g, device=device).to(torch.int32)
+    mu = k.double().mean(dim=0).float().contiguous()
+    n_full = seq_len // PAGE
+    sink_k = k[:sink_tokens].permute(1, 0, 2).unsqueeze(0).contiguous()
+    sink_v = v[:sink_tokens].permute(1, 0, 2).unsqueeze(0).contiguous()
+    tail_k = torch.zeros((1, hkv, PAGE, D), dtype=torch.bfloat16, device=device)
+    tail_v = torch.zeros_like(tail_k)
+    lo = max(sink_tokens, n_full * PAGE)
+    if seq_len > lo:
+        tail_k[0, :, lo - n_full * PAGE:seq_len - n_full * PAGE] = k[lo:].permute(1, 0, 2)
+        tail_v[0, :, lo - n_full * PAGE:seq_len - n_full * PAGE] = v[lo:].permute(1, 0, 2)
+    return {
+        "k": k, "v": v, "q": q, "key_shift": mu, "block_tables": perm.view(1, -1).contiguous(),
+        "seq_lens": torch.tensor([seq_len], dtype=torch.int32, device=device),
+        "num_pages": n_pages, "n_full": n_full, "page_ids": perm[:n_full].contiguous(),
+        "sink_k": sink_k, "sink_v": sink_v, "tail_k": tail_k, "tail_v": tail_v,
+        "seq_len": seq_len, "num_q_heads": num_q_heads, "num_kv_heads": hkv, "sink_tokens": sink_tokens,
+        "sigma": float(np.float32(1.0 / np.sqrt(128.0))),
+    }
+
+
+def bf16_pages_from_tokens(k, block_tables, num_pages: int):
+    """[L, Hkv, 128] bf16 tokens -> BF16 page pool [num_pages, Hkv, 128, 128]
+    placed through the block table (zero-padded partial last page)."""
+    import torch
+
+    L, hkv, _ = k.shape
+    n = -(-L // PAGE)
+    pad = n * PAGE - L
+    kk = torch.nn.functional.pad(k, (0, 0, 0, 0, 0, pad)) if pad else k
+    pages = kk.view(n, PAGE, hkv, D).permute(0, 2, 1, 3)
+    pool = torch.zeros((num_pages, hkv, PAGE, D), dtype=k.dtype, device=k.device)
+    pool[block_tables[0, :n].long()] = pages
+    return pool
+
+
+def torch_write_rows(seed: int = 0, tokens: int = 131072, num_kv_heads: int = 8, device="cuda"):
+    """The prefill-write workload drawn on the device (torch generator, seed):
+    K, V ~ N(0,1) bf16 [tokens, Hkv, 128]; keys with +-10 offsets (seeded
+    signs) on 8 seeded channels per head; mu = float32(mean of K); page_ids a
+    random permutation of the tokens/128 pages."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(2_000_000 + seed)
+    hkv = num_kv_heads
+    ch = torch.stack([torch.randperm(D, generator=g, device=device)[:8] for _ in range(hkv)])
+    sign = torch.where(torch.rand((hkv, 8), generator=g, device=device) < 0.5, -1.0, 1.0)
+    k = torch.randn((tokens, hkv, D), generator=g, device=device)
+    for h in range(hkv):
+        k[:, h, ch[h]] += 10.0 * sign[h]
+    k = k.to(torch.bfloat16)
+    v = torch.randn((tokens, hkv, D), generator=g, device=device).to(torch.bfloat16)
+    n = tokens // PAGE
+    ids = torch.randperm(n, generator=g, device=device).to(torch.int32)
+    mu = k.double().mean(dim=0).float().contiguous()
+    return {"k": k, "v": v, "page_ids": ids, "key_shift": mu, "num_pages": n, "tokens": tokens, "num_kv_heads": hkv}

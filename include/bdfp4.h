@@ -89,10 +89,13 @@ typedef struct {
  * [num_pages][num_kv_heads][bytes per page-head]; the block of (page p, head h)
  * starts at (p * num_kv_heads + h) * bytes. Sizes from bdfp4_cache_bytes().
  * Byte order inside a block (t = token in page 0..127, d = element 0..127,
- * j = scale block; two codes per byte, the even element in bits 3..0):
- *   K codes (8192 B): (t>>4)*1024 + (d>>5)*256 + (t&15)*16 + ((d&31)>>1)
- *   V codes (8192 B): ((((t>>5)*4 + ((t>>3)&3))*16 + (d>>3))*8 + (t&7))*4
- *                     + ((d&7)>>1)
+ * j = scale block; two codes per byte):
+ *   K codes (8192 B; elements d, d+1 of token t, d even in bits 3..0):
+ *     (t>>4)*1024 + (d>>5)*256 + (t&15)*16 + ((d&31)>>1)
+ *   V codes, NVFP4 (8192 B; tokens t, t+1 of element d, t even in bits 3..0):
+ *     (t>>5)*2048 + (((t>>3)&3)*16 + (d>>3))*32 + (d&7)*4 + ((t&7)>>1)
+ *   V codes, MXFP4 (8192 B; elements d, d+1 of token t, d even in bits 3..0):
+ *     ((((t>>5)*4 + ((t>>3)&3))*16 + (d>>3))*8 + (t&7))*4 + ((d&7)>>1)
  *   K scales, NVFP4 (1024 B, j = d>>4): (((j>>1)*16 + (t&15))*8 + (t>>4))*2 + (j&1)
  *   K scales, MXFP4 (512 B, j = d>>5):  (j*16 + (t&15))*8 + (t>>4)
  *   V scales, NVFP4 (1024 B): (((t>>5)*4 + ((t>>3)&3))*8 + j)*8 + (t&7)

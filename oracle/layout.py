@@ -11,11 +11,15 @@ maps and is the same one the C-ABI header documents. Each cache tensor is a
 dense array [num_pages, num_kv_heads, bytes_per_page_head]; the block of page
 p, head h starts at (p * num_kv_heads + h) * bytes_per_page_head.
 
-Codes: two 4-bit codes per byte, the even element in bits 3..0.
+Codes: two 4-bit codes per byte; which two, and which goes in bits 3..0,
+depends on the array.
 
-K codes (8192 B per page-head), token t, element d:
+K codes (8192 B per page-head), token t, element d (element d even in bits 3..0):
     byte = (t >> 4) * 1024 + (d >> 5) * 256 + (t & 15) * 16 + ((d & 31) >> 1)
-V codes (8192 B), token t, element d:
+V codes, NVFP4 (8192 B): a byte holds tokens t and t+1 (t even, in bits 3..0)
+of one element d:
+    byte = (t >> 5) * 2048 + (((t >> 3) & 3) * 16 + (d >> 3)) * 32 + (d & 7) * 4 + ((t & 7) >> 1)
+V codes, MXFP4 (8192 B), element d even in bits 3..0:
     byte = ((((t >> 5) * 4 + ((t >> 3) & 3)) * 16 + (d >> 3)) * 8 + (t & 7)) * 4 + ((d & 7) >> 1)
 NVFP4 K scales (1024 B), token t, 16-block j (0..7):
     byte = (((j >> 1) * 16 + (t & 15)) * 8 + (t >> 4)) * 2 + (j & 1)
@@ -43,8 +47,24 @@ def k_code_byte(t, d):
     return (t >> 4) * 1024 + (d >> 5) * 256 + (t & 15) * 16 + ((d & 31) >> 1)
 
 
-def v_code_byte(t, d):
-    return ((((t >> 5) * 4 + ((t >> 3) & 3)) * 16 + (d >> 3)) * 8 + (t & 7)) * 4 + ((d & 7) >> 1)
+def v_code_byte(t, d, mx: bool):
+    if mx:
+        return ((((t >> 5) * 4 + ((t >> 3) & 3)) * 16 + (d >> 3)) * 8 + (t & 7)) * 4 + ((d & 7) >> 1)
+    return (t >> 5) * 2048 + (((t >> 3) & 3) * 16 + (d >> 3)) * 32 + (d & 7) * 4 + ((t & 7) >> 1)
+
+
+def _code_map(which: str, mx: bool):
+    """(byte index, bit shift) of every (token, element) of a page-head."""
+    t = np.arange(PAGE)[:, None]
+    d = np.arange(D)[None, :]
+    if which == "k":
+        byte, hi = k_code_byte(t, d), d & 1
+    elif mx:
+        byte, hi = v_code_byte(t, d, True), d & 1
+    else:
+        byte, hi = v_code_byte(t, d, False), t & 1
+    return (np.broadcast_to(byte, (PAGE, D)).reshape(-1),
+            np.broadcast_to(hi * 4, (PAGE, D)).reshape(-1).astype(np.uint8))
 
 
 def k_scale_byte(t, j, mx: bool):
@@ -59,35 +79,25 @@ def v_scale_byte(t, j, mx: bool):
     return (((t >> 5) * 4 + ((t >> 3) & 3)) * 8 + j) * 8 + (t & 7)
 
 
-def pack_codes(nib: np.ndarray, which: str) -> np.ndarray:
+def pack_codes(nib: np.ndarray, which: str, mx: bool = False) -> np.ndarray:
     """nib: uint8 [..., 128 tokens, 128 elements] (4-bit codes) -> bytes [..., 8192]."""
     nib = np.asarray(nib, dtype=np.uint8)
     lead = nib.shape[:-2]
     out = np.zeros(lead + (CODE_BYTES,), dtype=np.uint8)
-    t = np.arange(PAGE)[:, None]
-    d = np.arange(D)[None, :]
-    fn = k_code_byte if which == "k" else v_code_byte
-    byte = np.broadcast_to(fn(t, d), (PAGE, D))
-    shift = np.broadcast_to((d & 1) * 4, (PAGE, D)).astype(np.uint8)
-    flat_b = byte.reshape(-1)
-    flat_s = shift.reshape(-1)
+    flat_b, flat_s = _code_map(which, mx)
     vals = (nib.reshape(lead + (PAGE * D,)) & 0xF) << flat_s
-    # every byte receives exactly two nibbles (even and odd element)
-    for parity in (0, 1):
-        sel = flat_s == 4 * parity
+    # every byte receives exactly two nibbles, one at shift 0 and one at shift 4
+    for sh in (0, 4):
+        sel = flat_s == sh
         out[..., flat_b[sel]] |= vals[..., sel].astype(np.uint8)
     return out
 
 
-def unpack_codes(buf: np.ndarray, which: str) -> np.ndarray:
+def unpack_codes(buf: np.ndarray, which: str, mx: bool = False) -> np.ndarray:
     """bytes [..., 8192] -> nibbles [..., 128 tokens, 128 elements]."""
     buf = np.asarray(buf, dtype=np.uint8)
-    t = np.arange(PAGE)[:, None]
-    d = np.arange(D)[None, :]
-    fn = k_code_byte if which == "k" else v_code_byte
-    byte = np.broadcast_to(fn(t, d), (PAGE, D))
-    shift = np.broadcast_to((d & 1) * 4, (PAGE, D)).astype(np.uint8)
-    return ((buf[..., byte] >> shift) & 0xF).astype(np.uint8)
+    flat_b, flat_s = _code_map(which, mx)
+    return ((buf[..., flat_b] >> flat_s) & 0xF).astype(np.uint8).reshape(buf.shape[:-1] + (PAGE, D))
 
 
 def pack_scales(sc: np.ndarray, which: str, mx: bool) -> np.ndarray:

@@ -85,7 +85,7 @@ def write_pages(recipe: Recipe, cache: dict, k_bf16: np.ndarray, v_bf16: np.ndar
     vs = vs.transpose(0, 2, 1, 3)
     cache["k_codes"][page_ids] = layout.pack_codes(kn, "k")
     cache["k_scales"][page_ids] = layout.pack_scales(ks, "k", kmx)
-    cache["v_codes"][page_ids] = layout.pack_codes(vn, "v")
+    cache["v_codes"][page_ids] = layout.pack_codes(vn, "v", vmx)
     cache["v_scales"][page_ids] = layout.pack_scales(vs, "v", vmx)
     return cache
 
@@ -97,7 +97,7 @@ def read_page_head(recipe: Recipe, cache: dict, page: int, head: int):
     vmx = recipe.scale_mode_v == Q.MXFP4_SEARCH
     kn = layout.unpack_codes(cache["k_codes"][page, head], "k")
     ks = layout.unpack_scales(cache["k_scales"][page, head], "k", kmx)
-    vn = layout.unpack_codes(cache["v_codes"][page, head], "v")
+    vn = layout.unpack_codes(cache["v_codes"][page, head], "v", vmx)
     vs = layout.unpack_scales(cache["v_scales"][page, head], "v", vmx)
     return (Q.dequantize(kn, ks, recipe.scale_mode_k),
             Q.dequantize(vn, vs, recipe.scale_mode_v))

@@ -39,15 +39,14 @@ def _golden(name):
 
 # ----------------------------------------------------------------- layout
 
-@pytest.mark.parametrize("which", ["k", "v"])
-def test_code_layout_is_a_bijection(which):
-    fn = LY.k_code_byte if which == "k" else LY.v_code_byte
-    t, d = np.meshgrid(np.arange(128), np.arange(128), indexing="ij")
-    slot = fn(t, d) * 2 + (d & 1)
-    assert np.array_equal(np.sort(slot.ravel()), np.arange(128 * 128))
+@pytest.mark.parametrize("which,mx", [("k", False), ("v", False), ("v", True)])
+def test_code_layout_is_a_bijection(which, mx):
+    b, sh = LY._code_map(which, mx)
+    slot = b.astype(np.int64) * 2 + sh // 4
+    assert np.array_equal(np.sort(slot), np.arange(128 * 128))
     rng = np.random.default_rng(0)
     nib = rng.integers(0, 16, size=(3, 128, 128)).astype(np.uint8)
-    assert np.array_equal(LY.unpack_codes(LY.pack_codes(nib, which), which), nib)
+    assert np.array_equal(LY.unpack_codes(LY.pack_codes(nib, which, mx), which, mx), nib)
 
 
 @pytest.mark.parametrize("which", ["k", "v"])
