@@ -27,22 +27,49 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // ---------------------------------------------------------------- E4M3
 
 // Code of the E4M3 value nearest to v >= 0 (ties to even), saturating at 448.
-// Branch-free: both the normal and the subnormal encodings are formed and one
-// is selected.
+// The gfx950 down-convert rounds to nearest even but turns values from 464
+// up into NaN, so the input is clamped to 448 first (448 itself and every
+// value in [448, 464) encode as 0x7E either way; a NaN clamps to 448).
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t r_norm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);  // RNE to 3 mantissa bits
-  const uint32_t r_sub = (uint32_t)__builtin_rintf(v * 512.0f);   // v < 2^-6: m * 2^-9, exact scaling; 8 -> 0x08
-  const uint32_t r = u < 0x3C800000u ? r_sub : r_norm;
-  return v < 448.0f ? r : 0x7Eu;
+  const float c = __builtin_fminf(v, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
-// Value of a non-negative finite E4M3 code (exact in float32).
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  const float sub = (float)m * 0.001953125f;                      // m * 2^-9
-  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return e == 0u ? sub : nrm;
+// Value of an E4M3 code (the hardware up-convert is exact for every code).
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
+
+// ---------------------------------------------------------------- exact quotients
+
+// RN(x / m) for a divisor m with r = RN(1/m): q0 = RN(x r), then one FMA
+// correction. Bit-identical to the IEEE quotient (signed zeros included) for
+// the eight E4M3 significands m = 1 + k/8 and for m = 6 whenever
+// |x| >= 2^-122 (exhaustive check over every float32 significand); for
+// smaller |x| every caller's code is zero regardless.
+__device__ __forceinline__ float quot(float x, float m, float r) {
+  const float q0 = __fmul_rn(x, r);
+  const float e = __builtin_fmaf(m, q0, -x);
+  return __builtin_fmaf(e, -r, q0);
+}
+
+// RN(a / 6).
+__device__ __forceinline__ float div6(float a) { return quot(a, 6.0f, __uint_as_float(0x3E2AAAABu)); }
+
+// Significand m in [1, 2) of a positive normal float32 s = 2^E m, and the
+// index k of m = 1 + k/8 when s is an E4M3 value.
+__device__ __forceinline__ float significand(float s) {
+  return __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+}
+__device__ __forceinline__ uint32_t sig_index(float s) { return (__float_as_uint(s) >> 20) & 7u; }
+
+// RN(1 / (1 + k/8)), k = 0..7.
+__device__ __forceinline__ float rcp_significand(uint32_t k) {
+  const uint32_t a0 = (k & 1u) ? 0x3F638E39u : 0x3F800000u;
+  const uint32_t a1 = (k & 1u) ? 0x3F3A2E8Cu : 0x3F4CCCCDu;
+  const uint32_t a2 = (k & 1u) ? 0x3F1D89D9u : 0x3F2AAAABu;
+  const uint32_t a3 = (k & 1u) ? 0x3F088889u : 0x3F124925u;
+  const uint32_t b0 = (k & 2u) ? a1 : a0;
+  const uint32_t b1 = (k & 2u) ? a3 : a2;
+  return __uint_as_float((k & 4u) ? b1 : b0);
 }
 
 // ---------------------------------------------------------------- E8M0
@@ -109,44 +136,71 @@ __device__ __forceinline__ uint32_t e2m1_nibble(float x, const E2m1Thr& T) {
   return T.zero ? 0u : (sgn | mag);
 }
 
+// E2M1 codes of x0 (bits 3..0) and x1 (bits 7..4) against a positive normal
+// scale s = 2^E m whose significand m has reciprocal r = RN(1/m): the exact
+// quotients x / m, then the gfx950 down-convert, which divides by 2^E (the
+// exponent of its scale operand), rounds to nearest even with saturation at
+// 6 and keeps the sign. A float32 quotient never lands on an E2M1 midpoint
+// unless it is exactly that midpoint, so each code is the one of the exact
+// ratio x / s.
+__device__ __forceinline__ uint32_t e2m1_pair(float x0, float x1, float s, float m, float r) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quot(x0, m, r), quot(x1, m, r), s, 0) & 0xFFu;
+}
+
 // ---------------------------------------------------------------- blocks
 
-// Quantize N in-register values with scale value s (float32): codes packed
-// 8 per uint32 (element 2i in the low nibble of byte i) and, when requested,
-// the float32 squared error summed as a balanced pairwise tree
-// ((e0+e1)+(e2+e3))+... . The tree is built incrementally: lvl[k] holds the
-// pending left sum of 2^k elements; element i is merged with the levels of
-// its trailing one bits (left operand the older sum), so the additions and
-// their order are exactly those of the level-by-level tree.
+// Quantize N in-register values (N even) with scale value s (float32):
+// codes packed 8 per uint32 (element 2i in the low nibble of byte i) and,
+// when requested, the float32 squared error summed as a balanced pairwise
+// tree ((e0+e1)+(e2+e3))+... . Normal scales take the exact-quotient route
+// of e2m1_pair; the float32 subnormal 2^-127 (the lowest E8M0 scale) takes
+// the threshold search; a zero scale gives all-zero codes. The error tree is
+// built incrementally: lvl[k] holds the pending left sum of 2^k elements;
+// element i is merged with the levels of its trailing one bits (left operand
+// the older sum), so the additions and their order are exactly those of the
+// level-by-level tree.
 template <int N, bool kSse>
 __device__ __forceinline__ float quant_block(const float* x, float s, uint32_t* packed) {
-  const E2m1Thr T = e2m1_thresholds(s);
-  constexpr int kLv = N == 32 ? 6 : (N == 16 ? 5 : (N == 8 ? 4 : 3));
-  float lvl[kLv];
+  static_assert(N % 2 == 0, "pairs of elements");
+  constexpr int kLv = N == 32 ? 6 : (N == 16 ? 5 : (N == 8 ? 4 : (N == 4 ? 3 : 2)));
+  constexpr int kW = (N + 7) / 8;
 #pragma unroll
-  for (int w = 0; w < N / 8; ++w) packed[w] = 0u;
+  for (int w = 0; w < kW; ++w) packed[w] = 0u;
+  if (s >= 1.17549435e-38f) {
+    const float m = significand(s);
+    const float r = rcp_significand(sig_index(s));
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float ax = __builtin_fabsf(x[i]);
-    const uint32_t mag = T.zero ? 0u : e2m1_mag(ax, T);
-    const uint32_t sgn = (__float_as_uint(x[i]) >> 31) << 3;
-    const uint32_t nib = T.zero ? 0u : (sgn | mag);
-    packed[i >> 3] |= nib << (4 * (i & 7));
-    if (kSse) {
-      const float q = __fmul_rn(e2m1_grid(mag), s);   // exact
-      const float d = __fsub_rn(ax, q);
-      float v = __fmul_rn(d, d);
-      int k = 0;
+    for (int i = 0; i < N; i += 2) packed[i >> 3] |= e2m1_pair(x[i], x[i + 1], s, m, r) << (4 * (i & 7));
+  } else if (s > 0.0f) {
+    const E2m1Thr T = e2m1_thresholds(s);
 #pragma unroll
-      for (int bit = 1; bit < N; bit <<= 1, ++k) {
-        if ((i & bit) == 0) break;
-        v = __fadd_rn(lvl[k], v);
-      }
-      lvl[k] = v;
-    }
+    for (int i = 0; i < N; ++i) packed[i >> 3] |= e2m1_nibble(x[i], T) << (4 * (i & 7));
   }
   if (!kSse) return 0.0f;
+  float lvl[kLv];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t mag = (packed[i >> 3] >> (4 * (i & 7))) & 7u;
+    const float q = __fmul_rn(e2m1_grid(mag), s);   // exact
+    const float d = __fsub_rn(__builtin_fabsf(x[i]), q);
+    float v = __fmul_rn(d, d);
+    int k = 0;
+#pragma unroll
+    for (int bit = 1; bit < N; bit <<= 1, ++k) {
+      if ((i & bit) == 0) break;
+      v = __fadd_rn(lvl[k], v);
+    }
+    lvl[k] = v;
+  }
   return lvl[kLv - 1];
+}
+
+// Scale code of an aligned 16-value block of p' = c p with block maximum
+// a >= 0: E4M3(a / 2) when kUnder and a < tau (amax2_or_amax6), otherwise
+// E4M3(a / 6) (amax6).
+template <bool kUnder>
+__device__ __forceinline__ uint32_t p_scale_code(float a, float tau) {
+  return e4m3_encode((kUnder && a < tau) ? __fmul_rn(a, 0.5f) : div6(a));
 }
 
 __device__ __forceinline__ float absmax16(const float* x) {
@@ -160,7 +214,7 @@ __device__ __forceinline__ float absmax16(const float* x) {
 template <bool kFourSix>
 __device__ __forceinline__ uint32_t nv_block(const float* x, uint32_t* packed) {
   const float a = absmax16(x);
-  const uint32_t c6 = e4m3_encode(a / 6.0f);
+  const uint32_t c6 = e4m3_encode(div6(a));
   if (!kFourSix) {
     quant_block<16, false>(x, e4m3_value(c6), packed);
     return c6;

@@ -10,35 +10,47 @@
 // dispatches to the paged attention kernel, which uses block scaling and scale
 // modes; the tail control plane keeps the partial page in BF16.
 //
-// Grid: one workgroup (256 threads, 4 waves) per (sequence, KV head,
-// partition). Partition 0 is the BF16 partition (sink + tail tokens, exact
-// float32 attention of the raw query). Partitions 1..S each own
-// pages_per_partition FP4 pages. A partition computes, for the 4 query heads
-// of its KV head, m = max logit, l = sum exp(t - m) and o = sum P_hat v_hat,
-// writes them to the workspace and takes a ticket; the last workgroup of the
-// (sequence, KV head) merges all partials and resets the ticket.
+// Grid: one workgroup (256 threads, 4 waves) per (sequence, KV head, FP4
+// partition); each FP4 partition owns pages_per_partition pages. The BF16
+// partition (sink + tail tokens, exact float32 attention of the raw query)
+// is computed by the first workgroup of each (sequence, KV head) after its
+// FP4 pages, so the grid has no extra short workgroups that would spill
+// the 2-per-CU residency into a second round. A partition computes, for the
+// 4 query heads of its KV head, m = max logit, l = sum exp(t - m) and
+// o = sum P_hat v_hat, writes them to the workspace and takes a ticket; the
+// last workgroup of the (sequence, KV head) merges all partials and resets
+// the ticket.
 //
 // FP4 partition, per workgroup:
 //  * the page ids are staged in LDS and each wave starts loading its first K
 //    page before the query prologue;
 //  * prologue: wave g rotates (128-point Hadamard, float32) and quantizes
-//    query row g as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32), 16 lanes
-//    of 8 elements; the dequantized terms are exact in 16 bits and become the
-//    A operands of v_mfma_f32_16x16x32_{f16,bf16} (rows 0..3 = heads, 12 zero
-//    rows). q . mu (raw float32 query, key means) seeds the accumulator.
+//    query row g as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32), two
+//    elements per lane; the dequantized terms are exact in 16 bits and become
+//    the A operands of v_mfma_f32_16x16x32_{f16,bf16}: row 2g + t holds term
+//    t of head g, rows 8..15 are zero. q . mu (raw float32 query, key means)
+//    seeds the term-1 rows of the accumulator.
 //  * pass 1 (QK^T): each wave streams whole pages, the next page in flight
 //    while the current one is used; per 16-token tile a lane holds 16 code
 //    bytes (one coalesced 1 KiB run per wave) and the page's scales come in
-//    one 16-byte load per lane. Logits sigma (q . mu + q_hat . k_hat) go to
-//    LDS [head][token]; sink slots of the first page get -inf.
+//    one 16-byte load per lane. Four MFMAs give both terms of all four heads;
+//    their sum, the raw logit q . mu + q_hat . k_hat, goes to LDS
+//    [head][token]. Sink tokens fill whole tiles of the first page and get
+//    -inf.
 //  * partition max over the 4 waves.
 //  * pass 2 (softmax, P quantization, PV): per 32-token chunk the 4 x 32
-//    probabilities p = exp(t - m) are formed two per lane; l accumulates the
-//    unquantized p; p' = c p is quantized per aligned 16-token block
-//    (amax2_or_amax6 with tau, or amax6) and s * e2m1 (exact in 16 bits) is
-//    staged in LDS as the A operand. V codes come as B operands of 8 MFMAs
-//    (one per output channel slab).
-//  * the 4 waves' o and l are summed in LDS; o is divided by c.
+//    values p' = c exp(sigma (t - m)) are formed two per lane; l accumulates
+//    them; p' is quantized per aligned 16-token block (amax2_or_amax6 with
+//    tau, or amax6) and s * e2m1 (exact in 16 bits) is staged in LDS as the A
+//    operand. V codes come as B operands of 8 MFMAs (one per output channel
+//    slab).
+//  * the 4 waves' o and l are summed in LDS; both are divided by c.
+//
+// E2M1 codes of p' are found without comparing against the grid midpoints:
+// with the block scale s = 2^E m (E4M3), the exact float32 quotient p' / m
+// (one multiply and two FMA corrections) goes through the hardware
+// down-convert, which divides by 2^E and rounds to nearest even; the result
+// is the code of the exact ratio p' / s (see quot and e2m1_pair).
 //
 // Operand construction. The scaled FP4 converts of gfx950 apply only the
 // exponent of their float32 scale. MXFP4 scales are powers of two and convert
@@ -131,13 +143,14 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
 // ------------------------------------------------------------ shared memory
 
 struct Smem {
-  float logit[4 * kMaxTok];                 // [head][token]; reused for the o reduction
-  uint16_t qhat[2][4][kD];                  // 16-bit dequantized query terms
+  float logit[4 * kMaxTok];                 // [head][token] raw logits; reused for the o reduction
+  uint16_t qhat[2][4][kD];                  // 16-bit dequantized query terms [term][head][channel]
   float q[4][kD];                           // raw float32 query (BF16 partition)
+  uint32_t pst[4][16][16];                  // per wave: P_hat staging [row][token pair]; rows 4..15 stay 0
   float qmu[4];
-  uint16_t p[4][4][32];                     // per wave: P_hat staging [head][token]
   float red[4][4];                          // per wave, per head
   float lsum[4][4];
+  float rcp[8];                             // RN(1 / (1 + k/8)), k = 0..7
   int page[kMaxPpp];                        // physical pages of the partition (-1: invalid)
   int ticket;
 };
@@ -261,121 +274,97 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
 
 // ------------------------------------------------------------ query prologue
 
-// DPP row controls (16-lane rows): shift left / right by 4, rotate by 8.
-constexpr int kDppRowShl4 = 0x104;
-constexpr int kDppRowShr4 = 0x114;
-constexpr int kDppRowRor8 = 0x128;
-
-// Butterfly stages with partner lane ^ 4 and lane ^ 8 inside a 16-lane row.
-__device__ __forceinline__ void fwht_xlane_4_8(float* x, int i) {
-  const bool up4 = (i & 4) != 0, up8 = (i & 8) != 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float p = shfl_xor(x[k], 4);
-    x[k] = up4 ? __fsub_rn(p, x[k]) : __fadd_rn(x[k], p);
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float p = shfl_xor(x[k], 8);
-    x[k] = up8 ? __fsub_rn(p, x[k]) : __fadd_rn(x[k], p);
-  }
+// Butterfly stage across lanes for the two elements a lane holds: the lane
+// whose selector bit is clear keeps own + partner, the other partner - own.
+__device__ __forceinline__ void xstage(float& x0, float& x1, float p0, float p1, bool upper) {
+  x0 = upper ? __fsub_rn(p0, x0) : __fadd_rn(x0, p0);
+  x1 = upper ? __fsub_rn(p1, x1) : __fadd_rn(x1, p1);
 }
 
-// The raw query elements and key means of lane i of row g (loaded first, so
-// their latency overlaps the page-id staging and the first page loads).
-struct QueryIn {
-  uint4 q;
-  float4 mu0, mu1;
-};
-
-__device__ __forceinline__ QueryIn query_load(const DecodeLaunch& P, int b, int h, int g, int i) {
-  QueryIn in;
-  in.q = *reinterpret_cast<const uint4*>(P.q + ((size_t)b * P.hq + h * kGroup + g) * kD + 8 * i);
-  if (P.key_smoothing) {
-    const float4* mu4 = reinterpret_cast<const float4*>(P.key_shift + h * kD + 8 * i);
-    in.mu0 = mu4[0];
-    in.mu1 = mu4[1];
-  } else {
-    in.mu0 = in.mu1 = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  return in;
+template <int kPattern>
+__device__ __forceinline__ float swizzle_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kPattern));
 }
 
-// Query row g of the group on 16 lanes (lane i holds elements [8i, 8i+8)):
-// q . mu, the Hadamard rotation (stages 1, 2, 4 in-lane, 8 .. 64 across
-// lanes by DPP), then Q1 and the residual Q2, dequantized into LDS. The same
-// float32 operations in the same order as the page writer's key path and the
-// row quantizer, so the codes are identical.
+// ds_swizzle bit-mode patterns: lane ^ 4, ^ 8, ^ 16 inside 32-lane halves.
+constexpr int kSwzXor4 = 0x101F;
+constexpr int kSwzXor8 = 0x201F;
+constexpr int kSwzXor16 = 0x401F;
+
+// Query row g of the group on a whole wave: lane i holds elements 2i, 2i+1.
+// q . mu (raw float32 query, key means), the Hadamard rotation (stage 1
+// in-lane, stages 2 .. 64 across lanes), then Q1 and the residual Q2,
+// dequantized into LDS as 16-bit MFMA operands. The quantizer is the one of
+// the page writer and the row quantizer (quant_block), so the codes are the
+// same functions of the rotated values.
 template <bool kMx, int kTerms>
-__device__ __forceinline__ void query_row(const DecodeLaunch& P, const QueryIn& in, Smem& sm, int g, int i) {
-  float x[8];
-  const uint32_t ww[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = bf16_lo(ww[k]);
-    x[2 * k + 1] = bf16_hi(ww[k]);
-  }
-  const float mu[8] = {in.mu0.x, in.mu0.y, in.mu0.z, in.mu0.w, in.mu1.x, in.mu1.y, in.mu1.z, in.mu1.w};
-  float dot = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) dot = fmaf(x[k], mu[k], dot);
+__device__ __forceinline__ void query_prologue(const DecodeLaunch& P, uint32_t qw, float2 mu, Smem& sm, int g,
+                                               int i) {
+  float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
+  float dot = __builtin_fmaf(x1, mu.y, __fmul_rn(x0, mu.x));
   dot = sum16(dot);
+  dot += shfl_xor(dot, 16);
+  dot += shfl_xor(dot, 32);
   if (i == 0) sm.qmu[g] = dot;
   if (P.rotation) {
-    fwht_inlane<8>(x);
-    fwht_xlane<8, kDppQuadXor1>(x, (i & 1) != 0);
-    fwht_xlane<8, kDppQuadXor2>(x, (i & 2) != 0);
-    fwht_xlane_4_8(x, i);
-    const float c = inv_sqrt_d();
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], c);
+    const float a = x0, c = x1;
+    x0 = __fadd_rn(a, c);
+    x1 = __fsub_rn(a, c);
+    xstage(x0, x1, dpp_f32<kDppQuadXor1>(x0), dpp_f32<kDppQuadXor1>(x1), (i & 1) != 0);
+    xstage(x0, x1, dpp_f32<kDppQuadXor2>(x0), dpp_f32<kDppQuadXor2>(x1), (i & 2) != 0);
+    xstage(x0, x1, swizzle_f32<kSwzXor4>(x0), swizzle_f32<kSwzXor4>(x1), (i & 4) != 0);
+    xstage(x0, x1, swizzle_f32<kSwzXor8>(x0), swizzle_f32<kSwzXor8>(x1), (i & 8) != 0);
+    xstage(x0, x1, swizzle_f32<kSwzXor16>(x0), swizzle_f32<kSwzXor16>(x1), (i & 16) != 0);
+    xstage(x0, x1, shfl_xor(x0, 32), shfl_xor(x1, 32), (i & 32) != 0);
+    const float cs = inv_sqrt_d();
+    x0 = __fmul_rn(x0, cs);
+    x1 = __fmul_rn(x1, cs);
   }
 #pragma unroll
   for (int term = 0; term < kTerms; ++term) {
-    float a = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a = __builtin_fmaxf(a, __builtin_fabsf(x[k]));
+    const float xx[2] = {x0, x1};
+    float a = __builtin_fmaxf(__builtin_fabsf(x0), __builtin_fabsf(x1));
     float s;
     uint32_t pk;
     if (kMx) {
-      // 32-element block = this quad of lanes; candidates E_hi, E_hi - 1
-      a = __builtin_fmaxf(a, dpp_f32<kDppQuadXor1>(a));
-      a = __builtin_fmaxf(a, dpp_f32<kDppQuadXor2>(a));
+      // 32-element block = 16 lanes; candidates E_hi, E_hi - 1 by squared error
+      a = max16(a);
       int ehi = a > 0.0f ? mx_exponent_hi(a) : -127;
       ehi = ehi < -127 ? -127 : (ehi > 127 ? 127 : ehi);
       const int elo = ehi - 1 < -127 ? -127 : ehi - 1;
       uint32_t phi, plo;
-      float ehi_err = quant_block<8, true>(x, pow2_f32(ehi), &phi);
-      float elo_err = quant_block<8, true>(x, pow2_f32(elo), &plo);
-      // the 32-element tree: ((t0 + t1) + (t2 + t3)) over the quad's subtrees
+      float ehi_err = quant_block<2, true>(xx, pow2_f32(ehi), &phi);
+      float elo_err = quant_block<2, true>(xx, pow2_f32(elo), &plo);
+      // levels 2 .. 5 of the 32-element tree: partners lane ^ 1, ^ 2, then
+      // the mirrors inside 8 and 16 lanes (the values are uniform per quad /
+      // per 8 lanes by then)
       ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppQuadXor1>(ehi_err));
-      ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppQuadXor2>(ehi_err));
       elo_err = __fadd_rn(elo_err, dpp_f32<kDppQuadXor1>(elo_err));
+      ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppQuadXor2>(ehi_err));
       elo_err = __fadd_rn(elo_err, dpp_f32<kDppQuadXor2>(elo_err));
+      ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppRowHalfMirror>(ehi_err));
+      elo_err = __fadd_rn(elo_err, dpp_f32<kDppRowHalfMirror>(elo_err));
+      ehi_err = __fadd_rn(ehi_err, dpp_f32<kDppRowMirror>(ehi_err));
+      elo_err = __fadd_rn(elo_err, dpp_f32<kDppRowMirror>(elo_err));
       const bool take_lo = (elo_err < ehi_err) && (elo < ehi) && a > 0.0f;
       s = a > 0.0f ? pow2_f32(take_lo ? elo : ehi) : 0.0f;
       pk = a > 0.0f ? (take_lo ? plo : phi) : 0u;
     } else {
-      // 16-element block = this pair of lanes
-      a = __builtin_fmaxf(a, dpp_f32<kDppQuadXor1>(a));
-      s = e4m3_value(e4m3_encode(a / 6.0f));
-      quant_block<8, false>(x, s, &pk);
+      // 16-element block = 8 lanes
+      a = max8(a);
+      s = e4m3_value(e4m3_encode(div6(a)));
+      quant_block<2, false>(xx, s, &pk);
     }
-    float deq[8];
+    float deq[2];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 2; ++k) {
       const uint32_t nib = (pk >> (4 * k)) & 0xFu;
       const float gv = __fmul_rn(e2m1_grid(nib & 7u), s);
       deq[k] = (nib & 8u) ? -gv : gv;
     }
-    uint4 o;
-    o.x = op16<kMx>(deq[0]) | (op16<kMx>(deq[1]) << 16);
-    o.y = op16<kMx>(deq[2]) | (op16<kMx>(deq[3]) << 16);
-    o.z = op16<kMx>(deq[4]) | (op16<kMx>(deq[5]) << 16);
-    o.w = op16<kMx>(deq[6]) | (op16<kMx>(deq[7]) << 16);
-    *reinterpret_cast<uint4*>(&sm.qhat[term][g][8 * i]) = o;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = __fsub_rn(x[k], deq[k]);
+    reinterpret_cast<uint32_t*>(&sm.qhat[term][g][0])[i] = op16<kMx>(deq[0]) | (op16<kMx>(deq[1]) << 16);
+    x0 = __fsub_rn(x0, deq[0]);
+    x1 = __fsub_rn(x1, deq[1]);
   }
 }
 
@@ -428,6 +417,12 @@ __device__ __forceinline__ void load_v(VPage& v, const DecodeLaunch& P, size_t b
 
 // ------------------------------------------------------------ FP4 partition
 
+__device__ __forceinline__ uint32_t umax_dpp8(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, false));
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowHalfMirror, 0xF, 0xF, false));
+}
+
 template <bool kMx, int kTerms, bool kUnder>
 __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, int L, int n_full) {
   const DecodeLaunch& P = A.L;
@@ -435,14 +430,22 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   const int p0 = (s - 1) * P.ppp;
   const int p1 = min(n_full, s * P.ppp);
   const int npg = p1 - p0;
-  const int lo = max(P.sink, kPage * p0);
   const size_t hkv = P.hkv;
-  QueryIn qin;
-  if (lane < 16) qin = query_load(P, b, h, wave, lane);
 
+  // the query row of this wave and the key means, first so their latency
+  // overlaps the page-id staging and the first page loads
+  const uint32_t qw =
+      reinterpret_cast<const uint32_t*>(P.q + ((size_t)b * P.hq + h * kGroup + wave) * kD)[lane];
+  const float2 mu = P.key_smoothing ? reinterpret_cast<const float2*>(P.key_shift + h * kD)[lane]
+                                    : make_float2(0.0f, 0.0f);
   if (tid < npg) {
     const int ph = P.block_tables[(size_t)b * P.max_pages_per_seq + p0 + tid];
     sm.page[tid] = (ph < 0 || ph >= P.num_pages) ? -1 : ph;
+  }
+  if (tid < 8) sm.rcp[tid] = rcp_significand((uint32_t)tid);
+  {
+    uint32_t* pz = &sm.pst[0][0][0];       // rows 4 .. 15 of every wave's staging tile
+    for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
   __syncthreads();
   auto blk_of = [&](int pi) -> size_t {
@@ -450,54 +453,71 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
     return (size_t)(ph < 0 ? 0 : ph) * hkv + h;
   };
 
-  KPage kcur, knxt;
+  KPage kcur;
   if (wave < npg) load_k<kMx>(kcur, P, blk_of(wave), lane);
-  if (lane < 16) query_row<kMx, kTerms>(P, qin, sm, wave, lane);
+  query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
 
-  // A operands: lane (row = lane & 15, k-group kg = lane >> 4); MFMA c covers
-  // channels 32 kg + 8 c + [0, 8)
+  // A operands: lane (row = lane & 15, k-group kg = lane >> 4); row 2 g + t
+  // holds query term t of head g (rows 8 .. 15 zero); MFMA c covers channels
+  // 32 kg + 8 c + [0, 8)
   const int row = lane & 15, kg = lane >> 4;
-  u32x4_t aq[2][4];
+  u32x4_t aq[4];
 #pragma unroll
-  for (int term = 0; term < 2; ++term) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row < 4 && term < kTerms) {
-        const uint4 t = *reinterpret_cast<const uint4*>(&sm.qhat[term][row][32 * kg + 8 * c]);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-      }
-      aq[term][c] = v;
+  for (int c = 0; c < 4; ++c) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < 2 * kGroup && ((row & 1) < kTerms)) {
+      const uint4 t = *reinterpret_cast<const uint4*>(&sm.qhat[row & 1][row >> 1][32 * kg + 8 * c]);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     }
+    aq[c] = v;
   }
-  const f32x4_t acc0 = {sm.qmu[0], sm.qmu[1], sm.qmu[2], sm.qmu[3]};
-  const float sigma = P.softmax_scale;
-  float* logit = sm.logit;
+  // D lane l holds rows 4 (l >> 4) + i: lanes 0..15 heads 0, 1 and lanes
+  // 16..31 heads 2, 3 (term 1 in i = 0, 2; term 2 in i = 1, 3); q . mu
+  // enters through the term-1 rows
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+  if (kg < 2) {
+    acc0[0] = sm.qmu[2 * kg];
+    acc0[2] = sm.qmu[2 * kg + 1];
+  }
+  float* lg_a = sm.logit + (2 * (kg & 1)) * kMaxTok + row;   // head 2 kg (lanes < 32)
+  float* lg_b = lg_a + kMaxTok;                                // head 2 kg + 1
 
-  // ---- pass 1: logits
-  float mrun[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-  for (int pi = wave; pi < npg; pi += 4) {
-    if (pi + 4 < npg) load_k<kMx>(knxt, P, blk_of(pi + 4), lane);
-    const bool has_sink = kPage * (p0 + pi) < lo;          // uniform per page
+  // ---- pass 1: raw logits q . mu + q_hat . k_hat
+  // Sink tokens (global tokens below the sink size, a multiple of 16) fill
+  // whole 16-token tiles of the sequence's first page; those tiles get -inf.
+  const int sink_tiles = p0 == 0 ? P.sink / 16 : 0;
+  float ma = kNegInf, mb = kNegInf;
+  auto k_page = [&](const KPage& cur, KPage& nxt, int pi) {
+    if (pi + 4 < npg) load_k<kMx>(nxt, P, blk_of(pi + 4), lane);
+    const int skip = pi == 0 ? sink_tiles : 0;             // uniform
+    float pa = kNegInf, pb = kNegInf;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
+      const int local = pi * kPage + t * 16;               // token - 128 p0 of the tile's first token
+      if (t < skip) {
+        if (lane < 32) {
+          lg_a[local] = kNegInf;
+          lg_b[local] = kNegInf;
+        }
+        continue;
+      }
       u32x4_t bk[4];
       if (kMx) {
-        const uint32_t sb = (word_of(kcur.sc, t >> 2) >> (8 * (t & 3))) & 0xFFu;
+        const uint32_t sb = (word_of(cur.sc, t >> 2) >> (8 * (t & 3))) & 0xFFu;
         const float sv = pow2_f32((int)sb - 127);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t cw = word_of(kcur.code[t], c);
+          const uint32_t cw = word_of(cur.code[t], c);
           bk[c] = (u32x4_t){cvt_bf16_pair(cw, sv, 0), cvt_bf16_pair(cw, sv, 1), cvt_bf16_pair(cw, sv, 2),
                             cvt_bf16_pair(cw, sv, 3)};
         }
       } else {
-        const f16x2_t sp = e4m3_pair_f16(word_of(kcur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
+        const f16x2_t sp = e4m3_pair_f16(word_of(cur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
         const f16x2_t slo = {sp[0], sp[0]}, shi = {sp[1], sp[1]};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t cw = word_of(kcur.code[t], c);
+          const uint32_t cw = word_of(cur.code[t], c);
           const f16x2_t sc = c < 2 ? slo : shi;
           bk[c] = (u32x4_t){u32_of(grid_f16_pair(cw, 0) * sc), u32_of(grid_f16_pair(cw, 1) * sc),
                             u32_of(grid_f16_pair(cw, 2) * sc), u32_of(grid_f16_pair(cw, 3) * sc)};
@@ -505,35 +525,34 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
       }
       f32x4_t acc = acc0;
 #pragma unroll
-      for (int term = 0; term < kTerms; ++term) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc = mfma<kMx>(aq[term][c], bk[c], acc);
+      for (int c = 0; c < 4; ++c) acc = mfma<kMx>(aq[c], bk[c], acc);
+      const float ta = __fadd_rn(acc[0], acc[1]);
+      const float tb = __fadd_rn(acc[2], acc[3]);
+      if (lane < 32) {
+        lg_a[local] = ta;
+        lg_b[local] = tb;
       }
-      if (lane < 16) {
-        const int local = pi * kPage + t * 16 + lane;        // token - 128 p0
-        float lg[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) lg[g] = sigma * acc[g];
-        if (has_sink && kPage * p0 + local < lo) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) lg[g] = kNegInf;
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          logit[g * kMaxTok + local] = lg[g];
-          mrun[g] = fmaxf(mrun[g], lg[g]);
-        }
-      }
+      pa = __builtin_fmaxf(pa, ta);
+      pb = __builtin_fmaxf(pb, tb);
     }
-    kcur = knxt;
+    ma = __builtin_fmaxf(ma, pa);
+    mb = __builtin_fmaxf(mb, pb);
+  };
+  {
+    KPage kb;
+    for (int pi = wave; pi < npg; pi += 8) {
+      k_page(kcur, kb, pi);
+      if (pi + 4 >= npg) break;
+      k_page(kb, kcur, pi + 4);
+    }
   }
-  VPage vcur, vnxt;
+  VPage vcur;
   if (wave < npg) load_v<kMx>(vcur, P, blk_of(wave), lane);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) mrun[g] = max16(mrun[g]);
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) sm.red[wave][g] = mrun[g];
+  ma = max16(ma);
+  mb = max16(mb);
+  if (lane == 0 || lane == 16) {
+    sm.red[wave][2 * kg] = ma;
+    sm.red[wave][2 * kg + 1] = mb;
   }
   __syncthreads();
   float m[4];
@@ -545,39 +564,43 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   const int ph = lane >> 4;          // head of this lane in the P step
   const int pj = lane & 15;          // token pair within the 32-token chunk
   const float mh = ph == 0 ? m[0] : (ph == 1 ? m[1] : (ph == 2 ? m[2] : m[3]));
+  const float ks = __fmul_rn(P.softmax_scale, 1.44269504088896341f);   // sigma log2(e)
   const float cf = (float)P.c;
   const float tau = P.tau;
-  const float* lrow = logit + ph * kMaxTok;
-  float lacc = 0.0f;
+  const float* lrow = sm.logit + ph * kMaxTok + 2 * pj;
+  uint32_t* pst_w = &sm.pst[wave][ph][pj];
+  const u32x4_t* pst_r = reinterpret_cast<const u32x4_t*>(&sm.pst[wave][row][4 * kg]);
+  float lacc = 0.0f;                 // sum of c p over this lane's tokens
   f32x4_t acco[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acco[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  for (int pi = wave; pi < npg; pi += 4) {
+  auto v_page = [&](const VPage& vcur, VPage& vnxt, int pi) {
     if (pi + 4 < npg) load_v<kMx>(vnxt, P, blk_of(pi + 4), lane);
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-      // probabilities of tokens (2 pj, 2 pj + 1), head ph
-      const int local = pi * kPage + ch * 32 + 2 * pj;
-      const float2 tt = *reinterpret_cast<const float2*>(lrow + local);
-      const float e0 = (mh == kNegInf) ? 0.0f : __expf(tt.x - mh);
-      const float e1 = (mh == kNegInf) ? 0.0f : __expf(tt.y - mh);
-      lacc += e0 + e1;
-      const float q0 = cf * e0, q1 = cf * e1;
-      const float a = max8(fmaxf(q0, q1));     // the aligned 16-token block is 8 lanes
-      const uint32_t scode = e4m3_encode((kUnder && a < tau) ? a * 0.5f : a / 6.0f);
-      const float sv = e4m3_value(scode);
-      const E2m1Thr T = e2m1_thresholds(sv);
-      const float g0 = T.zero ? 0.0f : __fmul_rn(e2m1_grid(e2m1_mag(q0, T)), sv);
-      const float g1 = T.zero ? 0.0f : __fmul_rn(e2m1_grid(e2m1_mag(q1, T)), sv);
-      *reinterpret_cast<uint32_t*>(&sm.p[wave][ph][2 * pj]) = op16<kMx>(g0) | (op16<kMx>(g1) << 16);
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging visible to the wave
-      __builtin_amdgcn_wave_barrier();
-      u32x4_t ap = {0u, 0u, 0u, 0u};
-      if (row < 4) {
-        const uint4 t = *reinterpret_cast<const uint4*>(&sm.p[wave][row][8 * kg]);
-        ap[0] = t.x; ap[1] = t.y; ap[2] = t.z; ap[3] = t.w;
+      // p' = c exp(sigma (t - m)) of tokens 2 pj, 2 pj + 1 of the chunk, head ph
+      const float2 tt = *reinterpret_cast<const float2*>(lrow + pi * kPage + ch * 32);
+      const float x0 = __fmul_rn(cf, __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(tt.x, mh), ks)));
+      const float x1 = __fmul_rn(cf, __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(tt.y, mh), ks)));
+      lacc = __fadd_rn(lacc, __fadd_rn(x0, x1));
+      // block maximum over the aligned 16 tokens (8 lanes); p' >= 0, so the
+      // unsigned order of the bit patterns is the float order
+      const float a = __uint_as_float(umax_dpp8(max(__float_as_uint(x0), __float_as_uint(x1))));
+      const uint32_t sc = p_scale_code<kUnder>(a, tau);
+      const float sv = e4m3_value(sc);
+      const uint32_t byte =
+          sv > 0.0f ? e2m1_pair(x0, x1, sv, significand(sv), sm.rcp[sig_index(sv)]) : 0u;
+      uint32_t word;
+      if (kMx) {
+        const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+        word = __builtin_amdgcn_perm(__float_as_uint(__fmul_rn(g[1], sv)), __float_as_uint(__fmul_rn(g[0], sv)),
+                                     0x07060302u);
+      } else {
+        const f16x2_t s16 = e4m3_pair_f16(sc * 0x0101u, false);
+        word = u32_of(grid_f16_pair(byte, 0) * s16);
       }
+      *pst_w = word;
+      const u32x4_t ap = *pst_r;     // LDS instructions of one wave complete in order
       const uint4 v0 = vcur.code[2 * ch], v1 = vcur.code[2 * ch + 1];
       const uint2 vs = vcur.sc[ch];
       const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -612,9 +635,15 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
           acco[j] = mfma<kMx>(ap, bv, acco[j]);
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
-    vcur = vnxt;
+  };
+  {
+    VPage vb;
+    for (int pi = wave; pi < npg; pi += 8) {
+      v_page(vcur, vb, pi);
+      if (pi + 4 >= npg) break;
+      v_page(vb, vcur, pi + 4);
+    }
   }
   lacc = sum16(lacc);                // lanes of one head are a 16-lane row
   if (pj == 0) sm.lsum[wave][ph] = lacc;
@@ -643,8 +672,9 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   const float nan = __builtin_nanf("");
   pstore2(part + head * kD + d, poisoned ? nan : o0 * invc, poisoned ? nan : o1 * invc);
   if (tid < 4) {
-    pstore(part + 512 + tid, poisoned ? 0.0f : m[tid]);
-    pstore(part + 516 + tid, poisoned ? 1.0f : sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid]);
+    const float l = (sm.lsum[0][tid] + sm.lsum[1][tid]) + (sm.lsum[2][tid] + sm.lsum[3][tid]);
+    pstore(part + 512 + tid, poisoned ? 0.0f : m[tid] * P.softmax_scale);
+    pstore(part + 516 + tid, poisoned ? 1.0f : l * invc);
   }
 }
 
@@ -652,23 +682,32 @@ template <bool kMx, int kTerms, bool kUnder>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
-  const int nps = P.max_parts + 1;
-  const int s = blockIdx.x % nps;
-  const int bh = blockIdx.x / nps;
+  const int G = P.max_parts > 0 ? P.max_parts : 1;     // workgroups per (sequence, KV head)
+  const int sp = blockIdx.x % G;
+  const int bh = blockIdx.x / G;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
   const int L = P.seq_lens[b];
   const int n_full = L > 0 ? L / kPage : 0;
   if (L < 1 || L > P.max_seq_len || n_full > P.max_pages_per_seq) {
-    if (s == 0) poison_rows(P.out, P.hq, b, h);
+    if (sp == 0) poison_rows(P.out, P.hq, b, h);
     return;
   }
   const int nparts = n_full > 0 ? (n_full + P.ppp - 1) / P.ppp : 0;
-  if (s > nparts) return;
-  if (s == 0)
-    bf16_partition(A, sm, b, h, L, n_full);
-  else
+  const int s = sp + 1;                                 // FP4 partition of this workgroup
+  if (s > nparts && sp != 0) return;
+  int inc = 0;
+  if (s <= nparts) {
     fp4_partition<kMx, kTerms, kUnder>(A, sm, b, h, s, L, n_full);
-  publish_and_merge(merge_ctx(A), &sm.ticket, &sm.red[0][0], sm.logit, 4 * kMaxTok, b, h, nparts + 1);
+    ++inc;
+  }
+  if (sp == 0) {
+    // the BF16 partition (slot 0) rides on the first workgroup, after its
+    // FP4 pages, so the grid is exactly one workgroup per FP4 partition
+    if (inc) __syncthreads();
+    bf16_partition(A, sm, b, h, L, n_full);
+    ++inc;
+  }
+  publish_and_merge(merge_ctx(A), &sm.ticket, &sm.red[0][0], sm.logit, 4 * kMaxTok, b, h, nparts + 1, inc);
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
@@ -676,7 +715,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   A.L = L;
   A.counters = static_cast<uint32_t*>(L.workspace);
   A.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(L.workspace) + kCounterBytes);
-  const dim3 grid((unsigned)(L.batch * L.hkv * (L.max_parts + 1))), block(256u);
+  const dim3 grid((unsigned)(L.batch * L.hkv * (L.max_parts > 0 ? L.max_parts : 1))), block(256u);
   const bool under = L.p_mode == 4;
 #define BDFP4_LAUNCH(MX, T, U) hipLaunchKernelGGL((decode_kernel<MX, T, U>), grid, block, 0, stream, A)
   if (L.mx) {

@@ -47,8 +47,9 @@ __device__ __forceinline__ float pload(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// All 256 threads call this after the partial of slot s is stored.
-// n_slots: number of partials of this (sequence, KV head). s_red: LDS scratch
+// All 256 threads call this after the workgroup's partials are stored.
+// n_slots: number of partials of this (sequence, KV head); inc: how many of
+// them this workgroup stored (the ticket advances by inc). s_red: LDS scratch
 // of at least 16 floats; s_w: LDS scratch of w_cap floats; s_ticket: one LDS
 // int.
 // The merging workgroup reads the slots in parallel: the per-head maxima and
@@ -57,14 +58,15 @@ __device__ __forceinline__ float pload(const float* p) {
 // over four groups of 64 threads (each a quarter of the slots, 8 channels
 // per thread, all its loads issued together) and added up in LDS.
 __device__ __forceinline__ void publish_and_merge(const MergeCtx& C, int* s_ticket, float* s_red, float* s_w,
-                                                  int w_cap, int b, int h, int n_slots) {
+                                                  int w_cap, int b, int h, int n_slots, int inc = 1) {
   const int bh = b * C.hkv + h;
   __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this thread's partial stores are complete
   __syncthreads();
   if (threadIdx.x == 0)
-    *s_ticket = (int)__hip_atomic_fetch_add(&C.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_ticket = (int)__hip_atomic_fetch_add(&C.counters[bh], (uint32_t)inc, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (*s_ticket != n_slots - 1) return;
+  if (*s_ticket + inc != n_slots) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float ninf = -__builtin_inff();
   const float* base = partial_slot(C, bh, 0);

@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(256) p_blocks_kernel(const float* pp, int n_bl
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, x[i]);
-  const uint32_t sc = e4m3_encode((mode == 4 && a < tau) ? a * 0.5f : a / 6.0f);
+  const uint32_t sc = mode == 4 ? p_scale_code<true>(a, tau) : p_scale_code<false>(a, tau);
   uint32_t pk[2];
   quant_block<16, false>(x, e4m3_value(sc), pk);
   *reinterpret_cast<uint2*>(codes + (size_t)b * 8) = make_uint2(pk[0], pk[1]);
