@@ -206,7 +206,7 @@ def cpu_baseline(args):
     k, v, ids = wl.writer_inputs()
     W.write_pages(r, cache, k, v, ids, wl.key_shift)
     sk, sv, tk, tv = wl.sink_tail()
-    ppp = 8
+    ppp = 4
     t0 = time.perf_counter()
     OD.decode(r, cache, wl.q, wl.block_tables, wl.seq_lens, sk, sv, tk, tv, wl.key_shift, wl.sigma, ppp)
     dt = time.perf_counter() - t0

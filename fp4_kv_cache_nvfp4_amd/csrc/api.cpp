@@ -115,14 +115,15 @@ bdfp4_status check_cache(const bdfp4_cache* c) {
 
 int32_t auto_ppp(int32_t batch, int32_t hkv, int32_t max_seq_len) {
   const int64_t n_full = max_seq_len / 128;
-  const int64_t work = (int64_t)batch * hkv * n_full;
-  int64_t ppp = (work + 511) / 512;       // about 512 FP4 workgroups: 2 resident per CU
+  const int64_t work = (int64_t)batch * hkv * n_full;     // full page-heads
+  // about 512 FP4 workgroups of four partitions: 2 resident per CU
+  int64_t ppp = (work + 2047) / 2048;
   if (ppp < 1) ppp = 1;
-  if (ppp > 16) ppp = 16;
+  if (ppp > 4) ppp = 4;
   return (int32_t)ppp;
 }
 
-constexpr int32_t kMaxPpp = 16;
+constexpr int32_t kMaxPpp = 4;   // a partition is one wave's pages; its logits sit in LDS
 
 bdfp4_status plan(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_in, int32_t* ppp,
                   int32_t* parts) {

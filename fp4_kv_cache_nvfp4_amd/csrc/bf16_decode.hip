@@ -187,14 +187,15 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
     o0 += sm.o[w][head][d];
     o1 += sm.o[w][head][d + 1];
   }
-  float* part = partial_slot(C, bh, s);
   const bool poisoned = sm.flag != 0;
   const float nan = __builtin_nanf("");
-  pstore2(part + head * kD + d, poisoned ? nan : o0, poisoned ? nan : o1);
-  if (tid < 4) {
-    pstore(part + 512 + tid, poisoned ? 0.0f : m[tid]);
-    pstore(part + 516 + tid, poisoned ? 1.0f : sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid]);
+  float mm[4], ll[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    mm[g] = poisoned ? 0.0f : m[g];
+    ll[g] = poisoned ? 1.0f : (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
   }
+  write_partial(partial_writer(C, bh, s), poisoned ? nan : o0, poisoned ? nan : o1, mm, ll);
   publish_and_merge(C, &sm.ticket, &sm.red[0][0], sm.logit, kMaxTokB * 4, b, h, nparts);
 }
 

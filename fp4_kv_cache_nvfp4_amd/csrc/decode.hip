@@ -73,8 +73,17 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxPpp = 16;
-constexpr int kMaxTok = kMaxPpp * kPage;   // tokens of one partition
+constexpr int kMaxPpw = 4;                 // pages per partition = per wave
+constexpr int kWaveTok = kMaxPpw * kPage;  // tokens of one partition
+
+// Workgroups per (sequence, KV head) for a number of FP4 partitions: four
+// partitions (one per wave) per workgroup, and at least one workgroup, which
+// also carries the BF16 partition.
+__host__ __device__ __forceinline__ int wgs_for_parts(int parts) { return (parts + 3) / 4; }
+__host__ __device__ __forceinline__ int wgs_per_seq(int max_parts) {
+  const int g = wgs_for_parts(max_parts);
+  return g > 0 ? g : 1;
+}
 constexpr float kNegInf = -__builtin_inff();
 
 struct DecArgs {
@@ -143,15 +152,15 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
 // ------------------------------------------------------------ shared memory
 
 struct Smem {
-  float logit[4 * kMaxTok];                 // [head][token] raw logits; reused for the o reduction
+  float logit[4][4 * kWaveTok];             // per wave: [head][token] raw logits; then its o [head][128]
   uint16_t qhat[2][4][kD];                  // 16-bit dequantized query terms [term][head][channel]
   float q[4][kD];                           // raw float32 query (BF16 partition)
   uint32_t pst[4][16][16];                  // per wave: P_hat staging [row][token pair]; rows 4..15 stay 0
   float qmu[4];
-  float red[4][4];                          // per wave, per head
-  float lsum[4][4];
+  float red[4][4];                          // per wave, per head: partition maximum (raw logit)
+  float lsum[4][4];                         // per wave, per head: sum of c p
   float rcp[8];                             // RN(1 / (1 + k/8)), k = 0..7
-  int page[kMaxPpp];                        // physical pages of the partition (-1: invalid)
+  int bad[4];                               // per wave: its block table names an invalid page
   int ticket;
 };
 
@@ -168,15 +177,14 @@ __device__ __forceinline__ MergeCtx merge_ctx(const DecArgs& A) {
   return C;
 }
 
-__device__ __forceinline__ float* partial_ptr(const DecArgs& A, int bh, int s) {
-  return partial_slot(merge_ctx(A), bh, s);
-}
 
 // ------------------------------------------------------------ BF16 partition
 
 // Tokens [0, min(S, L)) from the sink buffer and [max(S, 128 n), L) from the
-// tail page: exact float32 attention of the raw query, thread = token for the
-// logits, thread = (head, channel pair) for o.
+// tail page: exact float32 attention of the raw query. All of the
+// workgroup's loads (K row of token t for thread t, the query, and the V rows
+// of its token group for thread (token group, channel quad)) are issued
+// before the first barrier, so the partition costs one memory round trip.
 __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x;
@@ -185,28 +193,36 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
   const int tail_lo = S > kPage * n_full ? S : kPage * n_full;
   const int ntail = L > tail_lo ? L - tail_lo : 0;
   const int nb = nsink + ntail;                      // <= 112 + 127 < 256
+  const size_t bhk = (size_t)b * P.hkv + h;
+  const int tail0 = tail_lo - kPage * n_full;
+  auto row_of = [&](const uint16_t* sink, const uint16_t* tail, int j) -> const uint16_t* {
+    return j < nsink ? sink + (bhk * S + j) * kD : tail + (bhk * kPage + tail0 + (j - nsink)) * kD;
+  };
+  uint4 kw[16];
+  if (tid < nb) {
+    const uint4* k4 = reinterpret_cast<const uint4*>(row_of(P.sink_k, P.tail_k, tid));
+#pragma unroll
+    for (int c = 0; c < 16; ++c) kw[c] = k4[c];
+  }
+  constexpr int kVPer = 30;                          // ceil(240 / 8) tokens per token group
+  const int tg = tid >> 5, cq = tid & 31;            // token group, channel quad
+  uint2 vv[kVPer];
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    const int j = tg + 8 * k;
+    vv[k] = j < nb ? *reinterpret_cast<const uint2*>(row_of(P.sink_v, P.tail_v, j) + 4 * cq) : make_uint2(0u, 0u);
+  }
   for (int i = tid; i < 4 * kD; i += 256) {
     const int g = i >> 7, d = i & 127;
     sm.q[g][d] = bf16_lo(P.q[((size_t)b * P.hq + h * kGroup + g) * kD + d]);
   }
   __syncthreads();
   float t[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-  const int tok = tid;
-  if (tok < nb) {
-    const uint16_t* krow;
-    if (tok < nsink)
-      krow = P.sink_k + (((size_t)b * P.hkv + h) * S + tok) * kD;
-    else
-      krow = P.tail_k + (((size_t)b * P.hkv + h) * kPage + (tail_lo - kPage * n_full) + (tok - nsink)) * kD;
+  if (tid < nb) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const uint4* k4 = reinterpret_cast<const uint4*>(krow);
-    uint4 kw[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) kw[c] = k4[c];      // the whole row in flight at once
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const uint4 w = kw[c];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      const uint32_t ww[4] = {kw[c].x, kw[c].y, kw[c].z, kw[c].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 8 * c + 2 * i;
@@ -236,40 +252,61 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
   for (int g = 0; g < 4; ++g)
     m[g] = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
   float ls[4];
+  float4 pr;
+  {
+    float pv[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const float p = (tok < nb && m[g] != kNegInf) ? __expf(t[g] - m[g]) : 0.0f;
-    sm.logit[tok * 4 + g] = p;
-    float v = p;
-    for (int o = 32; o >= 1; o >>= 1) v += shfl_xor(v, o);
-    ls[g] = v;
+    for (int g = 0; g < 4; ++g) {
+      const float p = (tid < nb && m[g] != kNegInf) ? __expf(t[g] - m[g]) : 0.0f;
+      pv[g] = p;
+      float v = p;
+      for (int o = 32; o >= 1; o >>= 1) v += shfl_xor(v, o);
+      ls[g] = v;
+    }
+    pr = make_float4(pv[0], pv[1], pv[2], pv[3]);
   }
-  __syncthreads();
+  float* flat = &sm.logit[0][0];
+  reinterpret_cast<float4*>(flat)[tid] = pr;         // p of token tid, [token][head]
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) sm.lsum[wave][g] = ls[g];
   }
+  __syncthreads();
+  // o[head][4 cq .. +4] over the tokens tg, tg + 8, ... of this thread
+  float o[4][4] = {};
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    const int j = tg + 8 * k;
+    if (j < nb) {
+      const float4 p = reinterpret_cast<const float4*>(flat)[j];
+      const float v[4] = {bf16_lo(vv[k].x), bf16_hi(vv[k].x), bf16_lo(vv[k].y), bf16_hi(vv[k].y)};
+      const float pg[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[g][c] = fmaf(pg[g], v[c], o[g][c]);
+      }
+    }
+  }
+  float* so = flat + 1024;                           // [token group][head][128], past the p values
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<float4*>(so + (tg * 4 + g) * kD + 4 * cq) = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+  __syncthreads();
   const int head = tid >> 6, d = (tid & 63) * 2;
   float o0 = 0.f, o1 = 0.f;
-#pragma unroll 16
-  for (int j = 0; j < nb; ++j) {
-    const uint16_t* vrow;
-    if (j < nsink)
-      vrow = P.sink_v + (((size_t)b * P.hkv + h) * S + j) * kD;
-    else
-      vrow = P.tail_v + (((size_t)b * P.hkv + h) * kPage + (tail_lo - kPage * n_full) + (j - nsink)) * kD;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + d);
-    const float p = sm.logit[j * 4 + head];
-    o0 = fmaf(p, bf16_lo(w), o0);
-    o1 = fmaf(p, bf16_hi(w), o1);
+#pragma unroll
+  for (int g8 = 0; g8 < 8; ++g8) {
+    o0 += so[(g8 * 4 + head) * kD + d];
+    o1 += so[(g8 * 4 + head) * kD + d + 1];
   }
-  __syncthreads();
-  float* part = partial_ptr(A, b * P.hkv + h, 0);
-  pstore2(part + head * kD + d, o0, o1);
-  if (tid < 4) {
-    pstore(part + 512 + tid, nb > 0 ? m[tid] : kNegInf);
-    pstore(part + 516 + tid, sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid]);
+  float mm[4], ll[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    mm[g] = nb > 0 ? m[g] : kNegInf;
+    ll[g] = (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
   }
+  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, 0), o0, o1, mm, ll);
 }
 
 // ------------------------------------------------------------ query prologue
@@ -415,7 +452,7 @@ __device__ __forceinline__ void load_v(VPage& v, const DecodeLaunch& P, size_t b
   }
 }
 
-// ------------------------------------------------------------ FP4 partition
+// ------------------------------------------------------------ FP4 partitions
 
 __device__ __forceinline__ uint32_t umax_dpp8(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false));
@@ -423,38 +460,45 @@ __device__ __forceinline__ uint32_t umax_dpp8(uint32_t v) {
   return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowHalfMirror, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// The four FP4 partitions 4 sp + w (w = wave) of one (sequence, KV head):
+// each wave streams its own pages_per_partition consecutive pages through
+// pass 1, its own maximum and pass 2 with no workgroup barrier in between;
+// the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
+// workgroup's partial (slot sp + 1). With with_bf16 the workgroup also
+// computes the BF16 partition (slot 0) while its first K pages are loading.
 template <bool kMx, int kTerms, bool kUnder>
-__device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, int L, int n_full) {
+__device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, int n_full, bool with_bf16) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p0 = (s - 1) * P.ppp;
-  const int p1 = min(n_full, s * P.ppp);
-  const int npg = p1 - p0;
+  const int p0 = (4 * sp + wave) * P.ppp;                       // first page of this wave's partition
+  const int npg = max(0, min(n_full, p0 + P.ppp) - p0);         // its pages, 0 .. pages_per_partition
   const size_t hkv = P.hkv;
 
-  // the query row of this wave and the key means, first so their latency
-  // overlaps the page-id staging and the first page loads
+  // physical pages of the partition: lane i < npg holds page p0 + i
+  int pid = 0;
+  if (lane < npg) pid = P.block_tables[(size_t)b * P.max_pages_per_seq + p0 + lane];
+  const bool bad_lane = lane < npg && (pid < 0 || pid >= P.num_pages);
+  const bool bad = __ballot(bad_lane) != 0;
+  if (bad_lane) pid = 0;                                        // keep addresses inside the cache
+  auto blk_of = [&](int pi) -> size_t { return (size_t)__builtin_amdgcn_readlane(pid, pi) * hkv + h; };
+
+  // the query row of this wave and the key means
   const uint32_t qw =
       reinterpret_cast<const uint32_t*>(P.q + ((size_t)b * P.hq + h * kGroup + wave) * kD)[lane];
   const float2 mu = P.key_smoothing ? reinterpret_cast<const float2*>(P.key_shift + h * kD)[lane]
                                     : make_float2(0.0f, 0.0f);
-  if (tid < npg) {
-    const int ph = P.block_tables[(size_t)b * P.max_pages_per_seq + p0 + tid];
-    sm.page[tid] = (ph < 0 || ph >= P.num_pages) ? -1 : ph;
-  }
   if (tid < 8) sm.rcp[tid] = rcp_significand((uint32_t)tid);
   {
     uint32_t* pz = &sm.pst[0][0][0];       // rows 4 .. 15 of every wave's staging tile
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
-  __syncthreads();
-  auto blk_of = [&](int pi) -> size_t {
-    const int ph = sm.page[pi];
-    return (size_t)(ph < 0 ? 0 : ph) * hkv + h;
-  };
-
-  KPage kcur;
-  if (wave < npg) load_k<kMx>(kcur, P, blk_of(wave), lane);
+  KPage kA;
+  if (npg > 0) load_k<kMx>(kA, P, blk_of(0), lane);
+  if (with_bf16) bf16_partition(A, sm, b, h, L, n_full);
   query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
 
@@ -480,8 +524,9 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
     acc0[0] = sm.qmu[2 * kg];
     acc0[2] = sm.qmu[2 * kg + 1];
   }
-  float* lg_a = sm.logit + (2 * (kg & 1)) * kMaxTok + row;   // head 2 kg (lanes < 32)
-  float* lg_b = lg_a + kMaxTok;                                // head 2 kg + 1
+  float* lgw = &sm.logit[wave][0];                              // this wave's [head][token]
+  float* lg_a = lgw + (2 * (kg & 1)) * kWaveTok + row;          // head 2 kg (lanes < 32)
+  float* lg_b = lg_a + kWaveTok;                                // head 2 kg + 1
 
   // ---- pass 1: raw logits q . mu + q_hat . k_hat
   // Sink tokens (global tokens below the sink size, a multiple of 16) fill
@@ -489,12 +534,12 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
   const int sink_tiles = p0 == 0 ? P.sink / 16 : 0;
   float ma = kNegInf, mb = kNegInf;
   auto k_page = [&](const KPage& cur, KPage& nxt, int pi) {
-    if (pi + 4 < npg) load_k<kMx>(nxt, P, blk_of(pi + 4), lane);
-    const int skip = pi == 0 ? sink_tiles : 0;             // uniform
+    if (pi + 1 < npg) load_k<kMx>(nxt, P, blk_of(pi + 1), lane);
+    const int skip = pi == 0 ? sink_tiles : 0;                  // uniform
     float pa = kNegInf, pb = kNegInf;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int local = pi * kPage + t * 16;               // token - 128 p0 of the tile's first token
+      const int local = pi * kPage + t * 16;                    // first token of the tile - 128 p0
       if (t < skip) {
         if (lane < 32) {
           lg_a[local] = kNegInf;
@@ -505,7 +550,7 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
       u32x4_t bk[4];
       if (kMx) {
         const uint32_t sb = (word_of(cur.sc, t >> 2) >> (8 * (t & 3))) & 0xFFu;
-        const float sv = pow2_f32((int)sb - 127);
+        const float sv = __uint_as_float(sb << 23);             // E8M0: only the exponent field is used
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t cw = word_of(cur.code[t], c);
@@ -513,8 +558,8 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
                             cvt_bf16_pair(cw, sv, 3)};
         }
       } else {
-        const f16x2_t sp = e4m3_pair_f16(word_of(cur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
-        const f16x2_t slo = {sp[0], sp[0]}, shi = {sp[1], sp[1]};
+        const f16x2_t sp2 = e4m3_pair_f16(word_of(cur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
+        const f16x2_t slo = {sp2[0], sp2[0]}, shi = {sp2[1], sp2[1]};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t cw = word_of(cur.code[t], c);
@@ -539,35 +584,28 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
     mb = __builtin_fmaxf(mb, pb);
   };
   {
-    KPage kb;
-    for (int pi = wave; pi < npg; pi += 8) {
-      k_page(kcur, kb, pi);
-      if (pi + 4 >= npg) break;
-      k_page(kb, kcur, pi + 4);
+    KPage kB;
+    for (int pi = 0; pi < npg; pi += 2) {
+      k_page(kA, kB, pi);
+      if (pi + 1 >= npg) break;
+      k_page(kB, kA, pi + 1);
     }
   }
-  VPage vcur;
-  if (wave < npg) load_v<kMx>(vcur, P, blk_of(wave), lane);
+  VPage vA;
+  if (npg > 0) load_v<kMx>(vA, P, blk_of(0), lane);
+  // the partition maximum of each head (rows of 16 lanes hold heads 2 kg, 2 kg + 1)
   ma = max16(ma);
   mb = max16(mb);
-  if (lane == 0 || lane == 16) {
-    sm.red[wave][2 * kg] = ma;
-    sm.red[wave][2 * kg + 1] = mb;
-  }
-  __syncthreads();
-  float m[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-    m[g] = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
+  const float m4[4] = {readlane_f32(ma, 0), readlane_f32(mb, 0), readlane_f32(ma, 16), readlane_f32(mb, 16)};
 
   // ---- pass 2: P, PV
   const int ph = lane >> 4;          // head of this lane in the P step
   const int pj = lane & 15;          // token pair within the 32-token chunk
-  const float mh = ph == 0 ? m[0] : (ph == 1 ? m[1] : (ph == 2 ? m[2] : m[3]));
+  const float mh = ph == 0 ? m4[0] : (ph == 1 ? m4[1] : (ph == 2 ? m4[2] : m4[3]));
   const float ks = __fmul_rn(P.softmax_scale, 1.44269504088896341f);   // sigma log2(e)
   const float cf = (float)P.c;
   const float tau = P.tau;
-  const float* lrow = sm.logit + ph * kMaxTok + 2 * pj;
+  const float* lrow = lgw + ph * kWaveTok + 2 * pj;
   uint32_t* pst_w = &sm.pst[wave][ph][pj];
   const u32x4_t* pst_r = reinterpret_cast<const u32x4_t*>(&sm.pst[wave][row][4 * kg]);
   float lacc = 0.0f;                 // sum of c p over this lane's tokens
@@ -575,7 +613,7 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
 #pragma unroll
   for (int j = 0; j < 8; ++j) acco[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   auto v_page = [&](const VPage& vcur, VPage& vnxt, int pi) {
-    if (pi + 4 < npg) load_v<kMx>(vnxt, P, blk_of(pi + 4), lane);
+    if (pi + 1 < npg) load_v<kMx>(vnxt, P, blk_of(pi + 1), lane);
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
       // p' = c exp(sigma (t - m)) of tokens 2 pj, 2 pj + 1 of the chunk, head ph
@@ -610,7 +648,7 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
 #pragma unroll
         for (int ii = 0; ii < 8; ++ii) {
           const uint32_t sb = (ii < 4 ? (vs.x >> (8 * ii)) : (vs.y >> (8 * (ii - 4)))) & 0xFFu;
-          const float svv = pow2_f32((int)sb - 127);
+          const float svv = __uint_as_float(sb << 23);
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) x[ii][bb] = cvt_bf16_pair(vw[ii], svv, bb);
         }
@@ -625,64 +663,93 @@ __device__ void fp4_partition(const DecArgs& A, Smem& sm, int b, int h, int s, i
         }
       } else {
         // token pairs per byte: byte r of vw[j] = tokens 8 kg + 2r, +1 at channel 8n + j
-        const f16x2_t sp[4] = {e4m3_pair_f16(vs.x, false), e4m3_pair_f16(vs.x, true),
-                               e4m3_pair_f16(vs.y, false), e4m3_pair_f16(vs.y, true)};
+        const f16x2_t spv[4] = {e4m3_pair_f16(vs.x, false), e4m3_pair_f16(vs.x, true),
+                                e4m3_pair_f16(vs.y, false), e4m3_pair_f16(vs.y, true)};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           u32x4_t bv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bv[r] = u32_of(grid_f16_pair(vw[j], r) * sp[r]);
+          for (int r = 0; r < 4; ++r) bv[r] = u32_of(grid_f16_pair(vw[j], r) * spv[r]);
           acco[j] = mfma<kMx>(ap, bv, acco[j]);
         }
       }
     }
   };
   {
-    VPage vb;
-    for (int pi = wave; pi < npg; pi += 8) {
-      v_page(vcur, vb, pi);
-      if (pi + 4 >= npg) break;
-      v_page(vb, vcur, pi + 4);
+    VPage vB;
+    for (int pi = 0; pi < npg; pi += 2) {
+      v_page(vA, vB, pi);
+      if (pi + 1 >= npg) break;
+      v_page(vB, vA, pi + 1);
     }
   }
-  lacc = sum16(lacc);                // lanes of one head are a 16-lane row
-  if (pj == 0) sm.lsum[wave][ph] = lacc;
-  __syncthreads();                   // all waves done with the logits: reuse for o
-  float* so = sm.logit;              // [wave][head][128]
+  // ---- this wave's (m, l, o) to LDS: o over its own logit rows (read above
+  // by this wave only; its LDS instructions complete in order)
+  lacc = sum16(lacc);                // rows of 16 lanes = heads
+  float* so = lgw;                   // [head][128]
   if (lane < 16) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4* dst = reinterpret_cast<float4*>(so + (wave * 4 + r) * kD + 8 * lane);
+      float4* dst = reinterpret_cast<float4*>(so + r * kD + 8 * lane);
       dst[0] = make_float4(acco[0][r], acco[1][r], acco[2][r], acco[3][r]);
       dst[1] = make_float4(acco[4][r], acco[5][r], acco[6][r], acco[7][r]);
     }
   }
+  // cross-lane reads in uniform control flow: a lane's value is only
+  // guaranteed to live on while that lane itself still uses it
+  const float l4[4] = {readlane_f32(lacc, 0), readlane_f32(lacc, 16), readlane_f32(lacc, 32),
+                       readlane_f32(lacc, 48)};
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      sm.red[wave][g] = m4[g];
+      sm.lsum[wave][g] = l4[g];
+    }
+    sm.bad[wave] = bad ? 1 : 0;
+  }
   __syncthreads();
-  const int head = tid >> 6, d = (tid & 63) * 2;
+  // ---- log-sum-exp merge of the four partitions: thread (head, channel pair)
+  const float sigma = P.softmax_scale;
   const float invc = 1.0f / cf;      // exact (c is a power of two)
+  float mm[4], ll[4], wgt[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float M = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm.red[w][g];
+      wgt[g][w] = mw == kNegInf ? 0.0f : __expf(sigma * (mw - M));
+      l = fmaf(wgt[g][w], sm.lsum[w][g], l);
+    }
+    mm[g] = sigma * M;
+    ll[g] = l * invc;
+  }
+  const int head = tid >> 6, d = (tid & 63) * 2;
+  const float* wh = head == 0 ? wgt[0] : (head == 1 ? wgt[1] : (head == 2 ? wgt[2] : wgt[3]));
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    o0 += so[(w * 4 + head) * kD + d];
-    o1 += so[(w * 4 + head) * kD + d + 1];
+    const float* ow = &sm.logit[w][head * kD + d];
+    o0 = fmaf(wh[w], ow[0], o0);
+    o1 = fmaf(wh[w], ow[1], o1);
   }
-  bool poisoned = false;
-  for (int i = 0; i < npg; ++i) poisoned |= sm.page[i] < 0;
-  float* part = partial_ptr(A, b * P.hkv + h, s);
+  const bool poisoned = (sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3]) != 0;
   const float nan = __builtin_nanf("");
-  pstore2(part + head * kD + d, poisoned ? nan : o0 * invc, poisoned ? nan : o1 * invc);
-  if (tid < 4) {
-    const float l = (sm.lsum[0][tid] + sm.lsum[1][tid]) + (sm.lsum[2][tid] + sm.lsum[3][tid]);
-    pstore(part + 512 + tid, poisoned ? 0.0f : m[tid] * P.softmax_scale);
-    pstore(part + 516 + tid, poisoned ? 1.0f : l * invc);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    mm[g] = poisoned ? 0.0f : mm[g];
+    ll[g] = poisoned ? 1.0f : ll[g];
   }
+  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, sp + 1), poisoned ? nan : o0 * invc,
+                poisoned ? nan : o1 * invc, mm, ll);
 }
 
 template <bool kMx, int kTerms, bool kUnder>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
-  const int G = P.max_parts > 0 ? P.max_parts : 1;     // workgroups per (sequence, KV head)
+  const int G = wgs_per_seq(P.max_parts);
   const int sp = blockIdx.x % G;
   const int bh = blockIdx.x / G;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
@@ -693,21 +760,18 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     return;
   }
   const int nparts = n_full > 0 ? (n_full + P.ppp - 1) / P.ppp : 0;
-  const int s = sp + 1;                                 // FP4 partition of this workgroup
-  if (s > nparts && sp != 0) return;
-  int inc = 0;
-  if (s <= nparts) {
-    fp4_partition<kMx, kTerms, kUnder>(A, sm, b, h, s, L, n_full);
-    ++inc;
+  const int nwg = wgs_for_parts(nparts);                        // FP4 workgroups of this sequence
+  if (sp >= nwg && sp != 0) return;
+  int inc;
+  if (sp < nwg) {
+    fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L, n_full, sp == 0);
+    inc = sp == 0 ? 2 : 1;
+  } else {
+    bf16_partition(A, sm, b, h, L, n_full);                     // no full page: the BF16 tokens only
+    inc = 1;
   }
-  if (sp == 0) {
-    // the BF16 partition (slot 0) rides on the first workgroup, after its
-    // FP4 pages, so the grid is exactly one workgroup per FP4 partition
-    if (inc) __syncthreads();
-    bf16_partition(A, sm, b, h, L, n_full);
-    ++inc;
-  }
-  publish_and_merge(merge_ctx(A), &sm.ticket, &sm.red[0][0], sm.logit, 4 * kMaxTok, b, h, nparts + 1, inc);
+  publish_and_merge(merge_ctx(A), &sm.ticket, &sm.red[0][0], &sm.logit[0][0], 4 * 4 * kWaveTok, b, h, nwg + 1,
+                    inc);
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
@@ -715,7 +779,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   A.L = L;
   A.counters = static_cast<uint32_t*>(L.workspace);
   A.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(L.workspace) + kCounterBytes);
-  const dim3 grid((unsigned)(L.batch * L.hkv * (L.max_parts > 0 ? L.max_parts : 1))), block(256u);
+  const dim3 grid((unsigned)(L.batch * L.hkv * wgs_per_seq(L.max_parts))), block(256u);
   const bool under = L.p_mode == 4;
 #define BDFP4_LAUNCH(MX, T, U) hipLaunchKernelGGL((decode_kernel<MX, T, U>), grid, block, 0, stream, A)
   if (L.mx) {

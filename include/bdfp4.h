@@ -151,9 +151,11 @@ bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cach
                                   const int32_t* page_ids, int32_t n_pages,
                                   const float* key_shift, void* stream);
 
-/* Split plan of bdfp4_decode_attention (host). pages_per_partition = 0 picks
- * one from (batch, num_kv_heads, max_seq_len); the chosen value and the number
- * of FP4 partitions of the longest sequence are returned. */
+/* Split plan of bdfp4_decode_attention (host). pages_per_partition (1 .. 4)
+ * is the number of consecutive full pages one FP4 partition covers; 0 picks
+ * it from (batch, num_kv_heads, max_seq_len) so that about 512 workgroups of
+ * four partitions are launched. The chosen value and the number of FP4
+ * partitions of the longest sequence are returned. */
 bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads,
                                int32_t max_seq_len, int32_t pages_per_partition,
                                int32_t* pages_per_partition_out,
@@ -191,7 +193,8 @@ bdfp4_status bdfp4_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  * tokens [max(sink, 128 floor(L/128)), L) from the BF16 buffers. The query is
  * rotated and quantized as Q1 + Q2 (scale_mode_q); an FP4 token's logit is
  * sigma * (q_hat . k_hat + q . mu). Partition 0 holds the BF16 tokens (exact
- * float32 attention); partitions 1..S hold pages_per_partition pages each.
+ * float32 attention); partitions 1..S hold pages_per_partition (1 .. 4)
+ * consecutive full pages each (the last may hold fewer).
  * Per partition: m = max logit, p = exp(t - m), l = sum p; FP4 partitions
  * quantize p' = c p per 16-token block (scale_mode_p, tau) and accumulate
  * P_hat = s e2m1 / c times v_hat. Partitions are merged by log-sum-exp.

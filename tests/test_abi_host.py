@@ -100,17 +100,17 @@ def test_sizes_and_plan():
     assert bd.cache_bytes(nv, 10, 8) == (10 * 8 * 8192, 10 * 8 * 1024, 10 * 8 * 8192, 10 * 8 * 1024)
     assert bd.cache_bytes(mx, 3, 2) == (3 * 2 * 8192, 3 * 2 * 512, 3 * 2 * 8192, 3 * 2 * 512)
     # explicit plan
-    assert bd.decode_plan(1, 8, 131072, 8) == (8, 128)
+    assert bd.decode_plan(1, 8, 131072, 2) == (2, 512)
     assert bd.decode_plan(1, 1, 2048, 4) == (4, 4)
     assert bd.decode_plan(1, 1, 100, 4) == (4, 0)
     ppp, parts = bd.decode_plan(1, 8, 131072, 0)
-    assert 1 <= ppp <= 16 and parts == -(-1024 // ppp)
-    ws = bd.decode_workspace_size(1, 32, 8, 131072, 8)
-    assert ws == 65536 + 8 * 129 * 520 * 4
+    assert ppp == 4 and parts == -(-1024 // ppp)
+    ws = bd.decode_workspace_size(1, 32, 8, 131072, 4)
+    assert ws == 65536 + 8 * 257 * 520 * 4
     with pytest.raises(bd.Bdfp4Error) as ei:
         bd.decode_workspace_size(1, 24, 8, 1000, 0)
     assert ei.value.status == bd.E_UNSUPPORTED
-    for args in [(0, 8, 1000, 0), (1, 8, 0, 0), (1, 8, 1000, 17), (1, 8, 1000, -1)]:
+    for args in [(0, 8, 1000, 0), (1, 8, 0, 0), (1, 8, 1000, 5), (1, 8, 1000, -1)]:
         with pytest.raises(bd.Bdfp4Error) as ei:
             bd.decode_plan(*args)
         assert ei.value.status == bd.E_INVALID

@@ -34,7 +34,7 @@ def _run(r, wl, ppp, what):
     return got, ref, host
 
 
-@pytest.mark.parametrize("ppp", [4, 1, 3, 16])
+@pytest.mark.parametrize("ppp", [4, 1, 3, 2])
 def test_tiny_2k(ppp):
     _run(NV, synth.tiny(0), ppp, f"tiny ppp={ppp}")
 
@@ -61,7 +61,7 @@ def test_ragged_batch(sink):
 
 def test_ragged_batch_mxfp4():
     wl = synth.decode_workload("r", 5, [129, 1000, 4096 + 77], 12, 3, "qwen", extra_pages=2)
-    _run(MX, wl, 5, "ragged mxfp4")
+    _run(MX, wl, 3, "ragged mxfp4")
 
 
 def test_qwen_32k_layer():
