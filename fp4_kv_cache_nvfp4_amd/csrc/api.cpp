@@ -139,9 +139,12 @@ bdfp4_status plan(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_i
   return BDFP4_OK;
 }
 
-size_t workspace_bytes(int32_t batch, int32_t hkv, int32_t parts) {
-  return bdfp4::kCounterBytes +
-         (size_t)batch * hkv * (size_t)(parts + 1) * bdfp4::kPartialFloats * sizeof(float);
+// Partitions the workspace is sized for: those of the longest sequence
+// counting its partial last page (the BF16 decode reads it as a page).
+int32_t workspace_parts(int32_t max_seq_len, int32_t ppp) { return ((max_seq_len + 127) / 128 + ppp - 1) / ppp; }
+
+size_t workspace_bytes(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp) {
+  return bdfp4::workspace_bytes_for(batch, hkv, workspace_parts(max_seq_len, ppp));
 }
 
 bdfp4_status hip_status(hipError_t e, const char* what) {
@@ -261,9 +264,7 @@ bdfp4_status bdfp4_decode_workspace_size(int32_t batch, int32_t num_q_heads, int
   int32_t ppp, parts;
   bdfp4_status s = plan(batch, num_kv_heads, max_seq_len, pages_per_partition, &ppp, &parts);
   if (s != BDFP4_OK) return s;
-  // the BF16 decode also reads the partial last page: size for ceil(L/128) pages
-  const int32_t all_parts = ((max_seq_len + 127) / 128 + ppp - 1) / ppp;
-  *bytes = workspace_bytes(batch, num_kv_heads, all_parts > parts ? all_parts : parts);
+  *bytes = workspace_bytes(batch, num_kv_heads, max_seq_len, ppp);
   return ok();
 }
 
@@ -280,10 +281,17 @@ static bdfp4_status check_decode_common(const void* q, int32_t batch, int32_t hq
   if (!aligned16(q) || !aligned16(out)) return fail(BDFP4_E_INVALID, "q and out must be 16-byte aligned");
   if (max_pages_per_seq < 1) return fail(BDFP4_E_INVALID, "max_pages_per_seq must be positive");
   if (!isfinite(softmax_scale)) return fail(BDFP4_E_INVALID, "softmax_scale must be finite");
-  const size_t need = workspace_bytes(batch, hkv, *parts);
+  if (workspace != nullptr && !aligned16(workspace)) return fail(BDFP4_E_INVALID, "workspace must be 16-byte aligned");
+  return BDFP4_OK;
+}
+
+// Checked last, after every input check: the workspace holds the tickets and
+// the partials of the plan.
+static bdfp4_status check_workspace(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp,
+                                    const void* workspace, size_t workspace_bytes_in) {
+  const size_t need = workspace_bytes(batch, hkv, max_seq_len, ppp);
   if (workspace == nullptr || workspace_bytes_in < need)
     return fail(BDFP4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes_in);
-  if (!aligned16(workspace)) return fail(BDFP4_E_INVALID, "workspace must be 16-byte aligned");
   return BDFP4_OK;
 }
 
@@ -316,6 +324,8 @@ bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* ca
   if (max_seq_len / 128 > max_pages_per_seq)
     return fail(BDFP4_E_INVALID, "max_seq_len needs %d pages but block tables hold %d", max_seq_len / 128,
                 max_pages_per_seq);
+  if ((s = check_workspace(batch, cache->num_kv_heads, max_seq_len, ppp, workspace, workspace_bytes_in)) != BDFP4_OK)
+    return s;
   bdfp4::DecodeLaunch L;
   L.sink = r->sink_tokens;
   L.rotation = r->rotation;
@@ -347,7 +357,10 @@ bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* ca
   L.softmax_scale = softmax_scale;
   L.ppp = ppp;
   L.max_parts = parts;
-  L.workspace = workspace;
+  L.counters = static_cast<uint32_t*>(workspace);
+  L.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + bdfp4::kTicketBytes);
+  L.counter_stride = bdfp4::kTicketStride;
+  L.slot_stride = bdfp4::workspace_slot_stride(workspace_parts(max_seq_len, ppp));
   L.out = out;
   return hip_status(bdfp4::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
@@ -369,6 +382,8 @@ bdfp4_status bdfp4_bf16_decode_attention(const void* q_bf16, int32_t batch, int3
   if ((max_seq_len + 127) / 128 > max_pages_per_seq)
     return fail(BDFP4_E_INVALID, "max_seq_len needs %d pages but block tables hold %d",
                 (max_seq_len + 127) / 128, max_pages_per_seq);
+  if ((s = check_workspace(batch, num_kv_heads, max_seq_len, ppp, workspace, workspace_bytes_in)) != BDFP4_OK)
+    return s;
   bdfp4::Bf16DecodeLaunch L;
   L.q = static_cast<const uint16_t*>(q_bf16);
   L.batch = batch;
@@ -384,11 +399,12 @@ bdfp4_status bdfp4_bf16_decode_attention(const void* q_bf16, int32_t batch, int3
   L.softmax_scale = softmax_scale;
   // every page of a BF16 cache is read, the partial last one included
   L.ppp = ppp;
-  L.max_parts = ((max_seq_len + 127) / 128 + ppp - 1) / ppp;
-  L.workspace = workspace;
+  L.max_parts = workspace_parts(max_seq_len, ppp);
+  L.counters = static_cast<uint32_t*>(workspace);
+  L.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + bdfp4::kTicketBytes);
+  L.counter_stride = bdfp4::kTicketStride;
+  L.slot_stride = bdfp4::workspace_slot_stride(L.max_parts);
   L.out = out;
-  if (workspace_bytes_in < workspace_bytes(batch, num_kv_heads, L.max_parts))
-    return fail(BDFP4_E_WORKSPACE, "workspace too small for the BF16 decode");
   return hip_status(bdfp4::launch_bf16_decode(L, static_cast<hipStream_t>(stream)), "bf16 decode launch");
 }
 

@@ -39,25 +39,24 @@ struct SmemB {
 
 struct Bf16Args {
   Bf16DecodeLaunch L;
-  uint32_t* counters;
-  float* partials;
 };
 
 __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
   __shared__ __align__(16) SmemB sm;
   const Bf16DecodeLaunch& P = A.L;
-  const int nps = P.max_parts + 1;
+  const int nps = P.max_parts;                  // workgroups per (sequence, KV head)
   const int s = blockIdx.x % nps;
   const int bh = blockIdx.x / nps;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   MergeCtx C;
-  C.counters = A.counters;
-  C.partials = A.partials;
+  C.counters = P.counters;
+  C.partials = P.partials;
   C.out = P.out;
   C.hq = P.hq;
   C.hkv = P.hkv;
-  C.max_parts = P.max_parts;
+  C.counter_stride = P.counter_stride;
+  C.slot_stride = P.slot_stride;
 
   const int L = P.seq_lens[b];
   const int npages = L > 0 ? (L + kPage - 1) / kPage : 0;
@@ -196,7 +195,11 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
     ll[g] = poisoned ? 1.0f : (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
   }
   write_partial(partial_writer(C, bh, s), poisoned ? nan : o0, poisoned ? nan : o1, mm, ll);
-  publish_and_merge(C, &sm.ticket, &sm.red[0][0], sm.logit, kMaxTokB * 4, b, h, nparts);
+  uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
+  if (take_ticket(ticket, 1, &sm.ticket) + 1 == nparts) {
+    merge_slots(C, &sm.red[0][0], sm.logit, kMaxTokB * 4, b, h, 0, nparts, -1);
+    reset_ticket(ticket);
+  }
 }
 
 }  // namespace
@@ -204,10 +207,8 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
 hipError_t launch_bf16_decode(const Bf16DecodeLaunch& L, hipStream_t stream) {
   Bf16Args A;
   A.L = L;
-  A.counters = static_cast<uint32_t*>(L.workspace);
-  A.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(L.workspace) + kCounterBytes);
   // partition slots 0 .. max_parts-1 (there is no separate BF16 partition)
-  const dim3 grid((unsigned)(L.batch * L.hkv * (L.max_parts + 1))), block(256u);
+  const dim3 grid((unsigned)(L.batch * L.hkv * L.max_parts)), block(256u);
   hipLaunchKernelGGL(bf16_decode_kernel, grid, block, 0, stream, A);
   return hipGetLastError();
 }

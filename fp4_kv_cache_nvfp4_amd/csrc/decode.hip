@@ -76,20 +76,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMaxPpw = 4;                 // pages per partition = per wave
 constexpr int kWaveTok = kMaxPpw * kPage;  // tokens of one partition
 
-// Workgroups per (sequence, KV head) for a number of FP4 partitions: four
-// partitions (one per wave) per workgroup, and at least one workgroup, which
-// also carries the BF16 partition.
-__host__ __device__ __forceinline__ int wgs_for_parts(int parts) { return (parts + 3) / 4; }
-__host__ __device__ __forceinline__ int wgs_per_seq(int max_parts) {
-  const int g = wgs_for_parts(max_parts);
-  return g > 0 ? g : 1;
-}
 constexpr float kNegInf = -__builtin_inff();
 
 struct DecArgs {
   DecodeLaunch L;
-  uint32_t* counters;
-  float* partials;
 };
 
 // ------------------------------------------------------------ converts
@@ -168,12 +158,13 @@ struct Smem {
 
 __device__ __forceinline__ MergeCtx merge_ctx(const DecArgs& A) {
   MergeCtx C;
-  C.counters = A.counters;
-  C.partials = A.partials;
+  C.counters = A.L.counters;
+  C.partials = A.L.partials;
   C.out = A.L.out;
   C.hq = A.L.hq;
   C.hkv = A.L.hkv;
-  C.max_parts = A.L.max_parts;
+  C.counter_stride = A.L.counter_stride;
+  C.slot_stride = A.L.slot_stride;
   return C;
 }
 
@@ -185,7 +176,7 @@ __device__ __forceinline__ MergeCtx merge_ctx(const DecArgs& A) {
 // workgroup's loads (K row of token t for thread t, the query, and the V rows
 // of its token group for thread (token group, channel quad)) are issued
 // before the first barrier, so the partition costs one memory round trip.
-__device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full) {
+__device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full, int slot) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x;
   const int S = P.sink;
@@ -306,7 +297,7 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
     mm[g] = nb > 0 ? m[g] : kNegInf;
     ll[g] = (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
   }
-  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, 0), o0, o1, mm, ll);
+  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, slot), o0, o1, mm, ll);
 }
 
 // ------------------------------------------------------------ query prologue
@@ -468,10 +459,10 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 // each wave streams its own pages_per_partition consecutive pages through
 // pass 1, its own maximum and pass 2 with no workgroup barrier in between;
 // the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
-// workgroup's partial (slot sp + 1). With with_bf16 the workgroup also
-// computes the BF16 partition (slot 0) while its first K pages are loading.
+// workgroup's partial (slot sp). With bf16_slot >= 0 the workgroup also
+// computes the BF16 partition (into that slot) while its first K pages load.
 template <bool kMx, int kTerms, bool kUnder>
-__device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, int n_full, bool with_bf16) {
+__device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, int n_full, int bf16_slot) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p0 = (4 * sp + wave) * P.ppp;                       // first page of this wave's partition
@@ -496,9 +487,18 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
     uint32_t* pz = &sm.pst[0][0][0];       // rows 4 .. 15 of every wave's staging tile
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
-  KPage kA;
-  if (npg > 0) load_k<kMx>(kA, P, blk_of(0), lane);
-  if (with_bf16) bf16_partition(A, sm, b, h, L, n_full);
+  // The wave reads a stream of eight slots, K pages 0..3 then V pages 0..3
+  // (slots of pages >= npg are empty), keeping the next two slots in flight
+  // while one is used. K page i lands in kb[i % 3], V page j in vb[j % 3];
+  // every load has a fixed destination, so at most four buffers are live.
+  // The loads are unconditional (a slot past npg reads physical page 0,
+  // which always exists, and is never used) so the compiler can count the
+  // loads in flight exactly and wait only for the slot about to be used.
+  KPage kb0, kb1, kb2;
+  VPage vb0, vb1, vb2;
+  load_k<kMx>(kb0, P, blk_of(0), lane);
+  if (bf16_slot >= 0) bf16_partition(A, sm, b, h, L, n_full, bf16_slot);
+  load_k<kMx>(kb1, P, blk_of(1), lane);
   query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
 
@@ -533,8 +533,7 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
   // whole 16-token tiles of the sequence's first page; those tiles get -inf.
   const int sink_tiles = p0 == 0 ? P.sink / 16 : 0;
   float ma = kNegInf, mb = kNegInf;
-  auto k_page = [&](const KPage& cur, KPage& nxt, int pi) {
-    if (pi + 1 < npg) load_k<kMx>(nxt, P, blk_of(pi + 1), lane);
+  auto k_page = [&](const KPage& cur, int pi) {
     const int skip = pi == 0 ? sink_tiles : 0;                  // uniform
     float pa = kNegInf, pb = kNegInf;
 #pragma unroll
@@ -583,16 +582,15 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
     ma = __builtin_fmaxf(ma, pa);
     mb = __builtin_fmaxf(mb, pb);
   };
-  {
-    KPage kB;
-    for (int pi = 0; pi < npg; pi += 2) {
-      k_page(kA, kB, pi);
-      if (pi + 1 >= npg) break;
-      k_page(kB, kA, pi + 1);
-    }
-  }
-  VPage vA;
-  if (npg > 0) load_v<kMx>(vA, P, blk_of(0), lane);
+  static_assert(kMaxPpw == 4, "the stream below is unrolled for up to 4 pages");
+  load_k<kMx>(kb2, P, blk_of(2), lane);
+  if (npg > 0) k_page(kb0, 0);
+  load_k<kMx>(kb0, P, blk_of(3), lane);
+  if (npg > 1) k_page(kb1, 1);
+  load_v<kMx>(vb0, P, blk_of(0), lane);
+  if (npg > 2) k_page(kb2, 2);
+  load_v<kMx>(vb1, P, blk_of(1), lane);
+  if (npg > 3) k_page(kb0, 3);
   // the partition maximum of each head (rows of 16 lanes hold heads 2 kg, 2 kg + 1)
   ma = max16(ma);
   mb = max16(mb);
@@ -612,8 +610,7 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
   f32x4_t acco[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acco[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  auto v_page = [&](const VPage& vcur, VPage& vnxt, int pi) {
-    if (pi + 1 < npg) load_v<kMx>(vnxt, P, blk_of(pi + 1), lane);
+  auto v_page = [&](const VPage& vcur, int pi) {
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
       // p' = c exp(sigma (t - m)) of tokens 2 pj, 2 pj + 1 of the chunk, head ph
@@ -643,23 +640,25 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
       const uint2 vs = vcur.sc[ch];
       const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if (kMx) {
-        // element pairs per byte: vw[ii] = token 8 kg + ii, channels 8n .. 8n+7
-        uint32_t x[8][4];
+        // element pairs per byte: vw[ii] = token 8 kg + ii, channels 8n .. 8n+7;
+        // byte bb of every token gives channels 8n + 2bb, +1 (MFMAs j = 2bb, 2bb+1)
+        float svv[8];
 #pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const uint32_t sb = (ii < 4 ? (vs.x >> (8 * ii)) : (vs.y >> (8 * (ii - 4)))) & 0xFFu;
-          const float svv = __uint_as_float(sb << 23);
+        for (int ii = 0; ii < 8; ++ii)
+          svv[ii] = __uint_as_float(((ii < 4 ? (vs.x >> (8 * ii)) : (vs.y >> (8 * (ii - 4)))) & 0xFFu) << 23);
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb) x[ii][bb] = cvt_bf16_pair(vw[ii], svv, bb);
-        }
+        for (int bb = 0; bb < 4; ++bb) {
+          uint32_t x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int bb = j >> 1;
-          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t bv;
+          for (int ii = 0; ii < 8; ++ii) x[ii] = cvt_bf16_pair(vw[ii], svv[ii], bb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bv[r] = __builtin_amdgcn_perm(x[2 * r + 1][bb], x[2 * r][bb], sel);
-          acco[j] = mfma<kMx>(ap, bv, acco[j]);
+          for (int jj = 0; jj < 2; ++jj) {
+            const uint32_t sel = jj ? 0x07060302u : 0x05040100u;
+            u32x4_t bv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[r] = __builtin_amdgcn_perm(x[2 * r + 1], x[2 * r], sel);
+            acco[2 * bb + jj] = mfma<kMx>(ap, bv, acco[2 * bb + jj]);
+          }
         }
       } else {
         // token pairs per byte: byte r of vw[j] = tokens 8 kg + 2r, +1 at channel 8n + j
@@ -675,14 +674,12 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
       }
     }
   };
-  {
-    VPage vB;
-    for (int pi = 0; pi < npg; pi += 2) {
-      v_page(vA, vB, pi);
-      if (pi + 1 >= npg) break;
-      v_page(vB, vA, pi + 1);
-    }
-  }
+  load_v<kMx>(vb2, P, blk_of(2), lane);
+  if (npg > 0) v_page(vb0, 0);
+  load_v<kMx>(vb0, P, blk_of(3), lane);
+  if (npg > 1) v_page(vb1, 1);
+  if (npg > 2) v_page(vb2, 2);
+  if (npg > 3) v_page(vb0, 3);
   // ---- this wave's (m, l, o) to LDS: o over its own logit rows (read above
   // by this wave only; its LDS instructions complete in order)
   lacc = sum16(lacc);                // rows of 16 lanes = heads
@@ -741,7 +738,7 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
     mm[g] = poisoned ? 0.0f : mm[g];
     ll[g] = poisoned ? 1.0f : ll[g];
   }
-  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, sp + 1), poisoned ? nan : o0 * invc,
+  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, sp), poisoned ? nan : o0 * invc,
                 poisoned ? nan : o1 * invc, mm, ll);
 }
 
@@ -749,7 +746,7 @@ template <bool kMx, int kTerms, bool kUnder>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
-  const int G = wgs_per_seq(P.max_parts);
+  const int G = fp4_wgs(P.max_parts);
   const int sp = blockIdx.x % G;
   const int bh = blockIdx.x / G;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
@@ -760,26 +757,40 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     return;
   }
   const int nparts = n_full > 0 ? (n_full + P.ppp - 1) / P.ppp : 0;
-  const int nwg = wgs_for_parts(nparts);                        // FP4 workgroups of this sequence
+  const int nwg = nparts > 0 ? fp4_wgs(nparts) : 0;            // FP4 workgroups of this sequence
+  const int ng = fp4_groups(nwg);                               // their merge groups
   if (sp >= nwg && sp != 0) return;
-  int inc;
+  const MergeCtx C = merge_ctx(A);
+  uint32_t* tickets = C.counters + (size_t)bh * C.counter_stride;   // head ticket, then group tickets
+  const int bf16_slot = nwg + ng;
+  int inc_head = 0;
   if (sp < nwg) {
-    fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L, n_full, sp == 0);
-    inc = sp == 0 ? 2 : 1;
+    fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L, n_full, sp == 0 ? bf16_slot : -1);
+    if (sp == 0) ++inc_head;                                    // the BF16 partial
+    // group level: the last workgroup of the group merges its partials
+    const int gw = fp4_group_size(nwg);
+    const int grp = sp / gw;
+    const int gsz = min(gw, nwg - grp * gw);
+    if (take_ticket(&tickets[1 + grp], 1, &sm.ticket) + 1 == gsz) {
+      merge_slots(C, &sm.red[0][0], &sm.logit[0][0], 4 * 4 * kWaveTok, b, h, grp * gw, gsz, nwg + grp);
+      reset_ticket(&tickets[1 + grp]);
+      ++inc_head;
+    }
   } else {
-    bf16_partition(A, sm, b, h, L, n_full);                     // no full page: the BF16 tokens only
-    inc = 1;
+    bf16_partition(A, sm, b, h, L, n_full, bf16_slot);          // no full page: the BF16 tokens only
+    inc_head = 1;
   }
-  publish_and_merge(merge_ctx(A), &sm.ticket, &sm.red[0][0], &sm.logit[0][0], 4 * 4 * kWaveTok, b, h, nwg + 1,
-                    inc);
+  // head level: group results and the BF16 partial, slots nwg .. nwg + ng
+  if (inc_head > 0 && take_ticket(&tickets[0], inc_head, &sm.ticket) + inc_head == ng + 1) {
+    merge_slots(C, &sm.red[0][0], &sm.logit[0][0], 4 * 4 * kWaveTok, b, h, nwg, ng + 1, -1);
+    reset_ticket(&tickets[0]);
+  }
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   DecArgs A;
   A.L = L;
-  A.counters = static_cast<uint32_t*>(L.workspace);
-  A.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(L.workspace) + kCounterBytes);
-  const dim3 grid((unsigned)(L.batch * L.hkv * wgs_per_seq(L.max_parts))), block(256u);
+  const dim3 grid((unsigned)(L.batch * L.hkv * fp4_wgs(L.max_parts))), block(256u);
   const bool under = L.p_mode == 4;
 #define BDFP4_LAUNCH(MX, T, U) hipLaunchKernelGGL((decode_kernel<MX, T, U>), grid, block, 0, stream, A)
   if (L.mx) {

@@ -51,7 +51,9 @@ struct DecodeLaunch {
   const float* key_shift;
   float softmax_scale;
   int32_t ppp, max_parts;
-  void* workspace;
+  uint32_t* counters;     // workspace tickets
+  float* partials;        // workspace partials
+  int32_t counter_stride, slot_stride;
   float* out;
 };
 
@@ -69,17 +71,49 @@ struct Bf16DecodeLaunch {
   int32_t max_seq_len;
   float softmax_scale;
   int32_t ppp, max_parts;
-  void* workspace;
+  uint32_t* counters;
+  float* partials;
+  int32_t counter_stride, slot_stride;
   float* out;
 };
 
 hipError_t launch_bf16_decode(const Bf16DecodeLaunch& L, hipStream_t stream);
 
-// Workspace layout shared by both decodes: a fixed counter region followed
-// by the per-partition partials.
-constexpr size_t kCounterBytes = 65536;          // 16384 (sequence, KV head) tickets
-constexpr int kMaxSeqHeads = 16384;
 constexpr int kGroup = 4;                         // query heads per KV head
 constexpr int kPartialFloats = kGroup * 130;      // o[4][128], m[4], l[4] (+pad)
+constexpr int kMaxSeqHeads = 16384;               // (sequence, KV head) pairs per call
+constexpr int kMaxGroups = 32;                    // merge groups per (sequence, KV head)
+constexpr int kTicketStride = 1 + kMaxGroups;     // head ticket, then one per group
+
+// FP4 workgroups of a sequence with `parts` FP4 partitions (four per
+// workgroup; at least one, which also carries the BF16 partition), the
+// number of workgroups merged per group (8, more for very long sequences so
+// that there are at most kMaxGroups groups) and the number of groups.
+__host__ __device__ inline int fp4_wgs(int parts) {
+  const int g = (parts + 3) / 4;
+  return g > 0 ? g : 1;
+}
+__host__ __device__ inline int fp4_group_size(int wgs) {
+  const int g = (wgs + kMaxGroups - 1) / kMaxGroups;
+  return g > 8 ? g : 8;
+}
+__host__ __device__ inline int fp4_groups(int wgs) { return (wgs + fp4_group_size(wgs) - 1) / fp4_group_size(wgs); }
+
+// Workspace shared by both decodes. A fixed ticket region,
+// [kMaxSeqHeads][kTicketStride] uint32 (the same for every call, so one
+// zero-filled workspace serves calls of any shape), then partials
+// [batch * hkv][slot_stride][kPartialFloats] float32, slot_stride = parts + 2
+// for parts = partitions of the longest sequence counting its partial last
+// page (ceil(ceil(max_seq_len / 128) / pages_per_partition)). An FP4 decode
+// of a sequence with w workgroups and g groups uses slots 0 .. w-1
+// (workgroups), w .. w+g-1 (group merges) and w+g (the BF16 partition), at
+// most parts + 2; the BF16 decode uses one slot per partition.
+constexpr size_t kTicketBytes = (size_t)kMaxSeqHeads * kTicketStride * sizeof(uint32_t);
+
+inline int32_t workspace_slot_stride(int32_t parts) { return parts + 2; }
+
+inline size_t workspace_bytes_for(int32_t batch, int32_t hkv, int32_t parts) {
+  return kTicketBytes + (size_t)batch * hkv * workspace_slot_stride(parts) * kPartialFloats * sizeof(float);
+}
 
 }  // namespace bdfp4

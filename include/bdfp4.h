@@ -162,11 +162,15 @@ bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads,
                                int32_t* max_partitions_out);
 
 /* Workspace bytes for bdfp4_decode_attention / bdfp4_bf16_decode_attention
- * with these sizes (host output). The workspace must be zero-filled once
- * after it is allocated; every call leaves its counter words zero again, so a
- * buffer can be reused (and captured in a graph) without clearing. After a
- * call that did not complete (process killed, device error) zero it again.
- * Calls that share one workspace must not overlap in time. */
+ * with these sizes (host output): a fixed ticket region of
+ * 16384 * 33 * 4 bytes (the same for every call shape), then
+ * batch * num_kv_heads * (P + 2) partial slots of 2080 bytes, where
+ * P = ceil(ceil(max_seq_len / 128) / pages_per_partition). The workspace must
+ * be zero-filled once after it is allocated; every call leaves its ticket
+ * words zero again, so a buffer can be reused by calls of any shape (and
+ * captured in a graph) without clearing. After a call that did not complete
+ * (process killed, device error) zero it again. Calls that share one
+ * workspace must not overlap in time. */
 bdfp4_status bdfp4_decode_workspace_size(int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads,
                                          int32_t max_seq_len,
