@@ -194,10 +194,18 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
     mm[g] = poisoned ? 0.0f : m[g];
     ll[g] = poisoned ? 1.0f : (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
   }
-  write_partial(partial_writer(C, bh, s), poisoned ? nan : o0, poisoned ? nan : o1, mm, ll);
+  Partial mine;
+  mine.o0 = poisoned ? nan : o0;
+  mine.o1 = poisoned ? nan : o1;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    mine.m[g] = mm[g];
+    mine.l[g] = ll[g];
+  }
+  write_partial(partial_writer(C, bh, s), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.ticket) + 1 == nparts) {
-    merge_slots(C, &sm.red[0][0], sm.logit, kMaxTokB * 4, b, h, 0, nparts, -1);
+    merge_out(C, b, h, nparts, s, true, mine);
     reset_ticket(ticket);
   }
 }

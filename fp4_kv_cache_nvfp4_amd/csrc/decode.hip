@@ -10,41 +10,40 @@
 // dispatches to the paged attention kernel, which uses block scaling and scale
 // modes; the tail control plane keeps the partial page in BF16.
 //
-// Grid: one workgroup (256 threads, 4 waves) per (sequence, KV head, FP4
-// partition); each FP4 partition owns pages_per_partition pages. The BF16
-// partition (sink + tail tokens, exact float32 attention of the raw query)
-// is computed by the first workgroup of each (sequence, KV head) after its
-// FP4 pages, so the grid has no extra short workgroups that would spill
-// the 2-per-CU residency into a second round. A partition computes, for the
-// 4 query heads of its KV head, m = max logit, l = sum exp(t - m) and
-// o = sum P_hat v_hat, writes them to the workspace and takes a ticket; the
-// last workgroup of the (sequence, KV head) merges all partials and resets
-// the ticket.
+// Grid: one workgroup (256 threads, 4 waves) per 4 FP4 partitions of a
+// (sequence, KV head); each wave owns one partition of pages_per_partition
+// (1..4) consecutive full pages. The BF16 partition (sink + tail tokens,
+// exact float32 attention of the raw query) of (sequence, KV head) j is
+// computed by workgroup j, among the first dispatched, while its own first
+// K page loads. Every partition computes, for the 4 query heads of its KV
+// head, m = max logit, l = sum exp(t - m) and o = sum P_hat v_hat; a
+// workgroup merges its four waves in LDS, stores one partial and takes a
+// ticket; the last of a (sequence, KV head) merges all of them (merge.hpp).
 //
-// FP4 partition, per workgroup:
-//  * the page ids are staged in LDS and each wave starts loading its first K
-//    page before the query prologue;
+// FP4 partition, per wave:
+//  * page ids: lane i reads page i of the partition's block-table run; the
+//    wave then issues its first two K page loads;
 //  * prologue: wave g rotates (128-point Hadamard, float32) and quantizes
 //    query row g as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32), two
 //    elements per lane; the dequantized terms are exact in 16 bits and become
 //    the A operands of v_mfma_f32_16x16x32_{f16,bf16}: row 2g + t holds term
-//    t of head g, rows 8..15 are zero. q . mu (raw float32 query, key means)
-//    seeds the term-1 rows of the accumulator.
-//  * pass 1 (QK^T): each wave streams whole pages, the next page in flight
-//    while the current one is used; per 16-token tile a lane holds 16 code
-//    bytes (one coalesced 1 KiB run per wave) and the page's scales come in
-//    one 16-byte load per lane. Four MFMAs give both terms of all four heads;
-//    their sum, the raw logit q . mu + q_hat . k_hat, goes to LDS
-//    [head][token]. Sink tokens fill whole tiles of the first page and get
-//    -inf.
-//  * partition max over the 4 waves.
+//    t of head g and rows 8..15 repeat rows 0..7. q . mu (raw float32 query,
+//    key means) seeds the term-1 rows of the accumulator.
+//  * pass 1 (QK^T): the wave streams its K pages with two pages in flight;
+//    per 16-token tile a lane holds 16 code bytes (one coalesced 1 KiB run
+//    per wave) and the page's scales come in one 16-byte load per lane. Four
+//    MFMAs give both terms of all four heads; their sum, the raw logit
+//    q . mu + q_hat . k_hat, goes to the wave's LDS rows [head][token]. Sink
+//    tokens fill whole tiles of the first page and get -inf.
+//  * the partition maximum of each head (DPP within 16 lanes, then lanes).
 //  * pass 2 (softmax, P quantization, PV): per 32-token chunk the 4 x 32
 //    values p' = c exp(sigma (t - m)) are formed two per lane; l accumulates
 //    them; p' is quantized per aligned 16-token block (amax2_or_amax6 with
 //    tau, or amax6) and s * e2m1 (exact in 16 bits) is staged in LDS as the A
 //    operand. V codes come as B operands of 8 MFMAs (one per output channel
 //    slab).
-//  * the 4 waves' o and l are summed in LDS; both are divided by c.
+//  * the 4 waves' (m, l, o) are merged by log-sum-exp in LDS; o and l are
+//    divided by c.
 //
 // E2M1 codes of p' are found without comparing against the grid midpoints:
 // with the block scale s = 2^E m (E4M3), the exact float32 quotient p' / m
@@ -151,7 +150,7 @@ struct Smem {
   float lsum[4][4];                         // per wave, per head: sum of c p
   float rcp[8];                             // RN(1 / (1 + k/8)), k = 0..7
   int bad[4];                               // per wave: its block table names an invalid page
-  int ticket;
+  int tick;
 };
 
 // ------------------------------------------------------------ partials
@@ -176,7 +175,7 @@ __device__ __forceinline__ MergeCtx merge_ctx(const DecArgs& A) {
 // workgroup's loads (K row of token t for thread t, the query, and the V rows
 // of its token group for thread (token group, channel quad)) are issued
 // before the first barrier, so the partition costs one memory round trip.
-__device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full, int slot) {
+__device__ Partial bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x;
   const int S = P.sink;
@@ -291,13 +290,16 @@ __device__ void bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, 
     o0 += so[(g8 * 4 + head) * kD + d];
     o1 += so[(g8 * 4 + head) * kD + d + 1];
   }
-  float mm[4], ll[4];
+  Partial r;
+  r.o0 = o0;
+  r.o1 = o1;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    mm[g] = nb > 0 ? m[g] : kNegInf;
-    ll[g] = (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
+    r.m[g] = nb > 0 ? m[g] : kNegInf;
+    r.l[g] = (sm.lsum[0][g] + sm.lsum[1][g]) + (sm.lsum[2][g] + sm.lsum[3][g]);
   }
-  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, slot), o0, o1, mm, ll);
+  __syncthreads();                                   // LDS is reused by the caller
+  return r;
 }
 
 // ------------------------------------------------------------ query prologue
@@ -459,10 +461,9 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 // each wave streams its own pages_per_partition consecutive pages through
 // pass 1, its own maximum and pass 2 with no workgroup barrier in between;
 // the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
-// workgroup's partial (slot sp). With bf16_slot >= 0 the workgroup also
-// computes the BF16 partition (into that slot) while its first K pages load.
+// workgroup's partial (returned; the caller stores it).
 template <bool kMx, int kTerms, bool kUnder>
-__device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, int n_full, int bf16_slot) {
+__device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int n_full) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p0 = (4 * sp + wave) * P.ppp;                       // first page of this wave's partition
@@ -497,36 +498,37 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
   KPage kb0, kb1, kb2;
   VPage vb0, vb1, vb2;
   load_k<kMx>(kb0, P, blk_of(0), lane);
-  if (bf16_slot >= 0) bf16_partition(A, sm, b, h, L, n_full, bf16_slot);
   load_k<kMx>(kb1, P, blk_of(1), lane);
   query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
 
   // A operands: lane (row = lane & 15, k-group kg = lane >> 4); row 2 g + t
-  // holds query term t of head g (rows 8 .. 15 zero); MFMA c covers channels
+  // holds query term t of head g, and rows 8 .. 15 repeat rows 0 .. 7, so
+  // lanes 32 .. 63 of the result hold exactly what lanes 0 .. 31 hold and
+  // every lane can store its logits without a branch; MFMA c covers channels
   // 32 kg + 8 c + [0, 8)
   const int row = lane & 15, kg = lane >> 4;
+  const int qr = row & 7;
   u32x4_t aq[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row < 2 * kGroup && ((row & 1) < kTerms)) {
-      const uint4 t = *reinterpret_cast<const uint4*>(&sm.qhat[row & 1][row >> 1][32 * kg + 8 * c]);
+    if ((qr & 1) < kTerms) {
+      const uint4 t = *reinterpret_cast<const uint4*>(&sm.qhat[qr & 1][qr >> 1][32 * kg + 8 * c]);
       v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     }
     aq[c] = v;
   }
-  // D lane l holds rows 4 (l >> 4) + i: lanes 0..15 heads 0, 1 and lanes
-  // 16..31 heads 2, 3 (term 1 in i = 0, 2; term 2 in i = 1, 3); q . mu
-  // enters through the term-1 rows
+  // D lane l holds rows 4 (l >> 4) + i: lanes 0..15 (and 32..47) heads 0, 1,
+  // lanes 16..31 (and 48..63) heads 2, 3; term 1 in i = 0, 2, term 2 in
+  // i = 1, 3. q . mu enters through the term-1 rows.
+  const int hp = kg & 1;                                        // head pair of this lane's result
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
-  if (kg < 2) {
-    acc0[0] = sm.qmu[2 * kg];
-    acc0[2] = sm.qmu[2 * kg + 1];
-  }
+  acc0[0] = sm.qmu[2 * hp];
+  acc0[2] = sm.qmu[2 * hp + 1];
   float* lgw = &sm.logit[wave][0];                              // this wave's [head][token]
-  float* lg_a = lgw + (2 * (kg & 1)) * kWaveTok + row;          // head 2 kg (lanes < 32)
-  float* lg_b = lg_a + kWaveTok;                                // head 2 kg + 1
+  float* lg_a = lgw + (2 * hp) * kWaveTok + row;                // head 2 hp
+  float* lg_b = lg_a + kWaveTok;                                // head 2 hp + 1
 
   // ---- pass 1: raw logits q . mu + q_hat . k_hat
   // Sink tokens (global tokens below the sink size, a multiple of 16) fill
@@ -539,13 +541,6 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int local = pi * kPage + t * 16;                    // first token of the tile - 128 p0
-      if (t < skip) {
-        if (lane < 32) {
-          lg_a[local] = kNegInf;
-          lg_b[local] = kNegInf;
-        }
-        continue;
-      }
       u32x4_t bk[4];
       if (kMx) {
         const uint32_t sb = (word_of(cur.sc, t >> 2) >> (8 * (t & 3))) & 0xFFu;
@@ -570,12 +565,11 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
       f32x4_t acc = acc0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma<kMx>(aq[c], bk[c], acc);
-      const float ta = __fadd_rn(acc[0], acc[1]);
-      const float tb = __fadd_rn(acc[2], acc[3]);
-      if (lane < 32) {
-        lg_a[local] = ta;
-        lg_b[local] = tb;
-      }
+      const bool sink = t < skip;                               // uniform: a sink tile of page 0
+      const float ta = sink ? kNegInf : __fadd_rn(acc[0], acc[1]);
+      const float tb = sink ? kNegInf : __fadd_rn(acc[2], acc[3]);
+      lg_a[local] = ta;
+      lg_b[local] = tb;
       pa = __builtin_fmaxf(pa, ta);
       pb = __builtin_fmaxf(pb, tb);
     }
@@ -591,7 +585,7 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
   if (npg > 2) k_page(kb2, 2);
   load_v<kMx>(vb1, P, blk_of(1), lane);
   if (npg > 3) k_page(kb0, 3);
-  // the partition maximum of each head (rows of 16 lanes hold heads 2 kg, 2 kg + 1)
+  // the partition maximum of each head (rows of 16 lanes hold heads 2 hp, 2 hp + 1)
   ma = max16(ma);
   mb = max16(mb);
   const float m4[4] = {readlane_f32(ma, 0), readlane_f32(mb, 0), readlane_f32(ma, 16), readlane_f32(mb, 16)};
@@ -723,67 +717,77 @@ __device__ void fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, 
     ll[g] = l * invc;
   }
   const int head = tid >> 6, d = (tid & 63) * 2;
-  const float* wh = head == 0 ? wgt[0] : (head == 1 ? wgt[1] : (head == 2 ? wgt[2] : wgt[3]));
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
+    const float wh = head == 0 ? wgt[0][w] : (head == 1 ? wgt[1][w] : (head == 2 ? wgt[2][w] : wgt[3][w]));
     const float* ow = &sm.logit[w][head * kD + d];
-    o0 = fmaf(wh[w], ow[0], o0);
-    o1 = fmaf(wh[w], ow[1], o1);
+    o0 = fmaf(wh, ow[0], o0);
+    o1 = fmaf(wh, ow[1], o1);
   }
   const bool poisoned = (sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3]) != 0;
   const float nan = __builtin_nanf("");
+  Partial r;
+  r.o0 = poisoned ? nan : o0 * invc;
+  r.o1 = poisoned ? nan : o1 * invc;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    mm[g] = poisoned ? 0.0f : mm[g];
-    ll[g] = poisoned ? 1.0f : ll[g];
+    r.m[g] = poisoned ? 0.0f : mm[g];
+    r.l[g] = poisoned ? 1.0f : ll[g];
   }
-  write_partial(partial_writer(merge_ctx(A), b * P.hkv + h, sp), poisoned ? nan : o0 * invc,
-                poisoned ? nan : o1 * invc, mm, ll);
+  return r;
 }
 
+// Workgroup j is FP4 workgroup j % G of (sequence, KV head) j / G, G per
+// (sequence, KV head). The BF16 partition of (sequence, KV head) j is
+// computed by workgroup j of the grid after its FP4 partition: the first
+// workgroups are dispatched first and, being the oldest on their CUs, finish
+// first, so the extra work lands where there is slack. Slots: FP4 workgroup
+// sp -> sp, the BF16 partition -> the FP4 workgroup count of its sequence.
+// Each partition takes its (sequence, KV head)'s ticket once its partial is
+// stored; the last one merges all nwg + 1 partials.
 template <bool kMx, int kTerms, bool kUnder>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
+  const MergeCtx C = merge_ctx(A);
+  auto fp4_count = [&](int L) {
+    const int n_full = L / kPage;
+    return n_full > 0 ? fp4_wgs((n_full + P.ppp - 1) / P.ppp) : 0;
+  };
+  auto valid = [&](int L) { return L >= 1 && L <= P.max_seq_len && L / kPage <= P.max_pages_per_seq; };
+  // FP4 role
   const int G = fp4_wgs(P.max_parts);
-  const int sp = blockIdx.x % G;
-  const int bh = blockIdx.x / G;
+  const int bh = (int)blockIdx.x / G, sp = (int)blockIdx.x - bh * G;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
   const int L = P.seq_lens[b];
-  const int n_full = L > 0 ? L / kPage : 0;
-  if (L < 1 || L > P.max_seq_len || n_full > P.max_pages_per_seq) {
-    if (sp == 0) poison_rows(P.out, P.hq, b, h);
-    return;
-  }
-  const int nparts = n_full > 0 ? (n_full + P.ppp - 1) / P.ppp : 0;
-  const int nwg = nparts > 0 ? fp4_wgs(nparts) : 0;            // FP4 workgroups of this sequence
-  const int ng = fp4_groups(nwg);                               // their merge groups
-  if (sp >= nwg && sp != 0) return;
-  const MergeCtx C = merge_ctx(A);
-  uint32_t* tickets = C.counters + (size_t)bh * C.counter_stride;   // head ticket, then group tickets
-  const int bf16_slot = nwg + ng;
-  int inc_head = 0;
+  const int nwg = valid(L) ? fp4_count(L) : 0;
   if (sp < nwg) {
-    fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L, n_full, sp == 0 ? bf16_slot : -1);
-    if (sp == 0) ++inc_head;                                    // the BF16 partial
-    // group level: the last workgroup of the group merges its partials
-    const int gw = fp4_group_size(nwg);
-    const int grp = sp / gw;
-    const int gsz = min(gw, nwg - grp * gw);
-    if (take_ticket(&tickets[1 + grp], 1, &sm.ticket) + 1 == gsz) {
-      merge_slots(C, &sm.red[0][0], &sm.logit[0][0], 4 * 4 * kWaveTok, b, h, grp * gw, gsz, nwg + grp);
-      reset_ticket(&tickets[1 + grp]);
-      ++inc_head;
+    const Partial mine = fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L / kPage);
+    write_partial(partial_writer(C, bh, sp), mine);
+    uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
+    if (take_ticket(ticket, 1, &sm.tick) == nwg) {
+      merge_out(C, b, h, nwg + 1, sp, true, mine);
+      reset_ticket(ticket);
     }
-  } else {
-    bf16_partition(A, sm, b, h, L, n_full, bf16_slot);          // no full page: the BF16 tokens only
-    inc_head = 1;
   }
-  // head level: group results and the BF16 partial, slots nwg .. nwg + ng
-  if (inc_head > 0 && take_ticket(&tickets[0], inc_head, &sm.ticket) + inc_head == ng + 1) {
-    merge_slots(C, &sm.red[0][0], &sm.logit[0][0], 4 * 4 * kWaveTok, b, h, nwg, ng + 1, -1);
-    reset_ticket(&tickets[0]);
+  // BF16 role
+  const int bh2 = (int)blockIdx.x;
+  if (bh2 < P.batch * P.hkv) {
+    const int b2 = bh2 / P.hkv, h2 = bh2 - b2 * P.hkv;
+    const int L2 = P.seq_lens[b2];
+    if (!valid(L2)) {
+      poison_rows(P.out, P.hq, b2, h2);
+      return;
+    }
+    const int nwg2 = fp4_count(L2);
+    const Partial r = bf16_partition(A, sm, b2, h2, L2, L2 / kPage);
+    write_partial(partial_writer(C, bh2, nwg2), r);
+    uint32_t* ticket = C.counters + (size_t)bh2 * C.counter_stride;
+    if (take_ticket(ticket, 1, &sm.tick) == nwg2) {
+      merge_out(C, b2, h2, nwg2 + 1, nwg2, true, r);
+      reset_ticket(ticket);
+    }
   }
 }
 

@@ -82,22 +82,14 @@ hipError_t launch_bf16_decode(const Bf16DecodeLaunch& L, hipStream_t stream);
 constexpr int kGroup = 4;                         // query heads per KV head
 constexpr int kPartialFloats = kGroup * 130;      // o[4][128], m[4], l[4] (+pad)
 constexpr int kMaxSeqHeads = 16384;               // (sequence, KV head) pairs per call
-constexpr int kMaxGroups = 32;                    // merge groups per (sequence, KV head)
-constexpr int kTicketStride = 1 + kMaxGroups;     // head ticket, then one per group
+constexpr int kTicketStride = 1;                  // one completion ticket per (sequence, KV head)
 
 // FP4 workgroups of a sequence with `parts` FP4 partitions (four per
-// workgroup; at least one, which also carries the BF16 partition), the
-// number of workgroups merged per group (8, more for very long sequences so
-// that there are at most kMaxGroups groups) and the number of groups.
+// workgroup, at least one).
 __host__ __device__ inline int fp4_wgs(int parts) {
   const int g = (parts + 3) / 4;
   return g > 0 ? g : 1;
 }
-__host__ __device__ inline int fp4_group_size(int wgs) {
-  const int g = (wgs + kMaxGroups - 1) / kMaxGroups;
-  return g > 8 ? g : 8;
-}
-__host__ __device__ inline int fp4_groups(int wgs) { return (wgs + fp4_group_size(wgs) - 1) / fp4_group_size(wgs); }
 
 // Workspace shared by both decodes. A fixed ticket region,
 // [kMaxSeqHeads][kTicketStride] uint32 (the same for every call, so one
@@ -105,9 +97,9 @@ __host__ __device__ inline int fp4_groups(int wgs) { return (wgs + fp4_group_siz
 // [batch * hkv][slot_stride][kPartialFloats] float32, slot_stride = parts + 2
 // for parts = partitions of the longest sequence counting its partial last
 // page (ceil(ceil(max_seq_len / 128) / pages_per_partition)). An FP4 decode
-// of a sequence with w workgroups and g groups uses slots 0 .. w-1
-// (workgroups), w .. w+g-1 (group merges) and w+g (the BF16 partition), at
-// most parts + 2; the BF16 decode uses one slot per partition.
+// of a sequence with w FP4 workgroups uses slots 0 .. w-1 (one per
+// workgroup) and w (the BF16 partition); the BF16 decode uses one slot per
+// partition.
 constexpr size_t kTicketBytes = (size_t)kMaxSeqHeads * kTicketStride * sizeof(uint32_t);
 
 inline int32_t workspace_slot_stride(int32_t parts) { return parts + 2; }

@@ -7,15 +7,14 @@
 // partials s gives
 //   M = max m_s, L = sum l_s e^(m_s - M), o = sum o_s e^(m_s - M)
 // (partials with m_s = -inf are empty and weigh 0), and the output is o / L.
-// The workspace layout (tickets, slots) is described with workspace_layout.
+// The workspace layout (tickets, slots) is described beside kTicketBytes.
 //
 // Completion is counted with tickets: a workgroup stores its partial, then
-// takes a ticket; the one that draws the last ticket of its set does the
-// merge of that set and puts the ticket back to zero, so a workspace zeroed
-// once stays reusable. The FP4 decode merges in two levels (groups of
-// fp4_group_size workgroups, then the group results and the BF16 partition), so
-// most of the merging overlaps the workgroups still streaming and the last
-// one to finish reads only a few partials.
+// takes the ticket of its (sequence, KV head); the one that draws the last
+// ticket merges all partials in one level (their loads in one or two memory
+// round trips) and puts the ticket back to zero, so a workspace zeroed once
+// stays reusable. One level keeps the chain after the last partition short:
+// store, ticket, loads, output.
 //
 // Visibility without cache flushes: partials are written and read with
 // 16-byte buffer accesses carrying the SC1 cache policy (coherent at device
@@ -106,134 +105,105 @@ __device__ __forceinline__ void reset_ticket(uint32_t* ticket) {
   if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merges slots [first, first + n) of (sequence b, KV head h); all 256
-// threads. With to_slot >= 0 the result is stored as a partial in that slot,
-// otherwise out = o / L is written. s_red: LDS scratch of at least 16
-// floats; s_w: LDS scratch of w_cap floats (w_cap >= 1024).
-// One memory round trip for up to 32 slots: each thread issues the loads of
-// its share of o (float4 t & 127 of o for the slots of parity t >> 7)
-// together with the (m, l) of slot t, then M, the weights e^(m_s - M) (in
-// LDS) and L are formed while the o loads land.
-constexpr int kMergeBatch = 16;                  // slots per parity per round trip
+// One partition's result as its threads hold it: thread t has
+// o[t >> 6][2 (t & 63) .. +2]; m and l are the same in every thread.
+struct Partial {
+  float o0, o1;
+  float m[4], l[4];
+};
 
-__device__ __forceinline__ void merge_slots(const MergeCtx& C, float* s_red, float* s_w, int w_cap, int b, int h,
-                                            int first, int n, int to_slot) {
+__device__ __forceinline__ void write_partial(const PartialWriter& W, const Partial& p) {
+  write_partial(W, p.o0, p.o1, p.m, p.l);
+}
+
+__device__ __forceinline__ float cload1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ float2 cload2(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kCachePolicySc1));
+  return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+}
+
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// Maximum and sum over the 64 lanes of a wave (uniform result; the sum in a
+// fixed order).
+__device__ __forceinline__ float wave_max(float v) {
+  v = max16(v);
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+
+// v[g] of a 4-array held in registers, by value selects (an indexed or
+// pointer-selected access would put the array in scratch memory).
+__device__ __forceinline__ float of_head(float v0, float v1, float v2, float v3, int g) {
+  const float lo = g == 0 ? v0 : v1, hi = g == 2 ? v2 : v3;
+  return g < 2 ? lo : hi;
+}
+
+// Merges the n partials of (sequence b, KV head h) and writes out = o / L.
+// Each wave merges its own query head (wave g, head g) with no workgroup
+// barrier: per batch of 64 partials, lane i loads (m, l) of partial i and
+// every lane loads its two channels of o of all 64 (one memory round trip,
+// the (m, l) loads first so the maximum and the weights are formed while o
+// lands); a batch after the first rescales what came before. With own, the
+// caller's partial (slot `skip`, in registers; has_own) seeds the merge and
+// is not loaded again, so a merge of 65 partials is one round trip. Offsets
+// of absent partials are past the resource and read 0.
+constexpr int kMergeBatch = 64;
+
+__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n, int skip, bool has_own,
+                                          const Partial& own) {
   const int bh = b * C.hkv + h;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const float ninf = -__builtin_inff();
   const __amdgpu_buffer_rsrc_t R = partial_rsrc(C, bh);
   constexpr int kSlotBytes = kPartialFloats * 4;
-  const int base = first * kSlotBytes;
-  const int q = tid & 127, par = tid >> 7, head = q >> 5;
-  // the weights of slots [0, n_w) live in LDS past the o reduction area
-  const int n_w = min(n, (w_cap - 1024) / 4);
-  float* s_wt = s_w + 1024;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float M[4] = {ninf, ninf, ninf, ninf};
-  for (int s0 = 0; s0 < n; s0 += 2 * kMergeBatch) {
-    float4 ov[kMergeBatch];
+  constexpr int kAbsent = 0x7FFFFF00;            // past every resource: reads 0
+  float M = ninf, Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  int nl = n;                                    // partials to load
+  if (has_own) {
+    M = of_head(own.m[0], own.m[1], own.m[2], own.m[3], g);
+    Ls = of_head(own.l[0], own.l[1], own.l[2], own.l[3], g);
+    o0 = own.o0;
+    o1 = own.o1;
+    nl = n - 1;
+  }
+  auto slot_of = [&](int i) { return (has_own && i >= skip) ? i + 1 : i; };
+  for (int i0 = 0; i0 < nl; i0 += kMergeBatch) {
+    const int i = i0 + lane;
+    const bool ok = i < nl;
+    const int ml_off = ok ? slot_of(i) * kSlotBytes + (512 + g) * 4 : kAbsent;
+    const float mr = cload1(R, ml_off);
+    const float lr = cload1(R, ml_off + 16);
+    float2 ov[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int s = s0 + par + 2 * k;
-      ov[k] = s < n ? cload4(R, base + s * kSlotBytes + q * 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int ik = i0 + k;
+      ov[k] = cload2(R, ik < nl ? slot_of(ik) * kSlotBytes + (g * kD + 2 * lane) * 4 : kAbsent);
     }
-    if (s0 == 0) {
-      // M and L over all slots (thread t takes slots t, t + 256, ...)
-      float4 mv[4], lv[4];
-      float mx[4] = {ninf, ninf, ninf, ninf};
-      for (int sb = 0; sb < n; sb += 1024) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int s = sb + tid + 256 * k;
-          mv[k] = s < n ? cload4(R, base + s * kSlotBytes + 512 * 4) : make_float4(ninf, ninf, ninf, ninf);
-          lv[k] = s < n ? cload4(R, base + s * kSlotBytes + 516 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          mx[0] = fmaxf(mx[0], mv[k].x); mx[1] = fmaxf(mx[1], mv[k].y);
-          mx[2] = fmaxf(mx[2], mv[k].z); mx[3] = fmaxf(mx[3], mv[k].w);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        for (int o = 32; o >= 1; o >>= 1) mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], o, 64));
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) s_red[wave * 4 + g] = mx[g];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        M[g] = fmaxf(fmaxf(s_red[g], s_red[4 + g]), fmaxf(s_red[8 + g], s_red[12 + g]));
-      __syncthreads();
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int sb = 0; sb < n; sb += 1024) {
-        if (sb > 0) {                            // more than 1024 slots: reload (m, l)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int s = sb + tid + 256 * k;
-            mv[k] = s < n ? cload4(R, base + s * kSlotBytes + 512 * 4) : make_float4(ninf, ninf, ninf, ninf);
-            lv[k] = s < n ? cload4(R, base + s * kSlotBytes + 516 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int s = sb + tid + 256 * k;
-          const float mm[4] = {mv[k].x, mv[k].y, mv[k].z, mv[k].w}, ll[4] = {lv[k].x, lv[k].y, lv[k].z, lv[k].w};
-          float w[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            w[g] = mm[g] == ninf ? 0.0f : __expf(mm[g] - M[g]);
-            ls[g] = fmaf(w[g], ll[g], ls[g]);
-          }
-          if (s < n_w) *reinterpret_cast<float4*>(s_wt + 4 * s) = make_float4(w[0], w[1], w[2], w[3]);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        for (int o = 32; o >= 1; o >>= 1) ls[g] += __shfl_xor(ls[g], o, 64);
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) s_red[wave * 4 + g] = ls[g];
-      }
-      __syncthreads();
-    }
-    const float Mh = head == 0 ? M[0] : (head == 1 ? M[1] : (head == 2 ? M[2] : M[3]));
+    const float ms = ok ? mr : ninf;
+    const float Mn = fmaxf(M, wave_max(ms));
+    const float f = M == ninf ? 0.0f : __expf(M - Mn);     // rescale of the partials before
+    const float w = ms == ninf ? 0.0f : __expf(ms - Mn);
+    Ls = fmaf(Ls, f, wave_sum(w * (ok ? lr : 0.0f)));
+    o0 *= f;
+    o1 *= f;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int s = s0 + par + 2 * k;
-      float w = 0.0f;
-      if (s < n_w) {
-        w = s_wt[4 * s + head];
-      } else if (s < n) {
-        const float4 m = cload4(R, base + s * kSlotBytes + 512 * 4);
-        const float ms = head == 0 ? m.x : (head == 1 ? m.y : (head == 2 ? m.z : m.w));
-        w = ms == ninf ? 0.0f : __expf(ms - Mh);
-      }
-      acc.x = fmaf(w, ov[k].x, acc.x);
-      acc.y = fmaf(w, ov[k].y, acc.y);
-      acc.z = fmaf(w, ov[k].z, acc.z);
-      acc.w = fmaf(w, ov[k].w, acc.w);
+      const float wk = lane_f32(w, k);
+      o0 = fmaf(wk, ov[k].x, o0);
+      o1 = fmaf(wk, ov[k].y, o1);
     }
+    M = Mn;
   }
-  __syncthreads();
-  reinterpret_cast<float4*>(s_w)[tid] = acc;     // [parity][q]: o reduction area s_w[0, 1024)
-  __syncthreads();
-  const int oh = tid >> 6, od = 2 * (tid & 63);
-  float L4[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) L4[g] = (s_red[g] + s_red[4 + g]) + (s_red[8 + g] + s_red[12 + g]);
-  const float* lo_par = s_w + oh * kD + od;      // parity 0: float4 index q = oh * 32 + od / 4
-  const float r0 = lo_par[0] + lo_par[512], r1 = lo_par[1] + lo_par[513];
-  if (to_slot >= 0) {
-    write_partial(partial_writer(C, bh, to_slot), r0, r1, M, L4);
-  } else {
-    const float Lo = oh == 0 ? L4[0] : (oh == 1 ? L4[1] : (oh == 2 ? L4[2] : L4[3]));
-    float* out = C.out + ((size_t)b * C.hq + h * kGroup + oh) * kD + od;
-    *reinterpret_cast<float2*>(out) = make_float2(r0 / Lo, r1 / Lo);
-  }
+  float* out = C.out + ((size_t)b * C.hq + h * kGroup + g) * kD + 2 * lane;
+  *reinterpret_cast<float2*>(out) = make_float2(o0 / Ls, o1 / Ls);
 }
 
 // NaN output rows for a sequence whose length or pages are invalid.

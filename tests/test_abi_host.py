@@ -106,9 +106,9 @@ def test_sizes_and_plan():
     ppp, parts = bd.decode_plan(1, 8, 131072, 0)
     assert ppp == 4 and parts == -(-1024 // ppp)
     ws = bd.decode_workspace_size(1, 32, 8, 131072, 4)
-    assert ws == 16384 * 33 * 4 + 8 * (256 + 2) * 520 * 4
+    assert ws == 16384 * 4 + 8 * (256 + 2) * 520 * 4
     # a partial last page adds a BF16-decode partition
-    assert bd.decode_workspace_size(2, 8, 2, 1000, 3) == 16384 * 33 * 4 + 4 * (3 + 2) * 520 * 4
+    assert bd.decode_workspace_size(2, 8, 2, 1000, 3) == 16384 * 4 + 4 * (3 + 2) * 520 * 4
     with pytest.raises(bd.Bdfp4Error) as ei:
         bd.decode_workspace_size(1, 24, 8, 1000, 0)
     assert ei.value.status == bd.E_UNSUPPORTED
