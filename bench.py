@@ -258,6 +258,37 @@ def counter_traffic():
     return int(float(kv["traffic_bytes_per_launch"])), "counters"
 
 
+def read_ceiling(nbytes: int, slices: int = 8, rounds: int = 10, workgroups: int = 512):
+    """The practical HBM read ceiling for one decode layer's byte count: the
+    library's plain streaming read (bdfp4_stream_read) over `slices` distinct
+    buffers of that size in turn, so no slice is still in the last-level
+    cache when it is read again."""
+    import torch
+
+    import fp4_kv_cache_nvfp4_amd as bd
+
+    n = (nbytes + 15) // 16 * 16
+    buf = torch.empty(n * slices, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.empty(workgroups * 256, dtype=torch.int32, device="cuda")
+    views = [buf[i * n:(i + 1) * n] for i in range(slices)]
+    for v in views:
+        bd.stream_read(v, sink, workgroups)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for v in views:
+            bd.stream_read(v, sink, workgroups)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (rounds * slices)
+    del buf
+    return {"bytes": n, "us": round(us, 3), "GBps": round(n / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(n / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "workgroups": workgroups,
+            "kernel": "bdfp4_stream_read (plain coalesced read, 4 x 16 B in flight per thread)"}
+
+
 def copy_calibration():
     import torch
 
@@ -315,6 +346,9 @@ def main():
               f"{per * 1e3:.2f} us ({res[a]['kernel_GBps']:.0f} GB/s)", file=sys.stderr, flush=True)
     del layers
     torch.cuda.empty_cache()
+    ceiling = read_ceiling(res["nvfp4"]["bytes_per_layer"])
+    print(f"[bench] plain read of {ceiling['bytes']} B: {ceiling['us']:.2f} us ({ceiling['GBps']:.0f} GB/s)",
+          file=sys.stderr, flush=True)
     writer = {}
     if not args.no_writer:
         for mx in (False, True):
@@ -354,7 +388,9 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": "bdfp4::decode_kernel<false,2,true>",
                      "bytes_per_launch": h["bytes_per_layer"], "us_per_launch": round(us_launch, 3),
-                     "us_per_launch_single_events": round(h["us_kernel_events"], 3)},
+                     "us_per_launch_single_events": round(h["us_kernel_events"], 3),
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": round(ceiling["us"] / us_launch, 4)},
         "cpu_baseline": cpu,
         "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
         "writer_131072x8": writer,

@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
         "bdfp4_bf16_decode_attention": [P, I32, I32, I32, P, P, I32, P, I32, P, I32, F32, I32, P, SZ, P, P],
         "bdfp4_quantize_rows": [P, I32, P, I32, I32, I32, P, P, P],
         "bdfp4_quantize_p_blocks": [P, I32, I32, F32, P, P, P],
+        "bdfp4_stream_read": [P, SZ, P, SZ, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -247,6 +248,14 @@ def quantize_rows(rows, shift, rotation: int, mode: int, terms: int, codes, scal
 def quantize_p_blocks(pp, mode: int, tau: float, codes, scales, stream=None) -> None:
     _check(lib().bdfp4_quantize_p_blocks(_ptr(pp), int(pp.shape[0]) if pp is not None else 0, mode, float(tau),
                                          _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def stream_read(src, sink, workgroups: int, nbytes: int | None = None, stream=None) -> None:
+    """bdfp4_stream_read: a plain streaming read of `src` (the practical HBM
+    read ceiling for a byte count); `sink` takes one uint32 per thread."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().bdfp4_stream_read(_ptr(src), n, _ptr(sink), sink.numel() * sink.element_size(), int(workgroups),
+                                   _stream(stream)))
 
 
 class DecodeCall:

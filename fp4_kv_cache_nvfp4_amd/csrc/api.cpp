@@ -444,4 +444,16 @@ bdfp4_status bdfp4_quantize_p_blocks(const float* pp, int32_t n_blocks, int32_t 
                     "probability quantizer launch");
 }
 
+bdfp4_status bdfp4_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, int32_t workgroups,
+                               void* stream) {
+  if (workgroups < 1 || workgroups > 65536) return fail(BDFP4_E_INVALID, "workgroups must be in [1, 65536]");
+  if (bytes % 16 != 0) return fail(BDFP4_E_INVALID, "bytes must be a multiple of 16");
+  if (!src || !sink) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return fail(BDFP4_E_INVALID, "src must be 16-byte and sink 4-byte aligned");
+  if (sink_bytes < (size_t)workgroups * 256 * 4) return fail(BDFP4_E_INVALID, "sink needs workgroups * 1024 bytes");
+  return hip_status(bdfp4::launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), workgroups,
+                                              static_cast<hipStream_t>(stream)),
+                    "stream read launch");
+}
+
 }  // extern "C"

@@ -79,6 +79,8 @@ struct Bf16DecodeLaunch {
 
 hipError_t launch_bf16_decode(const Bf16DecodeLaunch& L, hipStream_t stream);
 
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+
 constexpr int kGroup = 4;                         // query heads per KV head
 constexpr int kPartialFloats = kGroup * 130;      // o[4][128], m[4], l[4] (+pad)
 constexpr int kMaxSeqHeads = 16384;               // (sequence, KV head) pairs per call

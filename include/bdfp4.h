@@ -246,6 +246,18 @@ bdfp4_status bdfp4_quantize_p_blocks(const float* pp, int32_t n_blocks,
                                      int32_t mode, float tau, uint8_t* codes,
                                      uint8_t* scales, void* stream);
 
+/* Diagnostic: a plain streaming read of `bytes` (a multiple of 16) at `src`
+ * (device, 16-byte aligned) by `workgroups` workgroups of 256 threads (1 ..
+ * 65536), grid-stride over 16-byte words with four loads in flight per
+ * thread. Every thread stores one uint32 fold (xor) of what it read to
+ * `sink` (device, at least workgroups * 256 * 4 bytes), so the reads cannot
+ * be elided. It measures the practical HBM read bandwidth for a byte count,
+ * the ceiling the decode's roofline fraction is read against. Asynchronous
+ * on `stream`; E_INVALID for bad sizes, alignment or NULL pointers. */
+bdfp4_status bdfp4_stream_read(const void* src, size_t bytes, void* sink,
+                               size_t sink_bytes, int32_t workgroups,
+                               void* stream);
+
 /* Name of a status code (static string). */
 const char* bdfp4_status_string(int32_t status);
 

@@ -204,3 +204,14 @@ def test_bf16_decode_rejects_before_launch():
     assert call(kp=None) == bd.E_INVALID
     assert call(maxlen=2049) == bd.E_INVALID       # 17 pages needed, 16 in the table
     assert call(wsb=64) == bd.E_WORKSPACE
+
+
+def test_stream_read_rejects_before_launch():
+    L = bd.lib()
+    ok_sink = 512 * 256 * 4
+    assert L.bdfp4_stream_read(FAKE, 4096, FAKE, ok_sink, 0, None) == bd.E_INVALID          # no workgroups
+    assert L.bdfp4_stream_read(FAKE, 4096, FAKE, ok_sink, 70000, None) == bd.E_INVALID      # too many
+    assert L.bdfp4_stream_read(FAKE, 4100, FAKE, ok_sink, 512, None) == bd.E_INVALID        # not 16-byte words
+    assert L.bdfp4_stream_read(None, 4096, FAKE, ok_sink, 512, None) == bd.E_INVALID
+    assert L.bdfp4_stream_read(FAKE + 8, 4096, FAKE, ok_sink, 512, None) == bd.E_INVALID    # misaligned source
+    assert L.bdfp4_stream_read(FAKE, 4096, FAKE, ok_sink - 4, 512, None) == bd.E_INVALID    # sink too small

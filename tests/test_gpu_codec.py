@@ -92,3 +92,19 @@ def test_p_blocks_bit_exact(mode, tau):
     nib, sc = Q.quantize_p(pp, mode, np.float32(tau))
     assert np.array_equal(scales.cpu().numpy(), sc[:, 0])
     assert np.array_equal(codes.cpu().numpy(), _pack_logical(nib))
+
+
+@pytest.mark.parametrize("nwords,wgs", [(1, 1), (1000, 3), (4096 * 7 + 5, 512), (1 << 20, 512)])
+def test_stream_read_folds_every_word_once(nwords, wgs):
+    # each 16-byte word is read by exactly one thread, which xors its four
+    # 32-bit lanes into its sink word: the xor of the sink is the xor of the
+    # whole buffer
+    g = torch.Generator().manual_seed(nwords)
+    host = torch.randint(-(1 << 31), (1 << 31) - 1, (nwords * 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    src = host.to("cuda")
+    sink = torch.full((wgs * 256,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    bd.stream_read(src, sink, wgs)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert got == want
