@@ -143,7 +143,6 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
 struct Smem {
   float logit[4][4 * kWaveTok];             // per wave: [head][token] raw logits; then its o [head][128]
   uint16_t qhat[2][4][kD];                  // 16-bit dequantized query terms [term][head][channel]
-  float q[4][kD];                           // raw float32 query (BF16 partition)
   uint32_t pst[4][16][16];                  // per wave: P_hat staging [row][token pair]; rows 4..15 stay 0
   float qmu[4];
   float red[4][4];                          // per wave, per head: partition maximum (raw logit)
@@ -171,67 +170,83 @@ __device__ __forceinline__ MergeCtx merge_ctx(const DecArgs& A) {
 // ------------------------------------------------------------ BF16 partition
 
 // Tokens [0, min(S, L)) from the sink buffer and [max(S, 128 n), L) from the
-// tail page: exact float32 attention of the raw query. All of the
-// workgroup's loads (K row of token t for thread t, the query, and the V rows
-// of its token group for thread (token group, channel quad)) are issued
-// before the first barrier, so the partition costs one memory round trip.
+// tail page: exact float32 attention of the raw query. QK^T runs on
+// v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact, the sums float32,
+// as in a float32 dot product of the bf16 inputs): wave w takes the 16-token
+// tiles w, w + 4, ..., rows 0..3 of A are the 4 query heads. The maximum and
+// l come from DPP row reductions and one LDS exchange across the waves; PV is
+// float32 on the VALU, thread (wave w, lane l) taking channels 2l, 2l + 1 of
+// the tokens w, w + 4, .... The query, K and V rows of up to 144 tokens are
+// all requested before the first wait, so the partition costs one memory
+// round trip; longer sink + tail spans read their remaining V rows after.
+constexpr int kBfTilesPerWave = 4;                 // 16 tiles of 16 tokens: up to 256 tokens
+constexpr int kBfVPerThread = 36;                  // V rows per thread requested up front (144 tokens)
+
 __device__ Partial bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int L, int n_full) {
   const DecodeLaunch& P = A.L;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = P.sink;
   const int nsink = L < S ? L : S;
   const int tail_lo = S > kPage * n_full ? S : kPage * n_full;
   const int ntail = L > tail_lo ? L - tail_lo : 0;
-  const int nb = nsink + ntail;                      // <= 112 + 127 < 256
+  const int nb = nsink + ntail;                      // <= 128 + 127 < 256
   const size_t bhk = (size_t)b * P.hkv + h;
   const int tail0 = tail_lo - kPage * n_full;
   auto row_of = [&](const uint16_t* sink, const uint16_t* tail, int j) -> const uint16_t* {
     return j < nsink ? sink + (bhk * S + j) * kD : tail + (bhk * kPage + tail0 + (j - nsink)) * kD;
   };
-  uint4 kw[16];
-  if (tid < nb) {
-    const uint4* k4 = reinterpret_cast<const uint4*>(row_of(P.sink_k, P.tail_k, tid));
+  const int row = lane & 15, kg = lane >> 4;
+  // A: query head `row` (rows 4..15 zero), channels 32 c + 8 kg .. + 8 for MFMA c
+  u32x4_t aq[4];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) kw[c] = k4[c];
-  }
-  constexpr int kVPer = 30;                          // ceil(240 / 8) tokens per token group
-  const int tg = tid >> 5, cq = tid & 31;            // token group, channel quad
-  uint2 vv[kVPer];
-#pragma unroll
-  for (int k = 0; k < kVPer; ++k) {
-    const int j = tg + 8 * k;
-    vv[k] = j < nb ? *reinterpret_cast<const uint2*>(row_of(P.sink_v, P.tail_v, j) + 4 * cq) : make_uint2(0u, 0u);
-  }
-  for (int i = tid; i < 4 * kD; i += 256) {
-    const int g = i >> 7, d = i & 127;
-    sm.q[g][d] = bf16_lo(P.q[((size_t)b * P.hq + h * kGroup + g) * kD + d]);
-  }
-  __syncthreads();
-  float t[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-  if (tid < nb) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint32_t ww[4] = {kw[c].x, kw[c].y, kw[c].z, kw[c].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 8 * c + 2 * i;
-        const float k0 = bf16_lo(ww[i]), k1 = bf16_hi(ww[i]);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) acc[g] = fmaf(sm.q[g][d + 1], k1, fmaf(sm.q[g][d], k0, acc[g]));
-      }
+  for (int c = 0; c < 4; ++c) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < kGroup) {
+      const uint4 t = *reinterpret_cast<const uint4*>(P.q + ((size_t)b * P.hq + h * kGroup + row) * kD + 32 * c + 8 * kg);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) t[g] = P.softmax_scale * acc[g];
+    aq[c] = v;
   }
-  float mx[4];
+  // B: token 16 tile + row of each of this wave's tiles, same channels
+  u32x4_t bk[kBfTilesPerWave][4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float v = t[g];
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
-    mx[g] = v;
+  for (int k = 0; k < kBfTilesPerWave; ++k) {
+    const int j = 16 * (wave + 4 * k) + row;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (j < nb) {
+        const uint4 t = *reinterpret_cast<const uint4*>(row_of(P.sink_k, P.tail_k, j) + 32 * c + 8 * kg);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+      }
+      bk[k][c] = v;
+    }
   }
-  const int wave = tid >> 6, lane = tid & 63;
+  // V: channels 2 lane, 2 lane + 1 of tokens wave + 4 m
+  uint32_t vv[kBfVPerThread];
+#pragma unroll
+  for (int m = 0; m < kBfVPerThread; ++m) {
+    const int j = wave + 4 * m;
+    vv[m] = j < nb ? reinterpret_cast<const uint32_t*>(row_of(P.sink_v, P.tail_v, j))[lane] : 0u;
+  }
+  // logits: lanes 0..15 hold token 16 tile + lane, heads 0..3 in acc[0..3]
+  const float sigma = P.softmax_scale;
+  float t[kBfTilesPerWave][4];
+  float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+  for (int k = 0; k < kBfTilesPerWave; ++k) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = mfma<true>(aq[c], bk[k][c], acc);
+    const bool live = lane < 16 && 16 * (wave + 4 * k) + lane < nb;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      t[k][g] = live ? sigma * acc[g] : kNegInf;
+      mx[g] = fmaxf(mx[g], t[k][g]);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) mx[g] = max16(mx[g]);  // lanes 0..15: this wave's maximum
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) sm.red[wave][g] = mx[g];
@@ -239,56 +254,56 @@ __device__ Partial bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int 
   __syncthreads();
   float m[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    m[g] = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
-  float ls[4];
-  float4 pr;
-  {
+  for (int g = 0; g < 4; ++g) m[g] = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
+  // p of the wave's tokens into LDS [token][head]; l per wave
+  float* flat = &sm.logit[0][0];
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kBfTilesPerWave; ++k) {
     float pv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float p = (tid < nb && m[g] != kNegInf) ? __expf(t[g] - m[g]) : 0.0f;
-      pv[g] = p;
-      float v = p;
-      for (int o = 32; o >= 1; o >>= 1) v += shfl_xor(v, o);
-      ls[g] = v;
+      pv[g] = t[k][g] == kNegInf ? 0.0f : __expf(t[k][g] - m[g]);
+      ls[g] += pv[g];
     }
-    pr = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    const int j = 16 * (wave + 4 * k) + lane;
+    if (lane < 16 && j < nb) reinterpret_cast<float4*>(flat)[j] = make_float4(pv[0], pv[1], pv[2], pv[3]);
   }
-  float* flat = &sm.logit[0][0];
-  reinterpret_cast<float4*>(flat)[tid] = pr;         // p of token tid, [token][head]
+#pragma unroll
+  for (int g = 0; g < 4; ++g) ls[g] = sum16(ls[g]);
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) sm.lsum[wave][g] = ls[g];
   }
   __syncthreads();
-  // o[head][4 cq .. +4] over the tokens tg, tg + 8, ... of this thread
-  float o[4][4] = {};
+  // PV over the tokens wave + 4 m
+  float o[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  auto pv_token = [&](int j, uint32_t w) {
+    const float4 p = reinterpret_cast<const float4*>(flat)[j];
+    const float v0 = bf16_lo(w), v1 = bf16_hi(w);
+    o[0][0] = fmaf(p.x, v0, o[0][0]); o[0][1] = fmaf(p.x, v1, o[0][1]);
+    o[1][0] = fmaf(p.y, v0, o[1][0]); o[1][1] = fmaf(p.y, v1, o[1][1]);
+    o[2][0] = fmaf(p.z, v0, o[2][0]); o[2][1] = fmaf(p.z, v1, o[2][1]);
+    o[3][0] = fmaf(p.w, v0, o[3][0]); o[3][1] = fmaf(p.w, v1, o[3][1]);
+  };
 #pragma unroll
-  for (int k = 0; k < kVPer; ++k) {
-    const int j = tg + 8 * k;
-    if (j < nb) {
-      const float4 p = reinterpret_cast<const float4*>(flat)[j];
-      const float v[4] = {bf16_lo(vv[k].x), bf16_hi(vv[k].x), bf16_lo(vv[k].y), bf16_hi(vv[k].y)};
-      const float pg[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[g][c] = fmaf(pg[g], v[c], o[g][c]);
-      }
-    }
+  for (int mm = 0; mm < kBfVPerThread; ++mm) {
+    const int j = wave + 4 * mm;
+    if (j < nb) pv_token(j, vv[mm]);
   }
-  float* so = flat + 1024;                           // [token group][head][128], past the p values
+  for (int j = wave + 4 * kBfVPerThread; j < nb; j += 4)        // spans longer than 144 tokens
+    pv_token(j, reinterpret_cast<const uint32_t*>(row_of(P.sink_v, P.tail_v, j))[lane]);
+  float* so = flat + 1024;                           // [wave][head][128], past the p values
 #pragma unroll
   for (int g = 0; g < 4; ++g)
-    *reinterpret_cast<float4*>(so + (tg * 4 + g) * kD + 4 * cq) = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+    *reinterpret_cast<float2*>(so + (wave * 4 + g) * kD + 2 * lane) = make_float2(o[g][0], o[g][1]);
   __syncthreads();
   const int head = tid >> 6, d = (tid & 63) * 2;
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-  for (int g8 = 0; g8 < 8; ++g8) {
-    o0 += so[(g8 * 4 + head) * kD + d];
-    o1 += so[(g8 * 4 + head) * kD + d + 1];
+  for (int w = 0; w < 4; ++w) {
+    o0 += so[(w * 4 + head) * kD + d];
+    o1 += so[(w * 4 + head) * kD + d + 1];
   }
   Partial r;
   r.o0 = o0;
@@ -461,11 +476,14 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 // each wave streams its own pages_per_partition consecutive pages through
 // pass 1, its own maximum and pass 2 with no workgroup barrier in between;
 // the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
-// workgroup's partial (returned; the caller stores it).
+// workgroup's partial (returned; the caller stores it). With bf16 the
+// workgroup also computes the (sequence, KV head)'s BF16 partition while its
+// first K page loads and folds it into the same partial.
 template <bool kMx, int kTerms, bool kUnder>
-__device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int n_full) {
+__device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_full = L / kPage;
   const int p0 = (4 * sp + wave) * P.ppp;                       // first page of this wave's partition
   const int npg = max(0, min(n_full, p0 + P.ppp) - p0);         // its pages, 0 .. pages_per_partition
   const size_t hkv = P.hkv;
@@ -498,6 +516,8 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   KPage kb0, kb1, kb2;
   VPage vb0, vb1, vb2;
   load_k<kMx>(kb0, P, blk_of(0), lane);
+  Partial bfp;
+  if (bf16) bfp = bf16_partition(A, sm, b, h, L, n_full);
   load_k<kMx>(kb1, P, blk_of(1), lane);
   query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
@@ -699,10 +719,14 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     sm.bad[wave] = bad ? 1 : 0;
   }
   __syncthreads();
-  // ---- log-sum-exp merge of the four partitions: thread (head, channel pair)
+  // ---- log-sum-exp merge of the four partitions, and of the BF16 partition
+  // when this workgroup computed it: thread (head, channel pair). The FP4
+  // part is formed against its own maximum as without the BF16 partition,
+  // then both parts are weighted against the overall maximum (a factor of
+  // exactly 1 for the larger one).
   const float sigma = P.softmax_scale;
   const float invc = 1.0f / cf;      // exact (c is a power of two)
-  float mm[4], ll[4], wgt[4][4];
+  float mm[4], ll[4], wgt[4][4], fa[4], fb[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const float M = fmaxf(fmaxf(sm.red[0][g], sm.red[1][g]), fmaxf(sm.red[2][g], sm.red[3][g]));
@@ -713,8 +737,13 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
       wgt[g][w] = mw == kNegInf ? 0.0f : __expf(sigma * (mw - M));
       l = fmaf(wgt[g][w], sm.lsum[w][g], l);
     }
-    mm[g] = sigma * M;
-    ll[g] = l * invc;
+    const float mf = sigma * M;                  // FP4 maximum (sigma included; -inf if empty)
+    const float mb = bf16 ? bfp.m[g] : kNegInf;  // BF16 maximum
+    const float mx = fmaxf(mf, mb);
+    fa[g] = M == kNegInf ? 0.0f : __expf(mf - mx);
+    fb[g] = mb == kNegInf ? 0.0f : __expf(mb - mx);
+    mm[g] = mx;
+    ll[g] = fmaf(fa[g], l * invc, bf16 ? fb[g] * bfp.l[g] : 0.0f);
   }
   const int head = tid >> 6, d = (tid & 63) * 2;
   float o0 = 0.f, o1 = 0.f;
@@ -725,11 +754,15 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     o0 = fmaf(wh, ow[0], o0);
     o1 = fmaf(wh, ow[1], o1);
   }
+  const float fah = head == 0 ? fa[0] : (head == 1 ? fa[1] : (head == 2 ? fa[2] : fa[3]));
+  const float fbh = head == 0 ? fb[0] : (head == 1 ? fb[1] : (head == 2 ? fb[2] : fb[3]));
+  o0 = fmaf(fah, o0 * invc, bf16 ? fbh * bfp.o0 : 0.0f);
+  o1 = fmaf(fah, o1 * invc, bf16 ? fbh * bfp.o1 : 0.0f);
   const bool poisoned = (sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3]) != 0;
   const float nan = __builtin_nanf("");
   Partial r;
-  r.o0 = poisoned ? nan : o0 * invc;
-  r.o1 = poisoned ? nan : o1 * invc;
+  r.o0 = poisoned ? nan : o0;
+  r.o1 = poisoned ? nan : o1;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     r.m[g] = poisoned ? 0.0f : mm[g];
@@ -738,56 +771,46 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   return r;
 }
 
-// Workgroup j is FP4 workgroup j % G of (sequence, KV head) j / G, G per
-// (sequence, KV head). The BF16 partition of (sequence, KV head) j is
-// computed by workgroup j of the grid after its FP4 partition: the first
-// workgroups are dispatched first and, being the oldest on their CUs, finish
-// first, so the extra work lands where there is slack. Slots: FP4 workgroup
-// sp -> sp, the BF16 partition -> the FP4 workgroup count of its sequence.
-// Each partition takes its (sequence, KV head)'s ticket once its partial is
-// stored; the last one merges all nwg + 1 partials.
+// Workgroup j works for (sequence, KV head) j % (B Hkv) as its FP4 workgroup
+// sp = j / (B Hkv): the first B Hkv workgroups of the grid, dispatched first
+// and the oldest on their CUs, are the sp = 0 workgroups of every (sequence,
+// KV head), and those also compute the BF16 partition (while their first K
+// page loads) and fold it into their partial. Workgroup sp stores its
+// partial in slot sp and takes the (sequence, KV head)'s ticket; the last of
+// the nwg merges them all. A sequence without a full page has only the BF16
+// partition, written straight to the output by its sp = 0 workgroup.
 template <bool kMx, int kTerms, bool kUnder>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
   const MergeCtx C = merge_ctx(A);
-  auto fp4_count = [&](int L) {
-    const int n_full = L / kPage;
-    return n_full > 0 ? fp4_wgs((n_full + P.ppp - 1) / P.ppp) : 0;
-  };
-  auto valid = [&](int L) { return L >= 1 && L <= P.max_seq_len && L / kPage <= P.max_pages_per_seq; };
-  // FP4 role
-  const int G = fp4_wgs(P.max_parts);
-  const int bh = (int)blockIdx.x / G, sp = (int)blockIdx.x - bh * G;
+  const int BH = P.batch * P.hkv;
+  const int bh = (int)blockIdx.x % BH, sp = (int)blockIdx.x / BH;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
   const int L = P.seq_lens[b];
-  const int nwg = valid(L) ? fp4_count(L) : 0;
-  if (sp < nwg) {
-    const Partial mine = fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L / kPage);
-    write_partial(partial_writer(C, bh, sp), mine);
-    uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
-    if (take_ticket(ticket, 1, &sm.tick) == nwg) {
-      merge_out(C, b, h, nwg + 1, sp, true, mine);
-      reset_ticket(ticket);
-    }
+  if (L < 1 || L > P.max_seq_len || L / kPage > P.max_pages_per_seq) {
+    if (sp == 0) poison_rows(P.out, P.hq, b, h);
+    return;
   }
-  // BF16 role
-  const int bh2 = (int)blockIdx.x;
-  if (bh2 < P.batch * P.hkv) {
-    const int b2 = bh2 / P.hkv, h2 = bh2 - b2 * P.hkv;
-    const int L2 = P.seq_lens[b2];
-    if (!valid(L2)) {
-      poison_rows(P.out, P.hq, b2, h2);
-      return;
+  const int n_full = L / kPage;
+  const int nwg = n_full > 0 ? fp4_wgs((n_full + P.ppp - 1) / P.ppp) : 0;   // FP4 workgroups of this sequence
+  if (nwg == 0) {
+    if (sp == 0) {
+      const Partial r = bf16_partition(A, sm, b, h, L, 0);
+      const int head = threadIdx.x >> 6, d = 2 * (threadIdx.x & 63);
+      const float l = of_head(r.l[0], r.l[1], r.l[2], r.l[3], head);
+      float* out = P.out + ((size_t)b * P.hq + h * kGroup + head) * kD + d;
+      *reinterpret_cast<float2*>(out) = make_float2(r.o0 / l, r.o1 / l);
     }
-    const int nwg2 = fp4_count(L2);
-    const Partial r = bf16_partition(A, sm, b2, h2, L2, L2 / kPage);
-    write_partial(partial_writer(C, bh2, nwg2), r);
-    uint32_t* ticket = C.counters + (size_t)bh2 * C.counter_stride;
-    if (take_ticket(ticket, 1, &sm.tick) == nwg2) {
-      merge_out(C, b2, h2, nwg2 + 1, nwg2, true, r);
-      reset_ticket(ticket);
-    }
+    return;
+  }
+  if (sp >= nwg) return;
+  const Partial mine = fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L, sp == 0);
+  write_partial(partial_writer(C, bh, sp), mine);
+  uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
+  if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
+    merge_out(C, b, h, nwg, sp, true, mine);
+    reset_ticket(ticket);
   }
 }
 

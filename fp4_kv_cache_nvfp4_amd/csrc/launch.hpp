@@ -99,9 +99,9 @@ __host__ __device__ inline int fp4_wgs(int parts) {
 // [batch * hkv][slot_stride][kPartialFloats] float32, slot_stride = parts + 2
 // for parts = partitions of the longest sequence counting its partial last
 // page (ceil(ceil(max_seq_len / 128) / pages_per_partition)). An FP4 decode
-// of a sequence with w FP4 workgroups uses slots 0 .. w-1 (one per
-// workgroup) and w (the BF16 partition); the BF16 decode uses one slot per
-// partition.
+// of a sequence with w FP4 workgroups uses slots 0 .. w-1, one per
+// workgroup (the BF16 partition is folded into slot 0); the BF16 decode uses
+// one slot per partition.
 constexpr size_t kTicketBytes = (size_t)kMaxSeqHeads * kTicketStride * sizeof(uint32_t);
 
 inline int32_t workspace_slot_stride(int32_t parts) { return parts + 2; }
