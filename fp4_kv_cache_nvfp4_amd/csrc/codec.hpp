@@ -147,6 +147,19 @@ __device__ __forceinline__ uint32_t e2m1_pair(float x0, float x1, float s, float
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quot(x0, m, r), quot(x1, m, r), s, 0) & 0xFFu;
 }
 
+typedef float e2m1_f32x2_t __attribute__((ext_vector_type(2)));
+
+// Signed grid values (exact float32) of the two E2M1 codes in byte `byte`
+// of w: the hardware convert with scale 1 (the select must be a constant).
+__device__ __forceinline__ e2m1_f32x2_t e2m1_grid_pair(uint32_t w, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
+}
+
 // ---------------------------------------------------------------- blocks
 
 // Quantize N in-register values (N even) with scale value s (float32):
@@ -179,18 +192,24 @@ __device__ __forceinline__ float quant_block(const float* x, float s, uint32_t* 
   if (!kSse) return 0.0f;
   float lvl[kLv];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const uint32_t mag = (packed[i >> 3] >> (4 * (i & 7))) & 7u;
-    const float q = __fmul_rn(e2m1_grid(mag), s);   // exact
-    const float d = __fsub_rn(__builtin_fabsf(x[i]), q);
-    float v = __fmul_rn(d, d);
-    int k = 0;
+  for (int i = 0; i < N; i += 2) {
+    // grid values of the two codes (hardware E2M1 -> float32 convert with
+    // scale 1: exact), then |x| - s |grid| (the product is exact)
+    const e2m1_f32x2_t gp = e2m1_grid_pair(packed[i >> 3], (i & 7) >> 1);
 #pragma unroll
-    for (int bit = 1; bit < N; bit <<= 1, ++k) {
-      if ((i & bit) == 0) break;
-      v = __fadd_rn(lvl[k], v);
+    for (int e = 0; e < 2; ++e) {
+      const int ie = i + e;
+      const float q = __fmul_rn(__builtin_fabsf(gp[e]), s);
+      const float d = __fsub_rn(__builtin_fabsf(x[ie]), q);
+      float v = __fmul_rn(d, d);
+      int k = 0;
+#pragma unroll
+      for (int bit = 1; bit < N; bit <<= 1, ++k) {
+        if ((ie & bit) == 0) break;
+        v = __fadd_rn(lvl[k], v);
+      }
+      lvl[k] = v;
     }
-    lvl[k] = v;
   }
   return lvl[kLv - 1];
 }
