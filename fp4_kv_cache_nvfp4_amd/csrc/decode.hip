@@ -507,14 +507,17 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
   // The wave reads a stream of eight slots, K pages 0..3 then V pages 0..3
-  // (slots of pages >= npg are empty), keeping the next two slots in flight
-  // while one is used. K page i lands in kb[i % 3], V page j in vb[j % 3];
-  // every load has a fixed destination, so at most four buffers are live.
-  // The loads are unconditional (a slot past npg reads physical page 0,
-  // which always exists, and is never used) so the compiler can count the
-  // loads in flight exactly and wait only for the slot about to be used.
-  KPage kb0, kb1, kb2;
-  VPage vb0, vb1, vb2;
+  // (slots of pages >= npg are empty), keeping the next slot in flight while
+  // one is used: K page i lands in kb[i % 2], V page j in vb[j % 2], and the
+  // load of a slot is issued once the slot two before it (same buffer) has
+  // been used. One page in flight per wave measured faster than two: with
+  // 8 waves per CU the memory pipe is already full, and deeper queues only
+  // delay the waves dispatched second. The loads are unconditional (a slot
+  // past npg reads physical page 0, which always exists, and is never used)
+  // so the compiler can count the loads in flight exactly and wait only for
+  // the slot about to be used.
+  KPage kb0, kb1;
+  VPage vb0, vb1;
   load_k<kMx>(kb0, P, blk_of(0), lane);
   Partial bfp;
   if (bf16) bfp = bf16_partition(A, sm, b, h, L, n_full);
@@ -597,14 +600,14 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     mb = __builtin_fmaxf(mb, pb);
   };
   static_assert(kMaxPpw == 4, "the stream below is unrolled for up to 4 pages");
-  load_k<kMx>(kb2, P, blk_of(2), lane);
   if (npg > 0) k_page(kb0, 0);
-  load_k<kMx>(kb0, P, blk_of(3), lane);
+  load_k<kMx>(kb0, P, blk_of(2), lane);
   if (npg > 1) k_page(kb1, 1);
+  load_k<kMx>(kb1, P, blk_of(3), lane);
+  if (npg > 2) k_page(kb0, 2);
   load_v<kMx>(vb0, P, blk_of(0), lane);
-  if (npg > 2) k_page(kb2, 2);
+  if (npg > 3) k_page(kb1, 3);
   load_v<kMx>(vb1, P, blk_of(1), lane);
-  if (npg > 3) k_page(kb0, 3);
   // the partition maximum of each head (rows of 16 lanes hold heads 2 hp, 2 hp + 1)
   ma = max16(ma);
   mb = max16(mb);
@@ -688,12 +691,12 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
       }
     }
   };
-  load_v<kMx>(vb2, P, blk_of(2), lane);
   if (npg > 0) v_page(vb0, 0);
-  load_v<kMx>(vb0, P, blk_of(3), lane);
+  load_v<kMx>(vb0, P, blk_of(2), lane);
   if (npg > 1) v_page(vb1, 1);
-  if (npg > 2) v_page(vb2, 2);
-  if (npg > 3) v_page(vb0, 3);
+  load_v<kMx>(vb1, P, blk_of(3), lane);
+  if (npg > 2) v_page(vb0, 2);
+  if (npg > 3) v_page(vb1, 3);
   // ---- this wave's (m, l, o) to LDS: o over its own logit rows (read above
   // by this wave only; its LDS instructions complete in order)
   lacc = sum16(lacc);                // rows of 16 lanes = heads
@@ -809,7 +812,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   write_partial(partial_writer(C, bh, sp), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
-    merge_out(C, b, h, nwg, sp, true, mine);
+    merge_out(C, b, h, nwg);
     reset_ticket(ticket);
   }
 }

@@ -151,55 +151,47 @@ __device__ __forceinline__ float of_head(float v0, float v1, float v2, float v3,
 // barrier: per batch of 64 partials, lane i loads (m, l) of partial i and
 // every lane loads its two channels of o of all 64 (one memory round trip,
 // the (m, l) loads first so the maximum and the weights are formed while o
-// lands); a batch after the first rescales what came before. With has_own,
-// the caller's partial (slot `skip`, in registers) takes its place in the
-// sequence without being loaded again. The partials are always combined in
-// slot order (lane order for l, slot order for o), so the result does not
-// depend on which workgroup merges: the output is deterministic. Offsets of
-// absent partials are past the resource and read 0.
+// lands); a batch after the first rescales what came before. The merging
+// workgroup reads its own partial back like the others (its stores completed
+// before it took the ticket). The resource covers exactly the n slots, so a
+// slot past them reads 0 and needs no address select; its weight is 0. The
+// partials are always combined in slot order (lane order for l, slot order
+// for o), so the result does not depend on which workgroup merges: the
+// output is deterministic.
 constexpr int kMergeBatch = 64;
 
-__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n, int skip, bool has_own,
-                                          const Partial& own) {
-  // (sequence, KV head) as a scalar: the buffer resource below must live in
-  // scalar registers, or every load becomes a loop over distinct values
+__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n) {
+  // (sequence, KV head) and n as scalars: the buffer resource below must
+  // live in scalar registers, or every load becomes a loop over distinct values
   const int bh = __builtin_amdgcn_readfirstlane(b * C.hkv + h);
+  const int ns = __builtin_amdgcn_readfirstlane(n);
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const float ninf = -__builtin_inff();
-  const __amdgpu_buffer_rsrc_t R = partial_rsrc(C, bh);
   constexpr int kSlotBytes = kPartialFloats * 4;
-  constexpr int kAbsent = 0x7FFFFF00;            // past every resource: reads 0
-  const int own_at = has_own ? skip : -1;
-  const float own_m = of_head(own.m[0], own.m[1], own.m[2], own.m[3], g);
-  const float own_l = of_head(own.l[0], own.l[1], own.l[2], own.l[3], g);
+  const __amdgpu_buffer_rsrc_t R =
+      __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0, ns * kSlotBytes, kRawBufferWord3);
+  const int o_off = (g * kD + 2 * lane) * 4;
   float M = ninf, Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+  for (int i0 = 0; i0 < ns; i0 += kMergeBatch) {
     const int i = i0 + lane;
-    const bool ok = i < n, mine = i == own_at;
-    const int ml_off = ok && !mine ? i * kSlotBytes + (512 + g) * 4 : kAbsent;
+    const int ml_off = i * kSlotBytes + (512 + g) * 4;
     const float mr = cload1(R, ml_off);
     const float lr = cload1(R, ml_off + 16);
     float2 ov[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const int ik = i0 + k;
-      ov[k] = cload2(R, ik < n && ik != own_at ? ik * kSlotBytes + (g * kD + 2 * lane) * 4 : kAbsent);
-    }
-    const float ms = ok ? (mine ? own_m : mr) : ninf;
-    const float lsl = ok ? (mine ? own_l : lr) : 0.0f;
+    for (int k = 0; k < kMergeBatch; ++k) ov[k] = cload2(R, (i0 + k) * kSlotBytes + o_off);
+    const float ms = i < ns ? mr : ninf;
     const float Mn = fmaxf(M, wave_max(ms));
     const float f = M == ninf ? 0.0f : __expf(M - Mn);     // rescale of the partials before
     const float w = ms == ninf ? 0.0f : __expf(ms - Mn);
-    Ls = fmaf(Ls, f, wave_sum(w * lsl));
+    Ls = fmaf(Ls, f, wave_sum(w * lr));
     o0 *= f;
     o1 *= f;
-    const int k_own = own_at - i0;                // uniform
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const float wk = lane_f32(w, k);
-      const bool here = k == k_own;
-      o0 = fmaf(wk, here ? own.o0 : ov[k].x, o0);
-      o1 = fmaf(wk, here ? own.o1 : ov[k].y, o1);
+      o0 = fmaf(wk, ov[k].x, o0);
+      o1 = fmaf(wk, ov[k].y, o1);
     }
     M = Mn;
   }
