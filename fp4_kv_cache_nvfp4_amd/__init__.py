@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "bdfp4_recipe_validate": [RP],
         "bdfp4_cache_bytes": [RP, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "bdfp4_quantize_pages": [RP, CP, P, P, P, I32, P, P],
+        "bdfp4_append_tokens": [RP, CP, P, P, I32, P, P, I32, P, P, P, P, P, P],
         "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
         "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
@@ -191,6 +192,19 @@ def quantize_pages(r: Recipe, cache: PagedCache, k, v, page_ids, key_shift=None,
     c = cache.struct()
     _check(lib().bdfp4_quantize_pages(ctypes.byref(r), ctypes.byref(c), _ptr(k), _ptr(v), _ptr(page_ids),
                                       n_pages, _ptr(key_shift), _stream(stream)))
+
+
+def append_tokens(r: Recipe, cache: PagedCache, k_new, v_new, positions, block_tables, sink_k, sink_v,
+                  tail_k, tail_v, key_shift=None, stream=None) -> None:
+    """One new token per sequence into its BF16 tail (and sink); a token that
+    fills a page freezes that page into the cache. k_new/v_new [B, Hkv, 128]
+    bf16, positions int32 [B] (device), block_tables int32 [B, max_pages]."""
+    batch = int(positions.numel())
+    c = cache.struct()
+    _check(lib().bdfp4_append_tokens(ctypes.byref(r), ctypes.byref(c), _ptr(k_new), _ptr(v_new), batch,
+                                     _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
+                                     _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v), _ptr(key_shift),
+                                     _stream(stream)))
 
 
 # ---------------------------------------------------------------- decode

@@ -249,6 +249,60 @@ bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cach
   return hip_status(bdfp4::launch_writer(L, static_cast<hipStream_t>(stream)), "page writer launch");
 }
 
+bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* k_new,
+                                 const void* v_new, int32_t batch, const int32_t* positions,
+                                 const int32_t* block_tables, int32_t max_pages_per_seq, void* sink_k,
+                                 void* sink_v, void* tail_k, void* tail_v, const float* key_shift,
+                                 void* stream) {
+  bdfp4_status s = check_kv_recipe(r);
+  if (s != BDFP4_OK) return s;
+  if ((s = check_cache(cache)) != BDFP4_OK) return s;
+  if (batch < 0) return fail(BDFP4_E_INVALID, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (max_pages_per_seq < 1 || max_pages_per_seq > (1 << 23))
+    return fail(BDFP4_E_INVALID, "max_pages_per_seq must be in [1, 2^23]");
+  if ((int64_t)batch * cache->num_kv_heads > 0x7FFFFFFF) return fail(BDFP4_E_INVALID, "batch too large");
+  if (!k_new || !v_new || !positions || !block_tables || !tail_k || !tail_v)
+    return fail(BDFP4_E_INVALID, "NULL input pointer");
+  if (r->sink_tokens > 0 && (!sink_k || !sink_v))
+    return fail(BDFP4_E_INVALID, "sink buffers required when sink_tokens > 0");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(tail_k) || !aligned16(tail_v) ||
+      (r->sink_tokens > 0 && (!aligned16(sink_k) || !aligned16(sink_v))))
+    return fail(BDFP4_E_INVALID, "token, tail and sink buffers must be 16-byte aligned");
+  if (r->key_smoothing && key_shift == nullptr)
+    return fail(BDFP4_E_INVALID, "key_smoothing needs key_shift (the key-mean sidecar)");
+  if (!r->key_smoothing && key_shift != nullptr)
+    return fail(BDFP4_E_INVALID, "key_shift given but key_smoothing is off");
+  if (key_shift && !aligned16(key_shift)) return fail(BDFP4_E_INVALID, "key_shift must be 16-byte aligned");
+  bdfp4::AppendLaunch L;
+  L.w.k = nullptr;
+  L.w.v = nullptr;
+  L.w.page_ids = nullptr;
+  L.w.key_shift = key_shift;
+  L.w.k_codes = cache->k_codes;
+  L.w.k_scales = cache->k_scales;
+  L.w.v_codes = cache->v_codes;
+  L.w.v_scales = cache->v_scales;
+  L.w.num_pages = cache->num_pages;
+  L.w.hkv = cache->num_kv_heads;
+  L.w.n_pages = 0;
+  L.w.rotation = r->rotation;
+  L.w.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
+  L.w.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
+  L.k_new = k_new;
+  L.v_new = v_new;
+  L.positions = positions;
+  L.block_tables = block_tables;
+  L.sink_k = r->sink_tokens > 0 ? sink_k : nullptr;
+  L.sink_v = r->sink_tokens > 0 ? sink_v : nullptr;
+  L.tail_k = tail_k;
+  L.tail_v = tail_v;
+  L.batch = batch;
+  L.max_pages_per_seq = max_pages_per_seq;
+  L.sink_tokens = r->sink_tokens;
+  return hip_status(bdfp4::launch_append(L, static_cast<hipStream_t>(stream)), "append launch");
+}
+
 bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                int32_t pages_per_partition, int32_t* ppp_out, int32_t* parts_out) {
   if (!ppp_out || !parts_out) return fail(BDFP4_E_INVALID, "NULL output");

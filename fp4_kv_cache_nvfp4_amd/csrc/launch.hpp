@@ -21,6 +21,23 @@ struct WriterLaunch {
 
 hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream);
 
+// Decode-time append: w carries the cache, key_shift, rotation and modes
+// (its k, v, page_ids and n_pages are unused).
+struct AppendLaunch {
+  WriterLaunch w;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
+  const int32_t* block_tables;
+  void* sink_k;
+  void* sink_v;
+  void* tail_k;
+  void* tail_v;
+  int32_t batch, max_pages_per_seq, sink_tokens;
+};
+
+hipError_t launch_append(const AppendLaunch& L, hipStream_t stream);
+
 hipError_t launch_rows(const void* rows, int n_rows, const float* shift, int rotation, int mode,
                        int terms, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 

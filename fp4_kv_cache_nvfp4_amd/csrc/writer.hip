@@ -10,7 +10,7 @@
 // KV_MODES bitdecoding-mxfp4 (mxfp4_search).
 //
 // One workgroup of 256 threads quantizes one (page, KV head) of either K or
-// V. Each row of 128 elements sits in four consecutive lanes, 32 elements per
+// V (page_head, shared by the bulk writer and the decode-time append). Each row of 128 elements sits in four consecutive lanes, 32 elements per
 // lane, so the rotation needs only two cross-lane (DPP quad) stages and every
 // NVFP4 block (16) / MXFP4 block (32) lies inside one lane. A wave covers a
 // 16-token tile, whose K codes are one contiguous 1 KiB run of the page
@@ -36,23 +36,36 @@ struct WriterArgs {
   int32_t rotation;
 };
 
-// kKMode / kVMode: 1 amax6, 2 four_six, 3 mxfp4_search.
-template <int kKMode, int kVMode>
-__global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
-  constexpr bool kKMx = kKMode == 3, kVMx = kVMode == 3;
-  __shared__ __align__(16) uint8_t s_codes[8192];
-  __shared__ __align__(16) uint8_t s_scales[1024];
+// Row t (token 0..127) of input page in_page of the bulk writer's
+// [pages * 128][hkv][128] input, for KV head h.
+struct WriterRows {
+  const uint16_t* src;
+  int in_page, hkv, h;
+  __device__ const uint16_t* operator()(int t) const {
+    return src + (((size_t)in_page * kPage + t) * hkv + h) * kD;
+  }
+};
 
+// Row t of the BF16 tail [128][128] of one (sequence, KV head), except row
+// 127, which is the token being appended.
+struct TailRows {
+  const uint16_t* tail;
+  const uint16_t* last;
+  __device__ const uint16_t* operator()(int t) const { return t == kPage - 1 ? last : tail + (size_t)t * kD; }
+};
+
+// Quantizes one (page, KV head) of K (is_v false) or V into cache block blk
+// (= physical page * hkv + h); rows(t) is the address of the page's row t
+// (128 bf16). All 256 threads of the workgroup call it (it has barriers).
+// kKMode / kVMode: 1 amax6, 2 four_six, 3 mxfp4_search.
+template <int kKMode, int kVMode, bool is_v, class Rows>
+__device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows, int h, size_t blk,
+                                          uint8_t* s_codes, uint8_t* s_scales) {
+  constexpr bool kKMx = kKMode == 3, kVMx = kVMode == 3;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int q = lane & 3;          // quarter of the row: elements [32q, 32q+32)
   const int n = lane >> 2;         // token within the 16-token tile
-  const int ph = blockIdx.x;       // input page * hkv + head
-  const bool is_v = blockIdx.y != 0;
-  const int in_page = ph / a.hkv, h = ph - in_page * a.hkv;
-  const int dst = a.page_ids[in_page];
-  if (dst < 0 || dst >= a.num_pages) return;
-  const size_t blk = (size_t)dst * a.hkv + h;
 
   float mu[32];
   if (!is_v && a.key_shift != nullptr) {
@@ -67,14 +80,12 @@ __global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
     for (int i = 0; i < 32; ++i) mu[i] = 0.0f;
   }
   const bool center = !is_v && a.key_shift != nullptr;
-  const uint16_t* src = is_v ? a.v : a.k;
 
 #pragma unroll 1
   for (int it = 0; it < 2; ++it) {
     const int tile = wave * 2 + it;
     const int t = tile * 16 + n;
-    const size_t row = ((size_t)in_page * kPage + t) * a.hkv + h;
-    const uint4* p = reinterpret_cast<const uint4*>(src + row * kD + 32 * q);
+    const uint4* p = reinterpret_cast<const uint4*>(rows(t) + 32 * q);
     uint4 w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) w[k] = p[k];
@@ -165,8 +176,67 @@ __global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
   }
 }
 
-hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
-  if (L.n_pages == 0) return hipSuccess;
+template <int kKMode, int kVMode>
+__global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
+  __shared__ __align__(16) uint8_t s_codes[8192];
+  __shared__ __align__(16) uint8_t s_scales[1024];
+  const int ph = blockIdx.x;       // input page * hkv + head
+  const bool is_v = blockIdx.y != 0;
+  const int in_page = ph / a.hkv, h = ph - in_page * a.hkv;
+  const int dst = a.page_ids[in_page];
+  if (dst < 0 || dst >= a.num_pages) return;
+  const WriterRows rows{is_v ? a.v : a.k, in_page, a.hkv, h};
+  if (is_v) page_head<kKMode, kVMode, true>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales);
+  else page_head<kKMode, kVMode, false>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales);
+}
+
+// Decode-time append with freeze-at-fill ("kv-landlords scripts/quant_ab.py"
+// PageSim: the hot page stays BF16 and is quantized once, when it fills).
+// Workgroup (sequence b, KV head h) of K (y = 0) or V (y = 1): the new row
+// goes to tail slot pos mod 128 (and to the sink when pos < sink_tokens);
+// when it fills slot 127, the workgroup quantizes the tail as one page into
+// block_tables[b][pos / 128], taking row 127 from the new row itself (the
+// tail rows 0..126 were written by earlier launches).
+struct AppendArgs {
+  WriterArgs w;                 // cache, key_shift, rotation, num_pages, hkv
+  const uint16_t* k_new;        // [B][hkv][128]
+  const uint16_t* v_new;
+  const int32_t* positions;     // [B]
+  const int32_t* block_tables;  // [B][max_pages_per_seq]
+  uint16_t* sink_k;             // [B][hkv][sink_tokens][128]
+  uint16_t* sink_v;
+  uint16_t* tail_k;             // [B][hkv][128][128]
+  uint16_t* tail_v;
+  int32_t max_pages_per_seq, sink_tokens;
+};
+
+template <int kKMode, int kVMode>
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+  __shared__ __align__(16) uint8_t s_codes[8192];
+  __shared__ __align__(16) uint8_t s_scales[1024];
+  const int hkv = a.w.hkv;
+  const int bh = blockIdx.x, b = bh / hkv, h = bh - b * hkv;
+  const bool is_v = blockIdx.y != 0;
+  const int pos = a.positions[b];
+  if (pos < 0 || pos >= kPage * a.max_pages_per_seq) return;   // padding row or past the block table
+  const int slot = pos & (kPage - 1);
+  const uint16_t* nrow = (is_v ? a.v_new : a.k_new) + (size_t)bh * kD;
+  uint16_t* tail = (is_v ? a.tail_v : a.tail_k) + (size_t)bh * kPage * kD;
+  if (threadIdx.x < 16) {
+    const uint4 w = reinterpret_cast<const uint4*>(nrow)[threadIdx.x];
+    reinterpret_cast<uint4*>(tail + (size_t)slot * kD)[threadIdx.x] = w;
+    if (pos < a.sink_tokens)
+      reinterpret_cast<uint4*>((is_v ? a.sink_v : a.sink_k) + ((size_t)bh * a.sink_tokens + pos) * kD)[threadIdx.x] = w;
+  }
+  if (slot != kPage - 1) return;
+  const int dst = a.block_tables[(size_t)b * a.max_pages_per_seq + pos / kPage];
+  if (dst < 0 || dst >= a.w.num_pages) return;
+  const TailRows rows{tail, nrow};
+  if (is_v) page_head<kKMode, kVMode, true>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales);
+  else page_head<kKMode, kVMode, false>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales);
+}
+
+static WriterArgs writer_args(const WriterLaunch& L) {
   WriterArgs a;
   a.k = static_cast<const uint16_t*>(L.k);
   a.v = static_cast<const uint16_t*>(L.v);
@@ -180,6 +250,12 @@ hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
   a.hkv = L.hkv;
   a.n_pages = L.n_pages;
   a.rotation = L.rotation;
+  return a;
+}
+
+hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
+  if (L.n_pages == 0) return hipSuccess;
+  const WriterArgs a = writer_args(L);
   const dim3 grid((unsigned)(L.n_pages * L.hkv), 2u), block(256u);
   if (L.k_mode == 2 && L.v_mode == 1)
     hipLaunchKernelGGL((writer_kernel<2, 1>), grid, block, 0, stream, a);
@@ -187,6 +263,33 @@ hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
     hipLaunchKernelGGL((writer_kernel<1, 1>), grid, block, 0, stream, a);
   else if (L.k_mode == 3 && L.v_mode == 3)
     hipLaunchKernelGGL((writer_kernel<3, 3>), grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendLaunch& L, hipStream_t stream) {
+  if (L.batch == 0) return hipSuccess;
+  AppendArgs a;
+  a.w = writer_args(L.w);
+  a.k_new = static_cast<const uint16_t*>(L.k_new);
+  a.v_new = static_cast<const uint16_t*>(L.v_new);
+  a.positions = L.positions;
+  a.block_tables = L.block_tables;
+  a.sink_k = static_cast<uint16_t*>(L.sink_k);
+  a.sink_v = static_cast<uint16_t*>(L.sink_v);
+  a.tail_k = static_cast<uint16_t*>(L.tail_k);
+  a.tail_v = static_cast<uint16_t*>(L.tail_v);
+  a.max_pages_per_seq = L.max_pages_per_seq;
+  a.sink_tokens = L.sink_tokens;
+  const dim3 grid((unsigned)(L.batch * L.w.hkv), 2u), block(256u);
+  const int km = L.w.k_mode, vm = L.w.v_mode;
+  if (km == 2 && vm == 1)
+    hipLaunchKernelGGL((append_kernel<2, 1>), grid, block, 0, stream, a);
+  else if (km == 1 && vm == 1)
+    hipLaunchKernelGGL((append_kernel<1, 1>), grid, block, 0, stream, a);
+  else if (km == 3 && vm == 3)
+    hipLaunchKernelGGL((append_kernel<3, 3>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

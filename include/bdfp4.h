@@ -151,6 +151,35 @@ bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cach
                                   const int32_t* page_ids, int32_t n_pages,
                                   const float* key_shift, void* stream);
 
+/* Decode-time append with freeze-at-fill ("kv-landlords scripts/quant_ab.py"
+ * PageSim: the hot page stays BF16 and is quantized once, when it fills;
+ * "BitDecoding-FP4 evaluation/config.py" KV_MODES "sink_tokens": 16). One new
+ * token per sequence, at 0-based position positions[b] (device int32 [batch]):
+ *   k_new, v_new:  bf16 [batch][num_kv_heads][128], 16-byte aligned.
+ *   tail_k/v:      bf16 [batch][num_kv_heads][128][128] (the buffers
+ *                  bdfp4_decode_attention reads); the token goes to slot
+ *                  positions[b] mod 128.
+ *   sink_k/v:      bf16 [batch][num_kv_heads][sink_tokens][128]; a token with
+ *                  position < sink_tokens is also written at that index.
+ *                  May be NULL when sink_tokens = 0.
+ *   block_tables:  int32 [batch][max_pages_per_seq], as for the decode.
+ *   key_shift:     as for bdfp4_quantize_pages.
+ * The token that fills slot 127 freezes the page: its 128 tail rows (slots
+ * 0..126 written by earlier calls, slot 127 this one) are quantized exactly
+ * as bdfp4_quantize_pages quantizes a whole page, into physical page
+ * block_tables[b][positions[b] / 128]; a page outside [0, num_pages) is
+ * skipped (the tail is still written). Rows with positions[b] < 0 (padding)
+ * or >= 128 * max_pages_per_seq are skipped entirely. The caller advances
+ * its sequence lengths afterwards (the decode after this call uses
+ * L = positions[b] + 1). Sequences of one call must not share tail, sink or
+ * destination pages. batch = 0 is a no-op. */
+bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache,
+                                 const void* k_new, const void* v_new, int32_t batch,
+                                 const int32_t* positions, const int32_t* block_tables,
+                                 int32_t max_pages_per_seq, void* sink_k, void* sink_v,
+                                 void* tail_k, void* tail_v, const float* key_shift,
+                                 void* stream);
+
 /* Split plan of bdfp4_decode_attention (host). pages_per_partition (1 .. 4)
  * is the number of consecutive full pages one FP4 partition covers; 0 picks
  * it from (batch, num_kv_heads, max_seq_len) so that about 512 workgroups of

@@ -215,3 +215,24 @@ def test_stream_read_rejects_before_launch():
     assert L.bdfp4_stream_read(None, 4096, FAKE, ok_sink, 512, None) == bd.E_INVALID
     assert L.bdfp4_stream_read(FAKE + 8, 4096, FAKE, ok_sink, 512, None) == bd.E_INVALID    # misaligned source
     assert L.bdfp4_stream_read(FAKE, 4096, FAKE, ok_sink - 4, 512, None) == bd.E_INVALID    # sink too small
+
+
+def test_append_rejects_before_launch():
+    r = bd.recipe_default_nvfp4()
+    c = _cache()
+    L = bd.lib()
+
+    def call(r=r, batch=2, kn=FAKE, maxp=8, sink=FAKE, tail=FAKE, mu=FAKE, cache=c):
+        return L.bdfp4_append_tokens(ctypes.byref(r), ctypes.byref(cache), kn, FAKE, batch, FAKE, FAKE, maxp,
+                                     sink, sink, tail, tail, mu, None)
+    assert call(batch=0) == bd.OK                 # nothing to append: no launch
+    assert call(batch=-1) == bd.E_INVALID
+    assert call(maxp=0) == bd.E_INVALID
+    assert call(kn=None) == bd.E_INVALID
+    assert call(kn=FAKE + 8) == bd.E_INVALID      # misaligned token rows
+    assert call(sink=None) == bd.E_INVALID        # sink_tokens = 16 needs the sink buffers
+    assert call(tail=None) == bd.E_INVALID
+    assert call(mu=None) == bd.E_INVALID          # key smoothing needs the key means
+    assert call(r.replace(key_smoothing=0)) == bd.E_INVALID
+    assert call(r.replace(scale_mode_k=bd.SCALE_MXFP4_SEARCH)) == bd.E_UNSUPPORTED
+    assert call(cache=_cache(num_pages=0)) == bd.E_INVALID
