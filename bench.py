@@ -13,8 +13,10 @@ timing; all inputs are resident in HBM when the timed region starts.
 A step is one decode token through all 36 layers: 36 launches of
 bdfp4_decode_attention (each: two-term query quantization, QK^T over the FP4
 pages, partition softmax, P quantization, PV, BF16 sink partition and the
-split-K merge). The MXFP4 and BF16-KV arms and the page writer (131,072
-tokens x 8 heads prefill write) are timed the same way and reported beside it.
+split-K merge). The MXFP4 and BF16-KV arms, the page writer (131,072
+tokens x 8 heads prefill write) and the decode-time append (batch 1 and 64 x 8
+KV heads, inside a page and at the token that freezes one) are timed the same
+way and reported beside it.
 
 Prints one JSON line; run `python bench.py --help` for options.
 """
@@ -45,6 +47,7 @@ def parse():
     ap.add_argument("--ppp", type=int, default=0, help="pages per partition (0 = library plan)")
     ap.add_argument("--arms", default="nvfp4,mxfp4,bf16")
     ap.add_argument("--no-writer", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,6 +186,49 @@ def bench_writer(args, mx: bool):
     torch.cuda.empty_cache()
     return {"us": ms * 1e3, "us_kernel_events": per * 1e3, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
             "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def append_bytes(batch: int, hkv: int, fill: bool, mx: bool) -> int:
+    """Algorithmic HBM bytes of one append call: the new K and V rows read,
+    written to the tail (256 B each); a fill also reads the other 127 tail
+    rows and writes the page's codes and scales."""
+    b = batch * hkv * 2 * (256 + 256)
+    if fill:
+        b += batch * hkv * 2 * (127 * 256 + 8192 + (512 if mx else 1024))
+    return b
+
+
+def bench_append(args, batch: int):
+    """One decode-time append per call for `batch` sequences x 8 KV heads:
+    at a position inside a page (tail write only) and at the last slot of a
+    page (tail write plus freezing the page)."""
+    import torch
+
+    import fp4_kv_cache_nvfp4_amd as bd
+
+    hkv = 8
+    r = bd.recipe_default_nvfp4(tau=1.0)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    rows = lambda *s: torch.randn(*s, device="cuda", generator=g).to(torch.bfloat16)
+    cache = bd.PagedCache.allocate(r, batch * 4, hkv)
+    bt = torch.arange(batch * 4, device="cuda", dtype=torch.int32).reshape(batch, 4)
+    tk, tv = rows(batch, hkv, 128, 128), rows(batch, hkv, 128, 128)
+    sk, sv = rows(batch, hkv, 16, 128), rows(batch, hkv, 16, 128)
+    kn, vn = rows(batch, hkv, 128), rows(batch, hkv, 128)
+    mu = torch.randn(hkv, 128, device="cuda", generator=g)
+    out = {}
+    for name, p in (("tail", 200), ("fill", 255)):
+        pos = torch.full((batch,), p, device="cuda", dtype=torch.int32)
+        fn = lambda: bd.append_tokens(r, cache, kn, vn, pos, bt, sk, sv, tk, tv, mu)
+        # 20 calls captured in one graph per step, so the host's per-call
+        # cost (argument marshalling) stays out of the device time; repeated
+        # appends at one position rewrite the same bytes
+        reps = 20
+        ms, per, _, med = time_launches([fn] * reps, max(args.steps, 20), 5, graph=True)
+        us = ms * 1e3 / reps
+        nb = append_bytes(batch, hkv, name == "fill", False)
+        out[name] = {"us": round(us, 3), "bytes": nb, "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+    return out
 
 
 def cpu_baseline(args):
@@ -355,6 +401,11 @@ def main():
             writer["mxfp4" if mx else "nvfp4"] = bench_writer(args, mx)
             print(f"[bench] writer {'mxfp4' if mx else 'nvfp4'}: {writer['mxfp4' if mx else 'nvfp4']['us']:.1f} us",
                   file=sys.stderr, flush=True)
+    append = {}
+    if not args.no_append:
+        for batch in (1, 64):
+            append[f"batch{batch}"] = bench_append(args, batch)
+            print(f"[bench] append batch {batch}: {append[f'batch{batch}']}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -394,6 +445,7 @@ def main():
         "cpu_baseline": cpu,
         "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
         "writer_131072x8": writer,
+        "append_x8_heads": append,
     }
     print(json.dumps(line))
 
