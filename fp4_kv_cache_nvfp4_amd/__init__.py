@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
         "bdfp4_cache_bytes": [RP, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "bdfp4_quantize_pages": [RP, CP, P, P, P, I32, P, P],
         "bdfp4_append_tokens": [RP, CP, P, P, I32, P, P, I32, P, P, P, P, P, P],
+        "bdfp4_key_means_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
+        "bdfp4_key_means": [P, I32, I32, P, SZ, P, P],
+        "bdfp4_error_sums": [P, P, ctypes.c_int64, P, P],
         "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
         "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
@@ -205,6 +208,58 @@ def append_tokens(r: Recipe, cache: PagedCache, k_new, v_new, positions, block_t
                                      _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
                                      _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v), _ptr(key_shift),
                                      _stream(stream)))
+
+
+# ---------------------------------------------------------------- calibration
+
+def key_means(k, num_kv_heads: int, stream=None):
+    """float32 [Hkv, 128] device tensor of the key means of k [T, Hkv, 128]
+    bf16 (the key-smoothing shift); the scratch is a torch allocation."""
+    import torch
+    tokens = int(k.shape[0])
+    need = ctypes.c_size_t()
+    _check(lib().bdfp4_key_means_workspace_size(tokens, num_kv_heads, ctypes.byref(need)))
+    ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=k.device)
+    mu = torch.empty((num_kv_heads, 128), dtype=torch.float32, device=k.device)
+    _check(lib().bdfp4_key_means(_ptr(k), tokens, num_kv_heads, _ptr(ws), need.value, _ptr(mu), _stream(stream)))
+    return mu
+
+
+def error_sums(got, ref, out, stream=None) -> None:
+    """out (float64 device, 2 values) = [sum (got - ref)^2, sum ref^2]."""
+    _check(lib().bdfp4_error_sums(_ptr(got), _ptr(ref), int(ref.numel()), _ptr(out), _stream(stream)))
+
+
+def calibrate_tau(r: Recipe, candidates, reference, decode_args: dict, stream=None):
+    """The tau search: for each candidate, the FP4 decode (decode_attention
+    with decode_args) and the error sums of its output against `reference`
+    (exact attention of the same calibration batch, e.g. from
+    bf16_decode_attention), all on the device; one copy of the sums to the
+    host at the end. Returns (best tau, relative L2 error per candidate);
+    equal errors keep the earlier candidate."""
+    import torch
+    sums = torch.zeros((len(candidates), 2), dtype=torch.float64, device=reference.device)
+    out = torch.empty_like(reference)
+    for i, t in enumerate(candidates):
+        decode_attention(r.replace(tau=float(t)), out=out, stream=stream, **decode_args)
+        error_sums(out, reference, sums[i], stream)
+    s = sums.cpu().numpy()
+    errs = [math.sqrt(a / b) for a, b in s]
+    best = min(range(len(errs)), key=lambda i: (errs[i], i))
+    return float(candidates[best]), errs
+
+
+def save_key_means(path: str, means: dict) -> None:
+    """Key-mean sidecar: {name: float32 [Hkv, 128] host array} to a
+    safetensors file (host I/O only)."""
+    import numpy as np
+    from safetensors.numpy import save_file
+    save_file({k: np.ascontiguousarray(v, dtype=np.float32) for k, v in means.items()}, path)
+
+
+def load_key_means(path: str) -> dict:
+    from safetensors.numpy import load_file
+    return load_file(path)
 
 
 # ---------------------------------------------------------------- decode

@@ -23,7 +23,7 @@ LIB = os.path.join(LIBDIR, "libbdfp4.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "writer.hip", "decode.hip", "bf16_decode.hip", "stream.hip"]
+SOURCES = ["api.cpp", "writer.hip", "decode.hip", "bf16_decode.hip", "stream.hip", "calib.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

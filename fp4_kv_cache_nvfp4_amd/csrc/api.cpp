@@ -303,6 +303,38 @@ bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache
   return hip_status(bdfp4::launch_append(L, static_cast<hipStream_t>(stream)), "append launch");
 }
 
+bdfp4_status bdfp4_key_means_workspace_size(int32_t tokens, int32_t num_kv_heads, size_t* bytes) {
+  if (!bytes) return fail(BDFP4_E_INVALID, "NULL output");
+  if (tokens < 1) return fail(BDFP4_E_INVALID, "tokens must be >= 1");
+  if (num_kv_heads < 1 || num_kv_heads > 65535) return fail(BDFP4_E_INVALID, "num_kv_heads must be in [1, 65535]");
+  *bytes = bdfp4::key_means_workspace_bytes(tokens, num_kv_heads);
+  return ok();
+}
+
+bdfp4_status bdfp4_key_means(const void* k_bf16, int32_t tokens, int32_t num_kv_heads, void* workspace,
+                             size_t workspace_bytes, float* mu_out, void* stream) {
+  size_t need = 0;
+  bdfp4_status s = bdfp4_key_means_workspace_size(tokens, num_kv_heads, &need);
+  if (s != BDFP4_OK) return s;
+  if (!k_bf16 || !workspace || !mu_out) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (!aligned16(k_bf16) || !aligned16(workspace) || !aligned16(mu_out))
+    return fail(BDFP4_E_INVALID, "keys, workspace and output must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BDFP4_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(bdfp4::launch_key_means(k_bf16, tokens, num_kv_heads, workspace, mu_out,
+                                            static_cast<hipStream_t>(stream)),
+                    "key means launch");
+}
+
+bdfp4_status bdfp4_error_sums(const float* got, const float* ref, int64_t n, double* sums_out, void* stream) {
+  if (n < 0 || n > ((int64_t)1 << 31)) return fail(BDFP4_E_INVALID, "n must be in [0, 2^31]");
+  if (!sums_out || (n > 0 && (!got || !ref))) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (((uintptr_t)got & 3) || ((uintptr_t)ref & 3) || ((uintptr_t)sums_out & 7))
+    return fail(BDFP4_E_INVALID, "misaligned pointer");
+  return hip_status(bdfp4::launch_error_sums(got, ref, n, sums_out, static_cast<hipStream_t>(stream)),
+                    "error sums launch");
+}
+
 bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                int32_t pages_per_partition, int32_t* ppp_out, int32_t* parts_out) {
   if (!ppp_out || !parts_out) return fail(BDFP4_E_INVALID, "NULL output");

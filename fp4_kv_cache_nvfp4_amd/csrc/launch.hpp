@@ -38,6 +38,13 @@ struct AppendLaunch {
 
 hipError_t launch_append(const AppendLaunch& L, hipStream_t stream);
 
+// Calibration: per-(KV head, channel) key means of tokens x hkv bf16 rows
+// (two passes through a float64 workspace of key_means_workspace_bytes), and
+// float64 error sums [sum (got - ref)^2, sum ref^2] over n floats.
+size_t key_means_workspace_bytes(int tokens, int hkv);
+hipError_t launch_key_means(const void* k, int tokens, int hkv, void* workspace, float* mu, hipStream_t stream);
+hipError_t launch_error_sums(const float* got, const float* ref, int64_t n, double* out, hipStream_t stream);
+
 hipError_t launch_rows(const void* rows, int n_rows, const float* shift, int rotation, int mode,
                        int terms, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 

@@ -180,6 +180,33 @@ bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache
                                  void* tail_k, void* tail_v, const float* key_shift,
                                  void* stream);
 
+/* Calibration of the key means ("BitDecoding-FP4 evaluation/config.py",
+ * RECIPE outlier_aware_key_quantization: key smoothing with a static key
+ * shift, created by a calibration pass when missing). mu_out[h][c] (float32
+ * [num_kv_heads][128], device) = the mean over the calibration tokens of
+ * float32(k[t][h][c]), summed in float64 in a fixed order (results do not
+ * depend on scheduling) and rounded to float32 once.
+ *   k_bf16:    [tokens][num_kv_heads][128] bf16, the rows bdfp4_quantize_pages
+ *              takes; 16-byte aligned.
+ *   workspace: device scratch of bdfp4_key_means_workspace_size bytes (no
+ *              initialization needed; contents undefined afterwards).
+ * E_INVALID for tokens < 1, num_kv_heads outside [1, 65535], NULL or
+ * misaligned pointers; E_WORKSPACE for a short workspace. */
+bdfp4_status bdfp4_key_means_workspace_size(int32_t tokens, int32_t num_kv_heads, size_t* bytes);
+bdfp4_status bdfp4_key_means(const void* k_bf16, int32_t tokens, int32_t num_kv_heads,
+                             void* workspace, size_t workspace_bytes, float* mu_out,
+                             void* stream);
+
+/* Error sums for calibration and diagnostics: sums_out[0] = sum over i < n
+ * of (got[i] - ref[i])^2 and sums_out[1] = sum of ref[i]^2, in float64 in a
+ * fixed order (device pointers; sums_out 8-byte aligned, two doubles). The
+ * tau search ("calibrate" in probability_environment) compares decode
+ * outputs for candidate taus with exact attention through these sums.
+ * n in [0, 2^31] (got and ref may be NULL when n = 0, which writes two
+ * zeros); one workgroup, meant for outputs and small tensors. */
+bdfp4_status bdfp4_error_sums(const float* got, const float* ref, int64_t n, double* sums_out,
+                              void* stream);
+
 /* Split plan of bdfp4_decode_attention (host). pages_per_partition (1 .. 4)
  * is the number of consecutive full pages one FP4 partition covers; 0 picks
  * it from (batch, num_kv_heads, max_seq_len) so that about 512 workgroups of

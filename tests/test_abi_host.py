@@ -236,3 +236,30 @@ def test_append_rejects_before_launch():
     assert call(r.replace(key_smoothing=0)) == bd.E_INVALID
     assert call(r.replace(scale_mode_k=bd.SCALE_MXFP4_SEARCH)) == bd.E_UNSUPPORTED
     assert call(cache=_cache(num_pages=0)) == bd.E_INVALID
+
+
+def test_calibration_entries_reject_before_launch():
+    L = bd.lib()
+    n = ctypes.c_size_t()
+    assert L.bdfp4_key_means_workspace_size(131072, 8, ctypes.byref(n)) == bd.OK
+    assert n.value == 512 * 8 * 128 * 8                    # float64 sums per 256-token chunk
+    assert L.bdfp4_key_means_workspace_size(0, 8, ctypes.byref(n)) == bd.E_INVALID
+    assert L.bdfp4_key_means_workspace_size(16, 0, ctypes.byref(n)) == bd.E_INVALID
+    assert L.bdfp4_key_means(FAKE, 1000, 2, FAKE, 16, FAKE, None) == bd.E_WORKSPACE
+    assert L.bdfp4_key_means(None, 1000, 2, FAKE, 1 << 20, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_key_means(FAKE + 8, 1000, 2, FAKE, 1 << 20, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_error_sums(FAKE, FAKE, -1, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_error_sums(FAKE, None, 16, FAKE, None) == bd.E_INVALID
+    assert L.bdfp4_error_sums(FAKE, FAKE, 16, None, None) == bd.E_INVALID
+    assert L.bdfp4_error_sums(FAKE, FAKE, 16, FAKE + 4, None) == bd.E_INVALID
+
+
+def test_key_mean_sidecar_round_trip(tmp_path):
+    import numpy as np
+    rng = np.random.default_rng(3)
+    means = {f"layer.{i}.key_shift": rng.standard_normal((8, 128)).astype(np.float32) for i in range(3)}
+    p = str(tmp_path / "key_means.safetensors")
+    bd.save_key_means(p, means)
+    back = bd.load_key_means(p)
+    assert sorted(back) == sorted(means)
+    assert all(np.array_equal(back[k], means[k]) and back[k].dtype == np.float32 for k in means)
