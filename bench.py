@@ -15,8 +15,9 @@ bdfp4_decode_attention (each: two-term query quantization, QK^T over the FP4
 pages, partition softmax, P quantization, PV, BF16 sink partition and the
 split-K merge). The MXFP4 and BF16-KV arms, the page writer (131,072
 tokens x 8 heads prefill write) and the decode-time append (batch 1 and 64 x 8
-KV heads, inside a page and at the token that freezes one) are timed the same
-way and reported beside it.
+KV heads, inside a page and at the token that freezes one) and the key-mean
+calibration over the prefill keys are timed the same way and reported beside
+it.
 
 Prints one JSON line; run `python bench.py --help` for options.
 """
@@ -48,6 +49,7 @@ def parse():
     ap.add_argument("--arms", default="nvfp4,mxfp4,bf16")
     ap.add_argument("--no-writer", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -231,6 +233,29 @@ def bench_append(args, batch: int):
     return out
 
 
+def bench_key_means(args):
+    """Key-mean calibration over the 131,072-token x 8-head prefill keys
+    (the writer's input): bytes = the bf16 keys read once."""
+    import torch
+
+    import fp4_kv_cache_nvfp4_amd as bd
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    w = synth.torch_write_rows(0)
+    k = w["k"]
+    tokens = int(k.shape[0])
+    need = bd.key_means_workspace_size(tokens, 8)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    mu = torch.empty((8, 128), dtype=torch.float32, device="cuda")
+    fn = lambda: bd.key_means_into(k, 8, ws, mu)
+    ms, per, _, med = time_launches([fn], max(args.steps, 10), 3)
+    nbytes = tokens * 8 * 128 * 2
+    del w, k
+    torch.cuda.empty_cache()
+    return {"us": round(ms * 1e3, 3), "bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(args):
     """The oracle (numpy) decode on a bounded sample of the same workload:
     one layer, 2 of the 8 KV heads (8 query heads), the full 131,072-token
@@ -406,6 +431,10 @@ def main():
         for batch in (1, 64):
             append[f"batch{batch}"] = bench_append(args, batch)
             print(f"[bench] append batch {batch}: {append[f'batch{batch}']}", file=sys.stderr, flush=True)
+    calibration = None
+    if not args.no_calibration:
+        calibration = {"key_means_131072x8": bench_key_means(args)}
+        print(f"[bench] key means: {calibration}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -446,6 +475,7 @@ def main():
         "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
         "writer_131072x8": writer,
         "append_x8_heads": append,
+        "calibration": calibration,
     }
     print(json.dumps(line))
 

@@ -212,6 +212,19 @@ def append_tokens(r: Recipe, cache: PagedCache, k_new, v_new, positions, block_t
 
 # ---------------------------------------------------------------- calibration
 
+def key_means_workspace_size(tokens: int, num_kv_heads: int) -> int:
+    need = ctypes.c_size_t()
+    _check(lib().bdfp4_key_means_workspace_size(tokens, num_kv_heads, ctypes.byref(need)))
+    return need.value
+
+
+def key_means_into(k, num_kv_heads: int, workspace, mu, stream=None) -> None:
+    """mu (float32 [Hkv, 128], device) = the key means of k [T, Hkv, 128] bf16,
+    with a caller-given scratch of key_means_workspace_size bytes."""
+    _check(lib().bdfp4_key_means(_ptr(k), int(k.shape[0]), num_kv_heads, _ptr(workspace),
+                                 int(workspace.numel() * workspace.element_size()), _ptr(mu), _stream(stream)))
+
+
 def key_means(k, num_kv_heads: int, stream=None):
     """float32 [Hkv, 128] device tensor of the key means of k [T, Hkv, 128]
     bf16 (the key-smoothing shift); the scratch is a torch allocation."""

@@ -17,12 +17,17 @@ namespace bdfp4 {
 
 namespace {
 
-constexpr int kMeanChunk = 256;   // tokens per workgroup of the first pass
+constexpr int kMeanChunk = 2048;  // tokens per workgroup of the first pass
+constexpr int kRound = 16;        // loads in flight per thread
 
-// Pass 1: workgroup (chunk c, head h) sums tokens [256 c, 256 c + 256) of
+// The sums start from +0.0 and absent entries add +0.0, as the plain sum
+// 0 + x_0 + x_1 + ... does (a channel of zeros of either sign sums to +0.0).
+
+// Pass 1: workgroup (chunk c, head h) sums tokens [2048 c, 2048 c + 2048) of
 // head h. Thread (r = tid >> 4, octet o = tid & 15) takes channels 8 o .. 8 o
-// + 7 of tokens 256 c + r + 16 k (k = 0..15, in order), one 16-byte load per
-// token; the 16 token lanes of a channel are then added in lane order.
+// + 7 of tokens 2048 c + r + 16 k (k = 0..127, in order; 16 loads in flight
+// per round), one 16-byte load per token; the 16 token lanes of a channel are
+// then added in lane order.
 __global__ void __launch_bounds__(256) key_sum_kernel(const uint16_t* k, int tokens, int hkv, double* part) {
   __shared__ double s[16][128];
   const int c = blockIdx.x, h = blockIdx.y;
@@ -30,34 +35,48 @@ __global__ void __launch_bounds__(256) key_sum_kernel(const uint16_t* k, int tok
   double acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-  for (int kk = 0; kk < kMeanChunk / 16; ++kk) {
-    const int t = c * kMeanChunk + r + 16 * kk;
-    if (t >= tokens) break;
-    const uint4 w = *reinterpret_cast<const uint4*>(k + ((size_t)t * hkv + h) * kD + 8 * o);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int k0 = 0; k0 < kMeanChunk / 16; k0 += kRound) {
+    uint4 w[kRound];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += (double)__uint_as_float(ws[j] << 16);
-      acc[2 * j + 1] += (double)__uint_as_float(ws[j] & 0xFFFF0000u);
+    for (int kk = 0; kk < kRound; ++kk) {
+      const int t = c * kMeanChunk + r + 16 * (k0 + kk);
+      w[kk] = t < tokens ? *reinterpret_cast<const uint4*>(k + ((size_t)t * hkv + h) * kD + 8 * o)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kRound; ++kk) {
+      const uint32_t ws[4] = {w[kk].x, w[kk].y, w[kk].z, w[kk].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += (double)__uint_as_float(ws[j] << 16);
+        acc[2 * j + 1] += (double)__uint_as_float(ws[j] & 0xFFFF0000u);
+      }
     }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) s[r][8 * o + j] = acc[j];
   __syncthreads();
   if (threadIdx.x < kD) {
-    double v = s[0][threadIdx.x];
-    for (int i = 1; i < 16; ++i) v += s[i][threadIdx.x];
+    double v = 0.0;
+    for (int i = 0; i < 16; ++i) v += s[i][threadIdx.x];
     part[((size_t)c * hkv + h) * kD + threadIdx.x] = v;
   }
 }
 
-// Pass 2: thread (h, channel) adds the chunk sums in chunk order and rounds
-// the float64 mean to float32.
+// Pass 2: thread (h, channel) adds the chunk sums in chunk order (16 loads in
+// flight per round) and rounds the float64 mean to float32.
 __global__ void __launch_bounds__(128) key_mean_kernel(const double* part, int nchunks, int tokens, int hkv,
                                                        float* mu) {
   const int h = blockIdx.x, ch = threadIdx.x;
   double v = 0.0;
-  for (int c = 0; c < nchunks; ++c) v += part[((size_t)c * hkv + h) * kD + ch];
+  for (int c0 = 0; c0 < nchunks; c0 += kRound) {
+    double x[kRound];
+#pragma unroll
+    for (int j = 0; j < kRound; ++j)
+      x[j] = c0 + j < nchunks ? part[((size_t)(c0 + j) * hkv + h) * kD + ch] : 0.0;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) v += x[j];
+  }
   mu[h * kD + ch] = (float)(v / (double)tokens);
 }
 

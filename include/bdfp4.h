@@ -185,7 +185,8 @@ bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache
  * shift, created by a calibration pass when missing). mu_out[h][c] (float32
  * [num_kv_heads][128], device) = the mean over the calibration tokens of
  * float32(k[t][h][c]), summed in float64 in a fixed order (results do not
- * depend on scheduling) and rounded to float32 once.
+ * depend on scheduling; the sum starts from +0.0, so zeros of either sign
+ * give +0.0) and rounded to float32 once.
  *   k_bf16:    [tokens][num_kv_heads][128] bf16, the rows bdfp4_quantize_pages
  *              takes; 16-byte aligned.
  *   workspace: device scratch of bdfp4_key_means_workspace_size bytes (no

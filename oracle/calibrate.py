@@ -28,7 +28,8 @@ from .formats import bf16_to_f32
 def key_means(k_bf16: np.ndarray) -> np.ndarray:
     """k_bf16: uint16 [T, Hkv, 128] calibration keys -> float32 [Hkv, 128]."""
     x = bf16_to_f32(k_bf16).astype(np.float64)
-    return (x.sum(axis=0) / x.shape[0]).astype(np.float32)
+    # the plain sum 0 + x_0 + x_1 + ...: it starts from +0.0
+    return (x.sum(axis=0, initial=0.0) / x.shape[0]).astype(np.float32)
 
 
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:

@@ -242,7 +242,7 @@ def test_calibration_entries_reject_before_launch():
     L = bd.lib()
     n = ctypes.c_size_t()
     assert L.bdfp4_key_means_workspace_size(131072, 8, ctypes.byref(n)) == bd.OK
-    assert n.value == 512 * 8 * 128 * 8                    # float64 sums per 256-token chunk
+    assert n.value == 64 * 8 * 128 * 8                     # float64 sums per 2048-token chunk
     assert L.bdfp4_key_means_workspace_size(0, 8, ctypes.byref(n)) == bd.E_INVALID
     assert L.bdfp4_key_means_workspace_size(16, 0, ctypes.byref(n)) == bd.E_INVALID
     assert L.bdfp4_key_means(FAKE, 1000, 2, FAKE, 16, FAKE, None) == bd.E_WORKSPACE

@@ -27,17 +27,21 @@ def test_key_means_bit_exact(tokens, hkv):
     rng = np.random.default_rng(tokens)
     x = rng.standard_normal((tokens, hkv, 128)).astype(np.float32)
     x[:, :, 11] += 9.0                                  # an outlier channel with a large mean
+    x[:, 0, 20] = -0.0                                  # zeros of either sign sum to +0.0
+    x[:, 0, 21] = 0.0
     k = synth.f32_to_bf16(x)
     mu = bd.key_means(dev_bf16(k), hkv)
     torch.cuda.synchronize()
-    assert np.array_equal(mu.cpu().numpy(), OC.key_means(k))
+    want = OC.key_means(k)
+    assert not np.signbit(want[0, 20]) and not np.signbit(want[0, 21])
+    assert np.array_equal(mu.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
 def test_key_means_full_prefill_bit_exact():
     w = synth.torch_write_rows(0)                       # 131,072 tokens x 8 heads, on the device
     mu = bd.key_means(w["k"], 8)
     torch.cuda.synchronize()
-    assert np.array_equal(mu.cpu().numpy(), OC.key_means(_u16(w["k"])))
+    assert np.array_equal(mu.cpu().numpy().view(np.uint32), OC.key_means(_u16(w["k"])).view(np.uint32))
 
 
 def test_error_sums_match_float64():
