@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         "bdfp4_key_means_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_key_means": [P, I32, I32, P, SZ, P, P],
         "bdfp4_error_sums": [P, P, ctypes.c_int64, P, P],
+        "bdfp4_page_errors_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
+        "bdfp4_page_errors": [RP, CP, P, P, P, I32, P, P, SZ, P, P],
         "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
         "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
@@ -260,6 +262,21 @@ def calibrate_tau(r: Recipe, candidates, reference, decode_args: dict, stream=No
     errs = [math.sqrt(a / b) for a, b in s]
     best = min(range(len(errs)), key=lambda i: (errs[i], i))
     return float(candidates[best]), errs
+
+
+def page_errors(r: Recipe, cache: PagedCache, k, v, page_ids, key_shift=None, stream=None):
+    """Device float64 [4] = [sum (k_hat - y)^2, sum y^2, sum (v_hat - v)^2,
+    sum v^2] of the pages quantize_pages wrote from these arguments."""
+    import torch
+    n_pages = int(page_ids.numel())
+    need = ctypes.c_size_t()
+    _check(lib().bdfp4_page_errors_workspace_size(n_pages, cache.num_kv_heads, ctypes.byref(need)))
+    ws = torch.empty(need.value, dtype=torch.uint8, device=k.device)
+    out = torch.empty(4, dtype=torch.float64, device=k.device)
+    c = cache.struct()
+    _check(lib().bdfp4_page_errors(ctypes.byref(r), ctypes.byref(c), _ptr(k), _ptr(v), _ptr(page_ids), n_pages,
+                                   _ptr(key_shift), _ptr(ws), need.value, _ptr(out), _stream(stream)))
+    return out
 
 
 def save_key_means(path: str, means: dict) -> None:

@@ -335,6 +335,51 @@ bdfp4_status bdfp4_error_sums(const float* got, const float* ref, int64_t n, dou
                     "error sums launch");
 }
 
+bdfp4_status bdfp4_page_errors_workspace_size(int32_t n_pages, int32_t num_kv_heads, size_t* bytes) {
+  if (!bytes) return fail(BDFP4_E_INVALID, "NULL output");
+  if (n_pages < 1 || num_kv_heads < 1 || (int64_t)n_pages * num_kv_heads > 0x7FFFFFFF)
+    return fail(BDFP4_E_INVALID, "n_pages and num_kv_heads must be >= 1 (product < 2^31)");
+  *bytes = bdfp4::page_errors_workspace_bytes(n_pages, num_kv_heads);
+  return ok();
+}
+
+bdfp4_status bdfp4_page_errors(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* k_bf16,
+                               const void* v_bf16, const int32_t* page_ids, int32_t n_pages,
+                               const float* key_shift, void* workspace, size_t workspace_bytes,
+                               double* sums_out, void* stream) {
+  bdfp4_status s = check_kv_recipe(r);
+  if (s != BDFP4_OK) return s;
+  if ((s = check_cache(cache)) != BDFP4_OK) return s;
+  size_t need = 0;
+  if ((s = bdfp4_page_errors_workspace_size(n_pages, cache->num_kv_heads, &need)) != BDFP4_OK) return s;
+  if (!k_bf16 || !v_bf16 || !page_ids || !workspace || !sums_out) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(workspace) || ((uintptr_t)sums_out & 7))
+    return fail(BDFP4_E_INVALID, "misaligned pointer");
+  if (r->key_smoothing && key_shift == nullptr)
+    return fail(BDFP4_E_INVALID, "key_smoothing needs key_shift (the key-mean sidecar)");
+  if (!r->key_smoothing && key_shift != nullptr)
+    return fail(BDFP4_E_INVALID, "key_shift given but key_smoothing is off");
+  if (workspace_bytes < need)
+    return fail(BDFP4_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  bdfp4::WriterLaunch L;
+  L.k = k_bf16;
+  L.v = v_bf16;
+  L.page_ids = page_ids;
+  L.key_shift = key_shift;
+  L.k_codes = cache->k_codes;
+  L.k_scales = cache->k_scales;
+  L.v_codes = cache->v_codes;
+  L.v_scales = cache->v_scales;
+  L.num_pages = cache->num_pages;
+  L.hkv = cache->num_kv_heads;
+  L.n_pages = n_pages;
+  L.rotation = r->rotation;
+  L.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
+  L.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
+  return hip_status(bdfp4::launch_page_errors(L, workspace, sums_out, static_cast<hipStream_t>(stream)),
+                    "page errors launch");
+}
+
 bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                int32_t pages_per_partition, int32_t* ppp_out, int32_t* parts_out) {
   if (!ppp_out || !parts_out) return fail(BDFP4_E_INVALID, "NULL output");

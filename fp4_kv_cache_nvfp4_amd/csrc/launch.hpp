@@ -38,6 +38,12 @@ struct AppendLaunch {
 
 hipError_t launch_append(const AppendLaunch& L, hipStream_t stream);
 
+// Quantization diagnostics over n_pages written pages (L as for the writer):
+// out (device double[4]) = [sum (k_hat - y)^2, sum y^2, sum (v_hat - v)^2,
+// sum v^2], through a float64 workspace of page_errors_workspace_bytes.
+size_t page_errors_workspace_bytes(int n_pages, int hkv);
+hipError_t launch_page_errors(const WriterLaunch& L, void* workspace, double* out, hipStream_t stream);
+
 // Calibration: per-(KV head, channel) key means of tokens x hkv bf16 rows
 // (two passes through a float64 workspace of key_means_workspace_bytes), and
 // float64 error sums [sum (got - ref)^2, sum ref^2] over n floats.

@@ -236,6 +236,146 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   else page_head<kKMode, kVMode, false>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales);
 }
 
+// Quantization diagnostics ("kv-landlords scripts/quant_ab.py" compares cache
+// schemes by reconstruction error): workgroup (input page, head) of K (y = 0)
+// or V (y = 1) recomputes the float32 rows that were quantized (keys centered
+// and rotated exactly as page_head does, values as they are), dequantizes
+// the stored page through the byte layout of the cache (codes and scales
+// staged in LDS) and adds (x_hat - x)^2 and x^2 in float64: thread sums in
+// element order, then a fixed tree. part[y][page-head][2] holds the sums.
+__device__ __forceinline__ double e2m1_f64(uint32_t nib) {
+  const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double m = mag[nib & 7u];
+  return (nib & 8u) ? -m : m;
+}
+
+template <bool kMx>
+__device__ __forceinline__ double scale_f64(uint32_t code) {
+  if (kMx) return ldexp(1.0, (int)code - 127);              // E8M0
+  return (double)e4m3_value(code);                          // E4M3 (exact in float32)
+}
+
+template <bool kKMx, bool kVMx, bool is_v>
+__device__ __forceinline__ void page_error(const WriterArgs& a, int in_page, int h, size_t blk, uint8_t* s_codes,
+                                           uint8_t* s_scales, double& err, double& ref) {
+  constexpr bool kMx = is_v ? kVMx : kKMx;
+  constexpr int sbytes = kMx ? 512 : 1024;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 3, n = lane >> 2;
+  const uint4* codes = reinterpret_cast<const uint4*>((is_v ? a.v_codes : a.k_codes) + blk * 8192);
+  const uint4* scales = reinterpret_cast<const uint4*>((is_v ? a.v_scales : a.k_scales) + blk * sbytes);
+  reinterpret_cast<uint4*>(s_codes)[tid] = codes[tid];
+  reinterpret_cast<uint4*>(s_codes)[tid + 256] = codes[tid + 256];
+  if (tid * 16 < sbytes) reinterpret_cast<uint4*>(s_scales)[tid] = scales[tid];
+  float mu[32];
+  const bool center = !is_v && a.key_shift != nullptr;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mu[i] = center ? a.key_shift[h * kD + 32 * q + i] : 0.0f;
+  __syncthreads();
+  const WriterRows rows{is_v ? a.v : a.k, in_page, a.hkv, h};
+#pragma unroll 1
+  for (int it = 0; it < 2; ++it) {
+    const int t = (wave * 2 + it) * 16 + n;
+    const uint4* p = reinterpret_cast<const uint4*>(rows(t) + 32 * q);
+    uint4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = p[k];
+    float x[32];
+    widen32(w, x);
+    if (!is_v) {
+      if (center) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = __fsub_rn(x[i], mu[i]);
+      }
+      if (a.rotation) rotate_row_quad(x, q);
+    }
+#pragma unroll 4
+    for (int e = 0; e < 32; ++e) {
+      const int d = 32 * q + e;
+      int cb, sb, shift;
+      if (!is_v) {
+        cb = (t >> 4) * 1024 + (d >> 5) * 256 + (t & 15) * 16 + ((d & 31) >> 1);
+        shift = 4 * (d & 1);
+        sb = kMx ? ((d >> 5) * 16 + (t & 15)) * 8 + (t >> 4)
+                 : ((((d >> 4) >> 1) * 16 + (t & 15)) * 8 + (t >> 4)) * 2 + ((d >> 4) & 1);
+      } else {
+        const int g = (t >> 5) * 4 + ((t >> 3) & 3);
+        if (kMx) {
+          cb = ((g * 16 + (d >> 3)) * 8 + (t & 7)) * 4 + ((d & 7) >> 1);
+          shift = 4 * (d & 1);
+          sb = (g * 4 + (d >> 5)) * 8 + (t & 7);
+        } else {
+          cb = (t >> 5) * 2048 + (((t >> 3) & 3) * 16 + (d >> 3)) * 32 + (d & 7) * 4 + ((t & 7) >> 1);
+          shift = 4 * (t & 1);
+          sb = (g * 8 + (d >> 4)) * 8 + (t & 7);
+        }
+      }
+      const double xh = e2m1_f64(((uint32_t)s_codes[cb] >> shift) & 15u) * scale_f64<kMx>(s_scales[sb]);
+      const double xv = (double)x[e];
+      err = fma(xh - xv, xh - xv, err);
+      ref = fma(xv, xv, ref);
+    }
+  }
+}
+
+template <bool kKMx, bool kVMx>
+__global__ void __launch_bounds__(256) page_error_kernel(WriterArgs a, double* part) {
+  __shared__ __align__(16) uint8_t s_codes[8192];
+  __shared__ __align__(16) uint8_t s_scales[1024];
+  __shared__ double s_e[256], s_r[256];
+  const int ph = blockIdx.x;
+  const bool is_v = blockIdx.y != 0;
+  const int in_page = ph / a.hkv, h = ph - in_page * a.hkv;
+  const int dst = a.page_ids[in_page];
+  double err = 0.0, ref = 0.0;
+  if (dst >= 0 && dst < a.num_pages) {
+    const size_t blk = (size_t)dst * a.hkv + h;
+    if (is_v) page_error<kKMx, kVMx, true>(a, in_page, h, blk, s_codes, s_scales, err, ref);
+    else page_error<kKMx, kVMx, false>(a, in_page, h, blk, s_codes, s_scales, err, ref);
+  }
+  s_e[threadIdx.x] = err;
+  s_r[threadIdx.x] = ref;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      s_e[threadIdx.x] += s_e[threadIdx.x + w];
+      s_r[threadIdx.x] += s_r[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double* o = part + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 2;
+    o[0] = s_e[0];
+    o[1] = s_r[0];
+  }
+}
+
+// out[2 y + c] = sum over page-heads i of part[y][i][c]: thread t adds
+// i = t, t + 256, ... in order, then a fixed tree (workgroup y).
+__global__ void __launch_bounds__(256) page_error_total_kernel(const double* part, int n, double* out) {
+  __shared__ double s_e[256], s_r[256];
+  const double* py = part + (size_t)blockIdx.x * n * 2;
+  double e = 0.0, r = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    e += py[2 * i];
+    r += py[2 * i + 1];
+  }
+  s_e[threadIdx.x] = e;
+  s_r[threadIdx.x] = r;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      s_e[threadIdx.x] += s_e[threadIdx.x + w];
+      s_r[threadIdx.x] += s_r[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = s_e[0];
+    out[2 * blockIdx.x + 1] = s_r[0];
+  }
+}
+
 static WriterArgs writer_args(const WriterLaunch& L) {
   WriterArgs a;
   a.k = static_cast<const uint16_t*>(L.k);
@@ -292,6 +432,23 @@ hipError_t launch_append(const AppendLaunch& L, hipStream_t stream) {
     hipLaunchKernelGGL((append_kernel<3, 3>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+size_t page_errors_workspace_bytes(int n_pages, int hkv) { return (size_t)n_pages * hkv * 2 * 2 * sizeof(double); }
+
+hipError_t launch_page_errors(const WriterLaunch& L, void* workspace, double* out, hipStream_t stream) {
+  const WriterArgs a = writer_args(L);
+  double* part = static_cast<double*>(workspace);
+  const int n = L.n_pages * L.hkv;
+  const dim3 grid((unsigned)n, 2u), block(256u);
+  if (L.k_mode == 3 && L.v_mode == 3)
+    hipLaunchKernelGGL((page_error_kernel<true, true>), grid, block, 0, stream, a, part);
+  else if (L.k_mode != 3 && L.v_mode != 3)
+    hipLaunchKernelGGL((page_error_kernel<false, false>), grid, block, 0, stream, a, part);
+  else
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(page_error_total_kernel, dim3(2u), dim3(256u), 0, stream, part, n, out);
   return hipGetLastError();
 }
 

@@ -208,6 +208,25 @@ bdfp4_status bdfp4_key_means(const void* k_bf16, int32_t tokens, int32_t num_kv_
 bdfp4_status bdfp4_error_sums(const float* got, const float* ref, int64_t n, double* sums_out,
                               void* stream);
 
+/* Quantization diagnostics ("kv-landlords scripts/quant_ab.py" compares
+ * cache schemes by reconstruction error; the recipe ablations of
+ * "BitDecoding-FP4 evaluation/config.py"): for n_pages pages written from
+ * k_bf16 / v_bf16 / page_ids / key_shift (the arguments bdfp4_quantize_pages
+ * took), sums_out (device double[4]) = [sum (k_hat - y)^2, sum y^2,
+ * sum (v_hat - v)^2, sum v^2] over every element, where y are the keys as
+ * quantized (centered and rotated in float32 exactly as the writer does)
+ * and k_hat, v_hat the values the cache holds (codes times scales, read
+ * through the layout above). Float64, fixed summation order. Pages whose
+ * destination is outside [0, num_pages) contribute nothing. workspace:
+ * bdfp4_page_errors_workspace_size bytes, 16-byte aligned, no
+ * initialization needed. */
+bdfp4_status bdfp4_page_errors_workspace_size(int32_t n_pages, int32_t num_kv_heads, size_t* bytes);
+bdfp4_status bdfp4_page_errors(const bdfp4_recipe* r, const bdfp4_cache* cache,
+                               const void* k_bf16, const void* v_bf16,
+                               const int32_t* page_ids, int32_t n_pages,
+                               const float* key_shift, void* workspace,
+                               size_t workspace_bytes, double* sums_out, void* stream);
+
 /* Split plan of bdfp4_decode_attention (host). pages_per_partition (1 .. 4)
  * is the number of consecutive full pages one FP4 partition covers; 0 picks
  * it from (batch, num_kv_heads, max_seq_len) so that about 512 workgroups of

@@ -263,3 +263,21 @@ def test_key_mean_sidecar_round_trip(tmp_path):
     back = bd.load_key_means(p)
     assert sorted(back) == sorted(means)
     assert all(np.array_equal(back[k], means[k]) and back[k].dtype == np.float32 for k in means)
+
+
+def test_page_errors_reject_before_launch():
+    r = bd.recipe_default_nvfp4()
+    L = bd.lib()
+    n = ctypes.c_size_t()
+    assert L.bdfp4_page_errors_workspace_size(4, 2, ctypes.byref(n)) == bd.OK and n.value == 4 * 2 * 4 * 8
+    assert L.bdfp4_page_errors_workspace_size(0, 2, ctypes.byref(n)) == bd.E_INVALID
+
+    def call(r=r, n_pages=4, wsb=1 << 20, mu=FAKE, out=FAKE, cache=None):
+        c = cache or _cache()
+        return L.bdfp4_page_errors(ctypes.byref(r), ctypes.byref(c), FAKE, FAKE, FAKE, n_pages, mu, FAKE, wsb,
+                                   out, None)
+    assert call(wsb=16) == bd.E_WORKSPACE
+    assert call(n_pages=0) == bd.E_INVALID
+    assert call(mu=None) == bd.E_INVALID
+    assert call(out=FAKE + 4) == bd.E_INVALID
+    assert call(r.replace(scale_mode_v=bd.SCALE_MXFP4_SEARCH)) == bd.E_UNSUPPORTED

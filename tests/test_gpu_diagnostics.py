@@ -1,0 +1,67 @@
+"""Quantization diagnostics through the C ABI against the oracle: the page
+squared-error sums of pages the HIP writer wrote equal the oracle's sums
+over the oracle's pages (float64, to summation order), for NVFP4 four_six /
+amax6, without rotation and centering, and MXFP4; a destination page outside
+the pool contributes nothing; sampled pages of the full 131,072-token x
+8-head prefill."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_nvfp4_amd as bd
+from fp4_kv_cache_nvfp4_amd import synth
+from oracle import diagnostics as DG
+from oracle import quant as Q
+from oracle import recipe as RC
+from oracle import writer as W
+
+from gpu_helpers import dev, dev_bf16, gpu_write, oracle_write, to_c
+
+pytestmark = pytest.mark.gpu
+
+RECIPES = {
+    "nvfp4": RC.nvfp4_default().with_(tau=1.0),
+    "nvfp4_amax6": RC.nvfp4_default().with_(tau=1.0, scale_mode_k=Q.AMAX6),
+    "nvfp4_plain": RC.nvfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
+    "mxfp4": RC.mxfp4_default().with_(tau=1.0),
+}
+
+
+def _u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", list(RECIPES))
+def test_page_errors_match_oracle(name):
+    r = RECIPES[name]
+    wl = synth.decode_workload("d", 9, [128 * 5 + 7, 128 * 2], 16, 4, "qwen", extra_pages=2)
+    k, v, ids = wl.writer_inputs()
+    mu = wl.key_shift if r.key_smoothing else None
+    cache = gpu_write(r, wl)
+    ids_f = ids.copy()
+    ids_f[1] = wl.num_pages + 3                         # this input page is not stored anywhere
+    got = bd.page_errors(to_c(r), cache, dev_bf16(k), dev_bf16(v), dev(ids_f),
+                         dev(mu) if mu is not None else None).cpu().numpy()
+    want = DG.page_errors(r, oracle_write(r, wl), k, v, ids_f, mu)
+    print(f"[diag] {name}: K rel {np.sqrt(got[0] / got[1]):.4f} V rel {np.sqrt(got[2] / got[3]):.4f}", flush=True)
+    assert np.allclose(got, want, rtol=1e-12, atol=0.0), (got, want)
+
+
+def test_page_errors_full_prefill_sampled():
+    r = RECIPES["nvfp4"]
+    rc = to_c(r)
+    w = synth.torch_write_rows(0)
+    cache = bd.PagedCache.allocate(rc, w["num_pages"], 8)
+    bd.quantize_pages(rc, cache, w["k"], w["v"], w["page_ids"], w["key_shift"])
+    rng = np.random.default_rng(1)
+    pick = np.sort(rng.choice(w["tokens"] // 128, size=12, replace=False))
+    rows = torch.from_numpy(np.concatenate([np.arange(p * 128, p * 128 + 128) for p in pick])).cuda()
+    ks, vs = w["k"][rows].contiguous(), w["v"][rows].contiguous()
+    ids = w["page_ids"][torch.from_numpy(pick).cuda()].contiguous()
+    got = bd.page_errors(rc, cache, ks, vs, ids, w["key_shift"]).cpu().numpy()
+    # the oracle writes the sampled pages itself and measures its own pages
+    kh, vh, ih, muh = _u16(ks), _u16(vs), ids.cpu().numpy(), w["key_shift"].cpu().numpy()
+    ocache = W.empty_cache(w["num_pages"], 8, r)
+    W.write_pages(r, ocache, kh, vh, ih, muh)
+    want = DG.page_errors(r, ocache, kh, vh, ih, muh)
+    assert np.allclose(got, want, rtol=1e-12, atol=0.0), (got, want)
