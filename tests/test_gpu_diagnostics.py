@@ -65,3 +65,42 @@ def test_page_errors_full_prefill_sampled():
     W.write_pages(r, ocache, kh, vh, ih, muh)
     want = DG.page_errors(r, ocache, kh, vh, ih, muh)
     assert np.allclose(got, want, rtol=1e-12, atol=0.0), (got, want)
+
+
+def _from_c(rc) -> RC.Recipe:
+    mode = {bd.SCALE_NONE: Q.NONE, bd.SCALE_AMAX6: Q.AMAX6, bd.SCALE_FOUR_SIX: Q.FOUR_SIX,
+            bd.SCALE_MXFP4_SEARCH: Q.MXFP4_SEARCH, bd.SCALE_AMAX2_OR_AMAX6: Q.AMAX2_OR_AMAX6}
+    return RC.Recipe(sink_tokens=rc.sink_tokens, rotation=bool(rc.rotation), key_smoothing=bool(rc.key_smoothing),
+                     scale_mode_k=mode[rc.scale_mode_k], scale_mode_v=mode[rc.scale_mode_v],
+                     scale_mode_q=mode[rc.scale_mode_q], scale_mode_p=mode[rc.scale_mode_p],
+                     query_terms=rc.query_terms, c=rc.c, tau=float(rc.tau))
+
+
+def test_ablation_report_matches_oracle():
+    from fp4_kv_cache_nvfp4_amd import diagnostics as D
+    from oracle import decode as OD
+
+    L, layer = 1024 + 77, 3
+    rep = D.ablation_report(context=L, layer=layer)
+    d = synth.torch_decode_layer(layer, seq_len=L)               # the same seeded inputs
+    k, v, q = _u16(d["k"]), _u16(d["v"]), _u16(d["q"])
+    bt, sl = d["block_tables"].cpu().numpy(), d["seq_lens"].cpu().numpy()
+    ids, n_full, mu = d["page_ids"].cpu().numpy(), d["n_full"], d["key_shift"].cpu().numpy()
+    sk, sv, tk, tv = (_u16(d[n]) for n in ("sink_k", "sink_v", "tail_k", "tail_v"))
+    kp = _u16(synth.bf16_pages_from_tokens(d["k"], d["block_tables"], d["num_pages"]))
+    vp = _u16(synth.bf16_pages_from_tokens(d["v"], d["block_tables"], d["num_pages"]))
+    ref = OD.bf16_decode(q, kp, vp, bt, sl, d["sigma"])
+    for name, rc in D.recipes().items():
+        r = _from_c(rc)
+        m = mu if r.key_smoothing else None
+        cache = W.empty_cache(d["num_pages"], 8, r)
+        W.write_pages(r, cache, k[:n_full * 128], v[:n_full * 128], ids, m)
+        pe = DG.page_errors(r, cache, k[:n_full * 128], v[:n_full * 128], ids, m)
+        out = OD.decode(r, cache, q, bt, sl, sk, sv, tk, tv, m, d["sigma"], rep["pages_per_partition"])
+        want = {"k_rel": np.sqrt(pe[0] / pe[1]), "v_rel": np.sqrt(pe[2] / pe[3]),
+                "out_rel_l2": np.linalg.norm(out - ref) / np.linalg.norm(ref)}
+        got = rep["recipes"][name]
+        print(f"[ablation] {name}: {got}", flush=True)
+        assert abs(got["k_rel"] - want["k_rel"]) <= 1e-9 * want["k_rel"], name
+        assert abs(got["v_rel"] - want["v_rel"]) <= 1e-9 * want["v_rel"], name
+        assert abs(got["out_rel_l2"] - want["out_rel_l2"]) <= 1e-3 * want["out_rel_l2"], name
