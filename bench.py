@@ -250,10 +250,22 @@ def bench_key_means(args):
     fn = lambda: bd.key_means_into(k, 8, ws, mu)
     ms, per, _, med = time_launches([fn], max(args.steps, 10), 3)
     nbytes = tokens * 8 * 128 * 2
-    del w, k
+    res = {"key_means_131072x8": {"us": round(ms * 1e3, 3), "bytes": nbytes,
+                                  "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                  "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    # diagnostics: page errors of the whole prefill (reads the bf16 K/V rows
+    # and the written pages)
+    r = bd.recipe_default_nvfp4(tau=1.0)
+    cache = bd.PagedCache.allocate(r, w["num_pages"], 8)
+    bd.quantize_pages(r, cache, w["k"], w["v"], w["page_ids"], w["key_shift"])
+    fn = lambda: bd.page_errors(r, cache, w["k"], w["v"], w["page_ids"], w["key_shift"])
+    ms, per, _, med = time_launches([fn], max(args.steps, 10), 3)
+    nbytes = writer_bytes(tokens, 8, False)
+    res["page_errors_131072x8"] = {"us": round(ms * 1e3, 3), "bytes": nbytes,
+                                   "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del w, k, cache
     torch.cuda.empty_cache()
-    return {"us": round(ms * 1e3, 3), "bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return res
 
 
 def cpu_baseline(args):
@@ -433,7 +445,7 @@ def main():
             print(f"[bench] append batch {batch}: {append[f'batch{batch}']}", file=sys.stderr, flush=True)
     calibration = None
     if not args.no_calibration:
-        calibration = {"key_means_131072x8": bench_key_means(args)}
+        calibration = bench_key_means(args)
         print(f"[bench] key means: {calibration}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
@@ -475,7 +487,7 @@ def main():
         "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
         "writer_131072x8": writer,
         "append_x8_heads": append,
-        "calibration": calibration,
+        "calibration_diagnostics": calibration,
     }
     print(json.dumps(line))
 
