@@ -45,7 +45,7 @@ import numpy as np
 from . import quant as Q
 from .formats import bf16_to_f32
 from .recipe import Recipe
-from .rotation import rotate
+from .rotation import hadamard_matrix, rotate
 from .writer import read_page_head
 
 PAGE = 128
@@ -129,7 +129,12 @@ def attend_head(recipe: Recipe, q_f32: np.ndarray, seq_len: int,
             m = t.max(axis=1)
             p = np.exp(t - m[:, None])
             ph = _p_hat(recipe, p)
-            partials.append((ph @ v_hat[lo:hi], m, p.sum(axis=1)))
+            o = ph @ v_hat[lo:hi]
+            if recipe.rotate_v:
+                # v_hat are rotated values: rotate this partition's output
+                # back (H / sqrt(128) is symmetric and its own inverse)
+                o = o @ (hadamard_matrix().astype(np.float64) / np.sqrt(128.0))
+            partials.append((o, m, p.sum(axis=1)))
     return merge(partials)
 
 

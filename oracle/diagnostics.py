@@ -7,7 +7,7 @@ their reconstruction error and memory ("BitDecoding-FP4 evaluation/config.py"
 lists the recipe ablations: rotation, key smoothing, K four_six vs amax6,
 query terms, c). Reading: the error of a page is measured in the domain it
 was quantized in - keys centered and rotated (what the codes approximate),
-values as stored - as float64 sums over every element of the written pages:
+values as stored (rotated in the rotate_v variant) - as float64 sums over every element of the written pages:
 
     [sum (k_hat - y)^2, sum y^2, sum (v_hat - v)^2, sum v^2]
 
@@ -22,7 +22,7 @@ import numpy as np
 from . import layout
 from .formats import bf16_to_f32
 from .recipe import Recipe
-from .writer import key_rows, read_page_head
+from .writer import key_rows, read_page_head, value_rows
 
 
 def page_errors(recipe: Recipe, cache: dict, k_bf16: np.ndarray, v_bf16: np.ndarray, page_ids,
@@ -44,6 +44,6 @@ def page_errors(recipe: Recipe, cache: dict, k_bf16: np.ndarray, v_bf16: np.ndar
             mu = None if key_shift is None or not recipe.key_smoothing else np.asarray(key_shift)[h]
             y = key_rows(k[i, :, h], mu, recipe.rotation).astype(np.float64)
             kh, vh = read_page_head(recipe, cache, p, h)
-            vv = v[i, :, h].astype(np.float64)
+            vv = value_rows(v[i, :, h], recipe.rotate_v).astype(np.float64)
             out += [np.sum((kh - y) ** 2), np.sum(y ** 2), np.sum((vh - vv) ** 2), np.sum(vv ** 2)]
     return out

@@ -47,6 +47,7 @@ class Recipe:
     query_terms: int = 2
     c: int = 8
     tau: float = float("nan")
+    rotate_v: bool = False          # recipe variant: values rotated as keys are, output rotated back
 
     def with_(self, **kw) -> "Recipe":
         return replace(self, **kw)

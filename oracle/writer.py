@@ -18,7 +18,10 @@ the comment that the runner creates missing key means):
     codes, scales = quantize(y, scale_mode_k)
 
 Value path: codes, scales = quantize(float32(v), scale_mode_v); the rotation
-is listed under key quantization only, so values are not rotated.
+is listed under key quantization only, so values are not rotated - except in
+the rotate_v recipe variant (the alternative reading: rotate V as well and
+rotate the attention output back), where v is rotated like a key (no
+centering) before quantization.
 """
 from __future__ import annotations
 
@@ -43,8 +46,14 @@ def quantize_k_rows(k_f32, mu, rotation: bool, mode: str):
     return Q.quantize(key_rows(k_f32, mu, rotation), mode)
 
 
-def quantize_v_rows(v_f32, mode: str):
-    return Q.quantize(np.asarray(v_f32, dtype=np.float32), mode)
+def value_rows(v_f32, rotate_v: bool) -> np.ndarray:
+    """The float32 value rows that get quantized."""
+    x = np.asarray(v_f32, dtype=np.float32)
+    return rotate(x) if rotate_v else x
+
+
+def quantize_v_rows(v_f32, mode: str, rotate_v: bool = False):
+    return Q.quantize(value_rows(v_f32, rotate_v), mode)
 
 
 def empty_cache(num_pages: int, num_kv_heads: int, recipe: Recipe) -> dict:
@@ -77,7 +86,7 @@ def write_pages(recipe: Recipe, cache: dict, k_bf16: np.ndarray, v_bf16: np.ndar
     kmx = recipe.scale_mode_k == Q.MXFP4_SEARCH
     vmx = recipe.scale_mode_v == Q.MXFP4_SEARCH
     kn, ks = quantize_k_rows(k, mu, recipe.rotation, recipe.scale_mode_k)
-    vn, vs = quantize_v_rows(v, recipe.scale_mode_v)
+    vn, vs = quantize_v_rows(v, recipe.scale_mode_v, recipe.rotate_v)
     # [n, tok, h, ...] -> [n, h, tok, ...]
     kn = kn.transpose(0, 2, 1, 3)
     ks = ks.transpose(0, 2, 1, 3)
@@ -92,7 +101,8 @@ def write_pages(recipe: Recipe, cache: dict, k_bf16: np.ndarray, v_bf16: np.ndar
 
 def read_page_head(recipe: Recipe, cache: dict, page: int, head: int):
     """Dequantized (k_hat, v_hat) of one page-head, float64 [128, 128] each,
-    in the quantized domain (keys centered and rotated)."""
+    in the quantized domain (keys centered and rotated; values rotated in the
+    rotate_v variant)."""
     kmx = recipe.scale_mode_k == Q.MXFP4_SEARCH
     vmx = recipe.scale_mode_v == Q.MXFP4_SEARCH
     kn = layout.unpack_codes(cache["k_codes"][page, head], "k")

@@ -4,6 +4,7 @@
 * layout: every nibble and scale byte of a page is used exactly once;
 * writer: on-grid pages (rotation and centering off) dequantize to the input;
 * decode with every quantizer off equals textbook softmax attention;
+  with values rotated (rotate_v) and the outputs rotated back, too;
   centering + rotation with quantizers off equals it to float32 rounding;
   on-grid pages read through the packed cache equal textbook attention;
 * with P unquantized the result is independent of the split plan;
@@ -197,7 +198,7 @@ def _rows_unquantized(wl, r):
         k = F.bf16_to_f32(wl.k_tokens[b][: n * 128, h])
         v = F.bf16_to_f32(wl.v_tokens[b][: n * 128, h])
         x = W.key_rows(k, wl.key_shift[h] if r.key_smoothing else None, r.rotation)
-        return x.astype(np.float64), v.astype(np.float64)
+        return x.astype(np.float64), W.value_rows(v, r.rotate_v).astype(np.float64)
     return rows
 
 
@@ -216,6 +217,18 @@ def test_centering_and_rotation_preserve_attention():
     r = RC.nvfp4_default().with_(**OFF)
     got = _run(r, wl, fp4_rows=_rows_unquantized(wl, r))
     assert np.max(np.abs(got - _textbook(wl))) <= 1e-6
+
+
+def test_value_rotation_preserves_attention():
+    # rotating the values and the partition outputs back changes nothing but
+    # float32 rounding of the rotated values
+    wl = _workload(seed=2)
+    r = RC.nvfp4_default().with_(rotate_v=True, **OFF)
+    got = _run(r, wl, fp4_rows=_rows_unquantized(wl, r))
+    assert np.max(np.abs(got - _textbook(wl))) <= 1e-6
+    # and without the rotation back the result is visibly different
+    plain = _run(r.with_(rotate_v=False), wl, fp4_rows=_rows_unquantized(wl, r))
+    assert np.max(np.abs(plain - _textbook(wl))) > 1e-2
 
 
 def test_on_grid_cache_through_packed_layout_is_textbook():
