@@ -41,6 +41,7 @@ class Recipe(ctypes.Structure):
         ("query_terms", ctypes.c_int32),
         ("c", ctypes.c_int32),
         ("tau", ctypes.c_float),
+        ("rotate_v", ctypes.c_int32),
     ]
 
     def replace(self, **kw) -> "Recipe":

@@ -46,6 +46,7 @@ bool is_mx_kv(const bdfp4_recipe* r) {
 bdfp4_status check_kv_recipe(const bdfp4_recipe* r) {
   if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
   if (r->rotation != 0 && r->rotation != 1) return fail(BDFP4_E_INVALID, "rotation must be 0 or 1");
+  if (r->rotate_v != 0 && r->rotate_v != 1) return fail(BDFP4_E_INVALID, "rotate_v must be 0 or 1");
   if (r->key_smoothing != 0 && r->key_smoothing != 1)
     return fail(BDFP4_E_INVALID, "key_smoothing must be 0 or 1");
   const int km = r->scale_mode_k, vm = r->scale_mode_v;
@@ -174,6 +175,7 @@ bdfp4_status bdfp4_recipe_default_nvfp4(bdfp4_recipe* r) {
   if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
   r->sink_tokens = 16;
   r->rotation = 1;
+  r->rotate_v = 0;
   r->key_smoothing = 1;
   r->scale_mode_k = BDFP4_SCALE_FOUR_SIX;
   r->scale_mode_v = BDFP4_SCALE_AMAX6;
@@ -244,6 +246,7 @@ bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cach
   L.hkv = cache->num_kv_heads;
   L.n_pages = n_pages;
   L.rotation = r->rotation;
+  L.rotate_v = r->rotate_v;
   L.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
   L.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
   return hip_status(bdfp4::launch_writer(L, static_cast<hipStream_t>(stream)), "page writer launch");
@@ -287,6 +290,7 @@ bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache
   L.w.hkv = cache->num_kv_heads;
   L.w.n_pages = 0;
   L.w.rotation = r->rotation;
+  L.w.rotate_v = r->rotate_v;
   L.w.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
   L.w.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
   L.k_new = k_new;
@@ -374,6 +378,7 @@ bdfp4_status bdfp4_page_errors(const bdfp4_recipe* r, const bdfp4_cache* cache, 
   L.hkv = cache->num_kv_heads;
   L.n_pages = n_pages;
   L.rotation = r->rotation;
+  L.rotate_v = r->rotate_v;
   L.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
   L.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
   return hip_status(bdfp4::launch_page_errors(L, workspace, sums_out, static_cast<hipStream_t>(stream)),
@@ -460,6 +465,7 @@ bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* ca
   bdfp4::DecodeLaunch L;
   L.sink = r->sink_tokens;
   L.rotation = r->rotation;
+  L.rotate_v = r->rotate_v;
   L.key_smoothing = r->key_smoothing;
   L.mx = is_mx_kv(r) ? 1 : 0;
   L.k_four_six = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX;

@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
   write_partial(partial_writer(C, bh, s), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.ticket) + 1 == nparts) {
-    merge_out(C, b, h, nparts);
+    merge_out(C, b, h, nparts, false);
     reset_ticket(ticket);
   }
 }

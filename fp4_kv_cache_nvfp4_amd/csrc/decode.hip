@@ -759,8 +759,12 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   }
   const float fah = head == 0 ? fa[0] : (head == 1 ? fa[1] : (head == 2 ? fa[2] : fa[3]));
   const float fbh = head == 0 ? fb[0] : (head == 1 ? fb[1] : (head == 2 ? fb[2] : fb[3]));
-  o0 = fmaf(fah, o0 * invc, bf16 ? fbh * bfp.o0 : 0.0f);
-  o1 = fmaf(fah, o1 * invc, bf16 ? fbh * bfp.o1 : 0.0f);
+  // with rotated values the FP4 part is in the rotated domain: the BF16
+  // partition (raw values) is rotated into it before the two are added
+  float bo0 = bf16 ? bfp.o0 : 0.0f, bo1 = bf16 ? bfp.o1 : 0.0f;
+  if (bf16 && P.rotate_v) wave_rotate2(bo0, bo1);       // uniform per workgroup
+  o0 = fmaf(fah, o0 * invc, bf16 ? fbh * bo0 : 0.0f);
+  o1 = fmaf(fah, o1 * invc, bf16 ? fbh * bo1 : 0.0f);
   const bool poisoned = (sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3]) != 0;
   const float nan = __builtin_nanf("");
   Partial r;
@@ -812,7 +816,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   write_partial(partial_writer(C, bh, sp), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
-    merge_out(C, b, h, nwg);
+    merge_out(C, b, h, nwg, P.rotate_v != 0);
     reset_ticket(ticket);
   }
 }

@@ -146,6 +146,28 @@ __device__ __forceinline__ float of_head(float v0, float v1, float v2, float v3,
   return g < 2 ? lo : hi;
 }
 
+// The normalised 128-point Hadamard rotation (H / sqrt(128), its own
+// inverse) of one head's row held by a wave, lane l holding channels 2l and
+// 2l + 1: stages h = 1, 2, ..., 64 of (a, b) -> (a + b, a - b) in float32,
+// then the factor 1/sqrt(128), as the key rotation. All 64 lanes take part.
+__device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
+  const int lane = threadIdx.x & 63;
+  {
+    const float a = x0, b = x1;
+    x0 = __fadd_rn(a, b);
+    x1 = __fsub_rn(a, b);
+  }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {                 // stage h = 2 s: partner lane l ^ s
+    const float p0 = __shfl_xor(x0, s, 64), p1 = __shfl_xor(x1, s, 64);
+    const bool upper = (lane & s) != 0;
+    x0 = upper ? __fsub_rn(p0, x0) : __fadd_rn(x0, p0);
+    x1 = upper ? __fsub_rn(p1, x1) : __fadd_rn(x1, p1);
+  }
+  x0 = __fmul_rn(x0, inv_sqrt_d());
+  x1 = __fmul_rn(x1, inv_sqrt_d());
+}
+
 // Merges the n partials of (sequence b, KV head h) and writes out = o / L.
 // Each wave merges its own query head (wave g, head g) with no workgroup
 // barrier: per batch of 64 partials, lane i loads (m, l) of partial i and
@@ -157,10 +179,11 @@ __device__ __forceinline__ float of_head(float v0, float v1, float v2, float v3,
 // slot past them reads 0 and needs no address select; its weight is 0. The
 // partials are always combined in slot order (lane order for l, slot order
 // for o), so the result does not depend on which workgroup merges: the
-// output is deterministic.
+// output is deterministic. With rotate_back (values stored rotated), the
+// merged o is rotated back before the division.
 constexpr int kMergeBatch = 64;
 
-__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n) {
+__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n, bool rotate_back) {
   // (sequence, KV head) and n as scalars: the buffer resource below must
   // live in scalar registers, or every load becomes a loop over distinct values
   const int bh = __builtin_amdgcn_readfirstlane(b * C.hkv + h);
@@ -195,6 +218,7 @@ __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n
     }
     M = Mn;
   }
+  if (rotate_back) wave_rotate2(o0, o1);                // uniform per workgroup
   float* out = C.out + ((size_t)b * C.hq + h * kGroup + g) * kD + 2 * lane;
   *reinterpret_cast<float2*>(out) = make_float2(o0 / Ls, o1 / Ls);
 }

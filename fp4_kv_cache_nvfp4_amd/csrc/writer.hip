@@ -34,6 +34,7 @@ struct WriterArgs {
   int32_t hkv;
   int32_t n_pages;
   int32_t rotation;
+  int32_t rotate_v;          // values rotated before quantization (recipe variant)
 };
 
 // Row t (token 0..127) of input page in_page of the bulk writer's
@@ -111,6 +112,7 @@ __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows,
       uint4* dstc = reinterpret_cast<uint4*>(a.k_codes + blk * 8192 + tile * 1024 + q * 256 + n * 16);
       *dstc = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     } else {
+      if (a.rotate_v) rotate_row_quad(x, q);
       uint32_t pk[4];
       const int chunk = t >> 5, qq = (t >> 3) & 3, i8 = t & 7;
       if (kVMx) {
@@ -288,6 +290,8 @@ __device__ __forceinline__ void page_error(const WriterArgs& a, int in_page, int
         for (int i = 0; i < 32; ++i) x[i] = __fsub_rn(x[i], mu[i]);
       }
       if (a.rotation) rotate_row_quad(x, q);
+    } else if (a.rotate_v) {
+      rotate_row_quad(x, q);
     }
 #pragma unroll 4
     for (int e = 0; e < 32; ++e) {
@@ -390,6 +394,7 @@ static WriterArgs writer_args(const WriterLaunch& L) {
   a.hkv = L.hkv;
   a.n_pages = L.n_pages;
   a.rotation = L.rotation;
+  a.rotate_v = L.rotate_v;
   return a;
 }
 

@@ -6,7 +6,8 @@ rotation, key smoothing, K four_six, two query terms, P amax2_or_amax6 with
 c and tau) and "kv-landlords scripts/quant_ab.py" compares cache schemes by
 reconstruction error; this driver measures each part's effect by switching
 it off alone, plus a plain NVFP4 cache (amax6 everywhere, no rotation or
-centering, one query term, tau = 0) and the MXFP4 recipe. For every recipe:
+centering, one query term, tau = 0), the rotated-values variant and the MXFP4
+recipe. For every recipe:
 
 * bdfp4_quantize_pages writes the layer's full pages;
 * bdfp4_page_errors gives the relative K error (centered, rotated domain)
@@ -37,6 +38,7 @@ ABLATIONS = {
     "query_terms_1": {"query_terms": 1},
     "c_1": {"c": 1},
     "p_amax6_tau_0": {"tau": 0.0},
+    "rotate_v": {"rotate_v": 1},
     "plain_nvfp4": {"scale_mode_k": SCALE_AMAX6, "rotation": 0, "key_smoothing": 0, "query_terms": 1,
                     "tau": 0.0},
     "bitdecoding-mxfp4": None,

@@ -83,6 +83,9 @@ typedef struct {
   int32_t query_terms;   /* 2: q ~ Q1 + Q2 (residual); 1: Q1 only              */
   int32_t c;             /* probability multiplier, 1 or 8                     */
   float tau;             /* threshold, finite in [0, 448]; NaN = "calibrate"  */
+  int32_t rotate_v;      /* recipe variant, 0 in both modes: 1 rotates values
+                            with the same Hadamard rotation before they are
+                            quantized, and the decode rotates its output back */
 } bdfp4_recipe;
 
 /* The quantized paged cache. Each of the four arrays is dense

@@ -39,6 +39,7 @@ def to_c(r: RC.Recipe) -> bd.Recipe:
     c.query_terms = r.query_terms
     c.c = r.c
     c.tau = float(r.tau)
+    c.rotate_v = int(r.rotate_v)
     return c
 
 

@@ -81,6 +81,7 @@ def test_recipe_validation_follows_probability_environment():
 @pytest.mark.parametrize("field,value,status", [
     ("sink_tokens", 8, bd.E_INVALID), ("sink_tokens", 128, bd.E_INVALID), ("sink_tokens", -16, bd.E_INVALID),
     ("query_terms", 3, bd.E_INVALID), ("rotation", 2, bd.E_INVALID), ("key_smoothing", 5, bd.E_INVALID),
+    ("rotate_v", 2, bd.E_INVALID),
     ("scale_mode_k", 9, bd.E_INVALID), ("scale_mode_v", bd.SCALE_FOUR_SIX, bd.E_INVALID),
     ("scale_mode_p", 7, bd.E_INVALID), ("scale_mode_p", bd.SCALE_NONE, bd.E_UNSUPPORTED),
     ("scale_mode_q", bd.SCALE_MXFP4_SEARCH, bd.E_UNSUPPORTED),

@@ -24,6 +24,7 @@ RECIPES = {
     "nvfp4": RC.nvfp4_default().with_(tau=1.0),
     "nvfp4_plain": RC.nvfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
     "mxfp4": RC.mxfp4_default().with_(tau=1.0),
+    "nvfp4_rotv": RC.nvfp4_default().with_(tau=1.0, rotate_v=True),
 }
 
 

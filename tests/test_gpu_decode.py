@@ -2,7 +2,8 @@
 quantized operands and the same split plan: max-abs <= 2e-3 and relative L2
 <= 1e-3 on float32 outputs. Covers the tiny 2K case, ragged batches (sink
 only, sink + tail, several partitions with a ragged last one), sink lengths,
-the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode, the
+the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode,
+rotated values (NVFP4 and MXFP4, ragged batch included), the
 32K Qwen3-4B-shaped layer with a 77-token tail, determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
 and the BF16-KV baseline arm."""
@@ -43,11 +44,13 @@ def test_tiny_2k_mxfp4():
     _run(MX, synth.tiny(0), 4, "tiny mxfp4")
 
 
-@pytest.mark.parametrize("variant", ["terms1", "c1", "tau0", "p_amax6", "k_amax6", "norot", "nosmooth"])
+@pytest.mark.parametrize("variant", ["terms1", "c1", "tau0", "p_amax6", "k_amax6", "norot", "nosmooth", "rotv",
+                                     "rotv_mx"])
 def test_recipe_variants(variant):
     r = {"terms1": NV.with_(query_terms=1), "c1": NV.with_(c=1), "tau0": NV.with_(tau=0.0),
          "p_amax6": NV.with_(scale_mode_p=Q.AMAX6), "k_amax6": NV.with_(scale_mode_k=Q.AMAX6),
-         "norot": NV.with_(rotation=False), "nosmooth": NV.with_(key_smoothing=False)}[variant]
+         "norot": NV.with_(rotation=False), "nosmooth": NV.with_(key_smoothing=False),
+         "rotv": NV.with_(rotate_v=True), "rotv_mx": MX.with_(rotate_v=True)}[variant]
     wl = synth.decode_workload("v", 3, [1500, 777], 8, 2, "qwen", extra_pages=1)
     _run(r, wl, 2, variant)
 
@@ -57,6 +60,13 @@ def test_ragged_batch(sink):
     # L = 1 (sink only), 100 (< one page), 300 (2 pages + 44 tail), 2049 (16 pages + 1), 640 (5 pages)
     wl = synth.decode_workload("r", 4, [1, 100, 300, 2049, 640], 8, 2, "tiny", extra_pages=2, sink_tokens=sink)
     _run(NV.with_(sink_tokens=sink), wl, 3, f"ragged sink={sink}")
+
+
+def test_ragged_batch_rotated_values():
+    # sequences with no full page (BF16 only, written directly) beside ones
+    # whose merged output is rotated back
+    wl = synth.decode_workload("r", 6, [1, 100, 300, 2049, 640], 8, 2, "qwen", extra_pages=2)
+    _run(NV.with_(rotate_v=True), wl, 3, "ragged rotate_v")
 
 
 def test_ragged_batch_mxfp4():

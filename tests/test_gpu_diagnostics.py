@@ -24,6 +24,7 @@ RECIPES = {
     "nvfp4_amax6": RC.nvfp4_default().with_(tau=1.0, scale_mode_k=Q.AMAX6),
     "nvfp4_plain": RC.nvfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
     "mxfp4": RC.mxfp4_default().with_(tau=1.0),
+    "nvfp4_rotv": RC.nvfp4_default().with_(tau=1.0, rotate_v=True),
 }
 
 
@@ -73,7 +74,7 @@ def _from_c(rc) -> RC.Recipe:
     return RC.Recipe(sink_tokens=rc.sink_tokens, rotation=bool(rc.rotation), key_smoothing=bool(rc.key_smoothing),
                      scale_mode_k=mode[rc.scale_mode_k], scale_mode_v=mode[rc.scale_mode_v],
                      scale_mode_q=mode[rc.scale_mode_q], scale_mode_p=mode[rc.scale_mode_p],
-                     query_terms=rc.query_terms, c=rc.c, tau=float(rc.tau))
+                     query_terms=rc.query_terms, c=rc.c, tau=float(rc.tau), rotate_v=bool(rc.rotate_v))
 
 
 def test_ablation_report_matches_oracle():

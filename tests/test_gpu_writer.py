@@ -24,6 +24,8 @@ RECIPES = {
     "nvfp4_plain": RC.nvfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
     "mxfp4": RC.mxfp4_default().with_(tau=1.0),
     "mxfp4_plain": RC.mxfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
+    "nvfp4_rotv": RC.nvfp4_default().with_(tau=1.0, rotate_v=True),
+    "mxfp4_rotv": RC.mxfp4_default().with_(tau=1.0, rotate_v=True),
 }
 
 
