@@ -4,7 +4,8 @@ quantized operands and the same split plan: max-abs <= 2e-3 and relative L2
 only, sink + tail, several partitions with a ragged last one), sink lengths,
 the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode,
 rotated values (NVFP4 and MXFP4, ragged batch included), the
-32K Qwen3-4B-shaped layer with a 77-token tail, determinism, paging
+32K Qwen3-4B-shaped layer with a 77-token tail, the full 128K layer in the
+benchmark's launch configuration (two KV heads sampled), determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
 and the BF16-KV baseline arm."""
 import numpy as np
@@ -16,6 +17,7 @@ from fp4_kv_cache_nvfp4_amd import synth
 from oracle import decode as OD
 from oracle import quant as Q
 from oracle import recipe as RC
+from oracle import writer as OW
 
 from gpu_helpers import (assert_close, cache_to_dev, dev, dev_bf16, gpu_decode, gpu_write,
                          oracle_decode, oracle_write, to_c)
@@ -153,3 +155,24 @@ def test_bf16_baseline(ppp):
                              dev(wl.seq_lens), msl, wl.sigma, ppp, ws, out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy().astype(np.float64), ref, f"bf16 baseline ppp={ppp}")
+
+
+def test_full_128k_layer_sampled_heads():
+    """The headline shape in the launch configuration the benchmark times:
+    batch 1, 131,072 tokens, 32 query / 8 KV heads, the library's own split
+    plan. The HIP writer and decode run on all 8 KV heads; the oracle writes
+    and decodes KV heads 0 and 5 from the same seeded inputs, and their 8
+    query-head rows are compared."""
+    L, heads = 131072, [0, 5]
+    wl = synth.decode_workload("full128k", 11, [L], 32, 8, "qwen")
+    ppp, parts = bd.decode_plan(1, 8, L, 0)
+    assert (ppp, parts) == (4, 256)                    # 512 workgroups, as the benchmark launches
+    got = gpu_decode(NV, wl, gpu_write(NV, wl), ppp)
+    rows = [4 * h + g for h in heads for g in range(4)]
+    k, v, ids = wl.writer_inputs()
+    cache = OW.empty_cache(wl.num_pages, len(heads), NV)
+    OW.write_pages(NV, cache, k[:, heads], v[:, heads], ids, wl.key_shift[heads])
+    sk, sv, tk, tv = wl.sink_tail()
+    ref = OD.decode(NV, cache, wl.q[:, rows], wl.block_tables, wl.seq_lens, sk[:, heads], sv[:, heads],
+                    tk[:, heads], tv[:, heads], wl.key_shift[heads], wl.sigma, ppp)
+    assert_close(got[:, rows], ref, "128k layer, KV heads 0 and 5")
