@@ -13,7 +13,8 @@ timing; all inputs are resident in HBM when the timed region starts.
 A step is one decode token through all 36 layers: 36 launches of
 bdfp4_decode_attention (each: two-term query quantization, QK^T over the FP4
 pages, partition softmax, P quantization, PV, BF16 sink partition and the
-split-K merge). The MXFP4 and BF16-KV arms, the page writer (131,072
+split-K merge). The MXFP4 and BF16-KV arms, a batch of 16 sequences of
+2K..16K tokens, the page writer (131,072
 tokens x 8 heads prefill write) and the decode-time append (batch 1 and 64 x 8
 KV heads, inside a page and at the token that freezes one) and the key-mean
 calibration over the prefill keys are timed the same way and reported beside
@@ -50,6 +51,7 @@ def parse():
     ap.add_argument("--no-writer", action="store_true")
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -170,6 +172,41 @@ def build_layers(args, arms):
         del d
         torch.cuda.synchronize()
     return layers, outs, ppp, parts
+
+
+def bench_batched(args):
+    """NVFP4 decode of 16 sequences with lengths drawn from 2K..16K (seeded)
+    over one shuffled pool (32 query / 8 KV heads), the library's plan for
+    the batch: one launch per step. Bytes = the sum of every sequence's
+    decode bytes."""
+    import torch
+
+    import fp4_kv_cache_nvfp4_amd as bd
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    wl = synth.batched(0)
+    r = bd.recipe_default_nvfp4(tau=1.0)
+    B, msl = wl.batch, int(wl.seq_lens.max())
+    ppp, parts = bd.decode_plan(B, 8, msl, 0)
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k, v, ids = wl.writer_inputs()
+    cache = bd.PagedCache.allocate(r, wl.num_pages, 8)
+    mu = t(wl.key_shift)
+    bd.quantize_pages(r, cache, t16(k), t16(v), t(ids), mu)
+    sk, sv, tk, tv = wl.sink_tail()
+    ws = bd.alloc_workspace(bd.decode_workspace_size(B, 32, 8, msl, ppp))
+    out = torch.empty((B, 32, 128), dtype=torch.float32, device="cuda")
+    call = bd.DecodeCall(r, cache, t16(wl.q), t(wl.block_tables), t(wl.seq_lens), msl, t16(sk), t16(sv),
+                         t16(tk), t16(tv), mu, wl.sigma, ppp, ws, out)
+    ms, per, _, med = time_launches([call], max(args.steps, 20), args.warmup)
+    nbytes = sum(decode_bytes(int(L), 32, 8, 16, False) for L in wl.seq_lens)
+    del cache
+    torch.cuda.empty_cache()
+    return {"workload": "16 sequences, L ~ U{2048..16384} (seed 0), shared shuffled pool",
+            "tokens": int(wl.seq_lens.sum()), "pages_per_partition": ppp, "max_partitions": parts,
+            "us": round(ms * 1e3, 3), "bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def bench_writer(args, mx: bool):
@@ -438,6 +475,10 @@ def main():
             writer["mxfp4" if mx else "nvfp4"] = bench_writer(args, mx)
             print(f"[bench] writer {'mxfp4' if mx else 'nvfp4'}: {writer['mxfp4' if mx else 'nvfp4']['us']:.1f} us",
                   file=sys.stderr, flush=True)
+    batched = None
+    if not args.no_batched:
+        batched = bench_batched(args)
+        print(f"[bench] batched: {batched}", file=sys.stderr, flush=True)
     append = {}
     if not args.no_append:
         for batch in (1, 64):
@@ -486,6 +527,7 @@ def main():
         "cpu_baseline": cpu,
         "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
         "writer_131072x8": writer,
+        "batched_16x_2k_16k": batched,
         "append_x8_heads": append,
         "calibration_diagnostics": calibration,
     }

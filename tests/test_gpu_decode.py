@@ -5,7 +5,8 @@ only, sink + tail, several partitions with a ragged last one), sink lengths,
 the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode,
 rotated values (NVFP4 and MXFP4, ragged batch included), the
 32K Qwen3-4B-shaped layer with a 77-token tail, the full 128K layer in the
-benchmark's launch configuration (two KV heads sampled), determinism, paging
+benchmark's launch configuration (two KV heads sampled), 16 sequences of
+2K..16K tokens (two sampled), determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
 and the BF16-KV baseline arm."""
 import numpy as np
@@ -176,3 +177,24 @@ def test_full_128k_layer_sampled_heads():
     ref = OD.decode(NV, cache, wl.q[:, rows], wl.block_tables, wl.seq_lens, sk[:, heads], sv[:, heads],
                     tk[:, heads], tv[:, heads], wl.key_shift[heads], wl.sigma, ppp)
     assert_close(got[:, rows], ref, "128k layer, KV heads 0 and 5")
+
+
+def test_batched_16_sequences_sampled():
+    """16 sequences with lengths drawn from 2K..16K over one shuffled pool,
+    the library's own plan for the batch. The HIP path writes and decodes
+    the whole batch; the oracle writes and decodes sequences 0 and 9 (every
+    KV head) from the same inputs."""
+    wl = synth.batched(0)
+    B, msl = wl.batch, int(wl.seq_lens.max())
+    ppp, _ = bd.decode_plan(B, 8, msl, 0)
+    got = gpu_decode(NV, wl, gpu_write(NV, wl), ppp)
+    pick = [0, 9]
+    cache = OW.empty_cache(wl.num_pages, 8, NV)
+    for b in pick:
+        n = wl.full_pages(b)
+        OW.write_pages(NV, cache, wl.k_tokens[b][:n * 128], wl.v_tokens[b][:n * 128], wl.block_tables[b, :n],
+                       wl.key_shift)
+    sk, sv, tk, tv = wl.sink_tail()
+    ref = OD.decode(NV, cache, wl.q[pick], wl.block_tables[pick], wl.seq_lens[pick], sk[pick], sv[pick],
+                    tk[pick], tv[pick], wl.key_shift, wl.sigma, ppp)
+    assert_close(got[pick], ref, f"batched 16 x 2k..16k ppp={ppp}, sequences {pick}")
