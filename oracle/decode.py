@@ -128,7 +128,15 @@ def attend_head(recipe: Recipe, q_f32: np.ndarray, seq_len: int,
             t = sigma * (qhat @ k_hat[lo:hi].T + qmu[:, None])
             m = t.max(axis=1)
             p = np.exp(t - m[:, None])
-            ph = _p_hat(recipe, p)
+            if recipe.p_running_max:
+                # recipe variant: each aligned 16-token block is normalised by
+                # the running maximum over the partition's blocks up to it (as
+                # a one-pass kernel would see it), quantized against that, and
+                # weighted back to the partition maximum
+                mrun = np.repeat(np.maximum.accumulate(t.reshape(G, -1, 16).max(axis=2), axis=1), 16, axis=1)
+                ph = _p_hat(recipe, np.exp(t - mrun)) * np.exp(mrun - m[:, None])
+            else:
+                ph = _p_hat(recipe, p)
             o = ph @ v_hat[lo:hi]
             if recipe.rotate_v:
                 # v_hat are rotated values: rotate this partition's output

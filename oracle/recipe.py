@@ -48,6 +48,7 @@ class Recipe:
     c: int = 8
     tau: float = float("nan")
     rotate_v: bool = False          # recipe variant: values rotated as keys are, output rotated back
+    p_running_max: bool = False     # recipe variant: P of each 16-token block against the running maximum
 
     def with_(self, **kw) -> "Recipe":
         return replace(self, **kw)

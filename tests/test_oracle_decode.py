@@ -4,7 +4,10 @@
 * layout: every nibble and scale byte of a page is used exactly once;
 * writer: on-grid pages (rotation and centering off) dequantize to the input;
 * decode with every quantizer off equals textbook softmax attention;
-  with values rotated (rotate_v) and the outputs rotated back, too;
+  with values rotated (rotate_v) and the outputs rotated back, too; and with
+  P normalised by the running block maximum (p_running_max), which with P
+  quantized equals the partition-maximum reading when every partition peaks
+  in its first block;
   centering + rotation with quantizers off equals it to float32 rounding;
   on-grid pages read through the packed cache equal textbook attention;
 * with P unquantized the result is independent of the split plan;
@@ -297,3 +300,34 @@ def test_bf16_baseline_is_textbook():
     kp, vp = wl.bf16_pages()
     got = OD.bf16_decode(wl.q, kp, vp, wl.block_tables, wl.seq_lens, wl.sigma)
     assert np.max(np.abs(got - _textbook(wl))) <= 1e-12
+
+
+def test_running_max_variant_reduces_to_partition_max_and_to_textbook():
+    wl = _workload(seed=3)
+    # P unquantized: the normaliser cancels, both readings are textbook attention
+    r = RC.nvfp4_default().with_(p_running_max=True, rotation=False, key_smoothing=False, **OFF)
+    got = _run(r, wl, fp4_rows=_rows_unquantized(wl, r))
+    assert np.max(np.abs(got - _textbook(wl))) <= 1e-12
+    # P quantized, each partition's maximum in its first 16-token block: the
+    # running maximum is the partition maximum throughout, the results coincide.
+    # One query head per KV head, whose key at the partition's first token is
+    # 50 q / |q| (logit 50 |q| sigma, far above the others).
+    wl1 = _workload(seed=3, g=1)
+    q = RC.nvfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False, scale_mode_k=Q.NONE,
+                                 scale_mode_v=Q.NONE, scale_mode_q=Q.NONE)
+    rows = _rows_unquantized(wl1, q)
+    qf = np.asarray(F.bf16_to_f32(wl1.q), dtype=np.float64)
+
+    def peaked(b, h, n):
+        k, v = rows(b, h, n)
+        k = k.copy()
+        for lo in ([16] if n else []) + [128 * p for p in range(1, n)]:   # each one-page partition's first token
+            k[lo] = 50.0 * qf[b, h] / np.linalg.norm(qf[b, h])
+        return k, v
+    a = _run(q.with_(p_running_max=True), wl1, fp4_rows=peaked, ppp=1)
+    b = _run(q, wl1, fp4_rows=peaked, ppp=1)
+    assert np.array_equal(a, b)
+    # and in general they differ (the variant is not a no-op)
+    c = _run(q.with_(p_running_max=True), wl1, fp4_rows=rows, ppp=1)
+    d = _run(q, wl1, fp4_rows=rows, ppp=1)
+    assert not np.array_equal(c, d)
