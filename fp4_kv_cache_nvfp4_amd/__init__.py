@@ -42,6 +42,7 @@ class Recipe(ctypes.Structure):
         ("c", ctypes.c_int32),
         ("tau", ctypes.c_float),
         ("rotate_v", ctypes.c_int32),
+        ("p_running_max", ctypes.c_int32),
     ]
 
     def replace(self, **kw) -> "Recipe":

@@ -74,6 +74,8 @@ bdfp4_status check_recipe(const bdfp4_recipe* r) {
                 r->sink_tokens);
   if (r->query_terms != 1 && r->query_terms != 2)
     return fail(BDFP4_E_INVALID, "query_terms must be 1 or 2, got %d", r->query_terms);
+  if (r->p_running_max != 0 && r->p_running_max != 1)
+    return fail(BDFP4_E_INVALID, "p_running_max must be 0 or 1");
   const int qm = r->scale_mode_q, pm = r->scale_mode_p;
   if (qm != BDFP4_SCALE_AMAX6 && qm != BDFP4_SCALE_MXFP4_SEARCH && qm != BDFP4_SCALE_NONE)
     return fail(BDFP4_E_INVALID, "scale_mode_q %d is not a query scale mode", qm);
@@ -97,6 +99,9 @@ bdfp4_status check_recipe(const bdfp4_recipe* r) {
     return fail(BDFP4_E_UNSUPPORTED, "NVFP4 pages take an amax6 query in this build");
   if (is_mx_kv(r) && qm != BDFP4_SCALE_MXFP4_SEARCH)
     return fail(BDFP4_E_UNSUPPORTED, "MXFP4 pages take an mxfp4_search query in this build");
+  if (r->p_running_max && (!is_nv_kv(r) || r->query_terms != 2 || pm != BDFP4_SCALE_AMAX2_OR_AMAX6))
+    return fail(BDFP4_E_UNSUPPORTED,
+                "p_running_max has a kernel for NVFP4 pages, two query terms and amax2_or_amax6 P only");
   return BDFP4_OK;
 }
 
@@ -176,6 +181,7 @@ bdfp4_status bdfp4_recipe_default_nvfp4(bdfp4_recipe* r) {
   r->sink_tokens = 16;
   r->rotation = 1;
   r->rotate_v = 0;
+  r->p_running_max = 0;
   r->key_smoothing = 1;
   r->scale_mode_k = BDFP4_SCALE_FOUR_SIX;
   r->scale_mode_v = BDFP4_SCALE_AMAX6;
@@ -466,6 +472,7 @@ bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* ca
   L.sink = r->sink_tokens;
   L.rotation = r->rotation;
   L.rotate_v = r->rotate_v;
+  L.run_max = r->p_running_max;
   L.key_smoothing = r->key_smoothing;
   L.mx = is_mx_kv(r) ? 1 : 0;
   L.k_four_six = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX;

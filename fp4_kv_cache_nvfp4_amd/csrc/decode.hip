@@ -150,6 +150,7 @@ struct Smem {
   float rcp[8];                             // RN(1 / (1 + k/8)), k = 0..7
   int bad[4];                               // per wave: its block table names an invalid page
   int tick;
+  float tmax[4][4][kWaveTok / 16];          // running-max variant: per wave, head, 16-token block: raw maximum
 };
 
 // ------------------------------------------------------------ partials
@@ -479,7 +480,7 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 // workgroup's partial (returned; the caller stores it). With bf16 the
 // workgroup also computes the (sequence, KV head)'s BF16 partition while its
 // first K page loads and folds it into the same partial.
-template <bool kMx, int kTerms, bool kUnder>
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax>
 __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -595,6 +596,14 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
       lg_b[local] = tb;
       pa = __builtin_fmaxf(pa, ta);
       pb = __builtin_fmaxf(pb, tb);
+      if (kRunMax) {
+        // the block's maximum per head (rows of 16 lanes = the tile's tokens)
+        const float xa = max16(ta), xb = max16(tb);
+        if (lane < 32 && row == 0) {
+          sm.tmax[wave][2 * hp][(pi * kPage + t * 16) >> 4] = xa;
+          sm.tmax[wave][2 * hp + 1][(pi * kPage + t * 16) >> 4] = xb;
+        }
+      }
     }
     ma = __builtin_fmaxf(ma, pa);
     mb = __builtin_fmaxf(mb, pb);
@@ -624,6 +633,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   uint32_t* pst_w = &sm.pst[wave][ph][pj];
   const u32x4_t* pst_r = reinterpret_cast<const u32x4_t*>(&sm.pst[wave][row][4 * kg]);
   float lacc = 0.0f;                 // sum of c p over this lane's tokens
+  float mrun = kNegInf;              // running-max variant: maximum of the blocks before this chunk
   f32x4_t acco[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acco[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -632,9 +642,22 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int ch = 0; ch < 4; ++ch) {
       // p' = c exp(sigma (t - m)) of tokens 2 pj, 2 pj + 1 of the chunk, head ph
       const float2 tt = *reinterpret_cast<const float2*>(lrow + pi * kPage + ch * 32);
-      const float x0 = __fmul_rn(cf, __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(tt.x, mh), ks)));
-      const float x1 = __fmul_rn(cf, __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(tt.y, mh), ks)));
-      lacc = __fadd_rn(lacc, __fadd_rn(x0, x1));
+      // the reference maximum: the partition's, or (running-max variant) the
+      // maximum over this partition's 16-token blocks up to this lane's block,
+      // with w = exp(sigma (mref - m)) weighting its P back to the partition's
+      float mref = mh, w = 1.0f;
+      if (kRunMax) {
+        const int blk = (pi * kPage + ch * 32) >> 4;
+        const float mA = __builtin_fmaxf(mrun, sm.tmax[wave][ph][blk]);
+        const float mB = __builtin_fmaxf(mA, sm.tmax[wave][ph][blk + 1]);
+        mref = pj < 8 ? mA : mB;
+        mrun = mB;
+        w = __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(mref, mh), ks));   // mref = -inf gives 0
+      }
+      const bool live = !kRunMax || mref != kNegInf;             // a block of sink slots only
+      const float x0 = live ? __fmul_rn(cf, __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(tt.x, mref), ks))) : 0.0f;
+      const float x1 = live ? __fmul_rn(cf, __builtin_amdgcn_exp2f(__fmul_rn(__fsub_rn(tt.y, mref), ks))) : 0.0f;
+      lacc = kRunMax ? __fadd_rn(lacc, __fmul_rn(__fadd_rn(x0, x1), w)) : __fadd_rn(lacc, __fadd_rn(x0, x1));
       // block maximum over the aligned 16 tokens (8 lanes); p' >= 0, so the
       // unsigned order of the bit patterns is the float order
       const float a = __uint_as_float(umax_dpp8(max(__float_as_uint(x0), __float_as_uint(x1))));
@@ -647,6 +670,12 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
         const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
         word = __builtin_amdgcn_perm(__float_as_uint(__fmul_rn(g[1], sv)), __float_as_uint(__fmul_rn(g[0], sv)),
                                      0x07060302u);
+      } else if (kRunMax) {
+        // P_hat w, rounded once to f16 (P_hat = s e2m1 is exact in float32)
+        const e2m1_f32x2_t g = e2m1_grid_pair(byte, 0);
+        const _Float16 h0 = (_Float16)__fmul_rn(__fmul_rn(g[0], sv), w);
+        const _Float16 h1 = (_Float16)__fmul_rn(__fmul_rn(g[1], sv), w);
+        word = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
       } else {
         const f16x2_t s16 = e4m3_pair_f16(sc * 0x0101u, false);
         word = u32_of(grid_f16_pair(byte, 0) * s16);
@@ -786,7 +815,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
 // partial in slot sp and takes the (sequence, KV head)'s ticket; the last of
 // the nwg merges them all. A sequence without a full page has only the BF16
 // partition, written straight to the output by its sp = 0 workgroup.
-template <bool kMx, int kTerms, bool kUnder>
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
@@ -812,7 +841,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     return;
   }
   if (sp >= nwg) return;
-  const Partial mine = fp4_wg<kMx, kTerms, kUnder>(A, sm, b, h, sp, L, sp == 0);
+  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax>(A, sm, b, h, sp, L, sp == 0);
   write_partial(partial_writer(C, bh, sp), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
@@ -826,8 +855,13 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   A.L = L;
   const dim3 grid((unsigned)(L.batch * L.hkv * fp4_wgs(L.max_parts))), block(256u);
   const bool under = L.p_mode == 4;
-#define BDFP4_LAUNCH(MX, T, U) hipLaunchKernelGGL((decode_kernel<MX, T, U>), grid, block, 0, stream, A)
-  if (L.mx) {
+#define BDFP4_LAUNCH(MX, T, U) hipLaunchKernelGGL((decode_kernel<MX, T, U, false>), grid, block, 0, stream, A)
+  if (L.run_max) {
+    // the host admits the running-max variant only for NVFP4, two query
+    // terms and amax2_or_amax6 P
+    if (L.mx || L.terms != 2 || !under) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_kernel<false, 2, true, true>), grid, block, 0, stream, A);
+  } else if (L.mx) {
     if (L.terms == 2) { if (under) BDFP4_LAUNCH(true, 2, true); else BDFP4_LAUNCH(true, 2, false); }
     else { if (under) BDFP4_LAUNCH(true, 1, true); else BDFP4_LAUNCH(true, 1, false); }
   } else {

@@ -59,7 +59,7 @@ hipError_t launch_p_blocks(const float* pp, int n_blocks, int mode, float tau, u
 
 struct DecodeLaunch {
   // recipe
-  int32_t sink, rotation, key_smoothing, mx, k_four_six, p_mode, terms, c, rotate_v;
+  int32_t sink, rotation, key_smoothing, mx, k_four_six, p_mode, terms, c, rotate_v, run_max;
   float tau;
   // cache
   const uint8_t* k_codes;

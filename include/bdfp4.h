@@ -86,6 +86,12 @@ typedef struct {
   int32_t rotate_v;      /* recipe variant, 0 in both modes: 1 rotates values
                             with the same Hadamard rotation before they are
                             quantized, and the decode rotates its output back */
+  int32_t p_running_max; /* recipe variant, 0 in both modes: 1 normalises the
+                            P of each 16-token block by the running maximum
+                            over the partition's blocks up to it (one-pass
+                            softmax) instead of the partition maximum, and
+                            weights it back; NVFP4 K/V, two query terms and
+                            AMAX2_OR_AMAX6 only (else E_UNSUPPORTED)          */
 } bdfp4_recipe;
 
 /* The quantized paged cache. Each of the four arrays is dense

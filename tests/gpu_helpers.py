@@ -40,6 +40,7 @@ def to_c(r: RC.Recipe) -> bd.Recipe:
     c.c = r.c
     c.tau = float(r.tau)
     c.rotate_v = int(r.rotate_v)
+    c.p_running_max = int(r.p_running_max)
     return c
 
 

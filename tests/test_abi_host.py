@@ -81,7 +81,7 @@ def test_recipe_validation_follows_probability_environment():
 @pytest.mark.parametrize("field,value,status", [
     ("sink_tokens", 8, bd.E_INVALID), ("sink_tokens", 128, bd.E_INVALID), ("sink_tokens", -16, bd.E_INVALID),
     ("query_terms", 3, bd.E_INVALID), ("rotation", 2, bd.E_INVALID), ("key_smoothing", 5, bd.E_INVALID),
-    ("rotate_v", 2, bd.E_INVALID),
+    ("rotate_v", 2, bd.E_INVALID), ("p_running_max", 3, bd.E_INVALID),
     ("scale_mode_k", 9, bd.E_INVALID), ("scale_mode_v", bd.SCALE_FOUR_SIX, bd.E_INVALID),
     ("scale_mode_p", 7, bd.E_INVALID), ("scale_mode_p", bd.SCALE_NONE, bd.E_UNSUPPORTED),
     ("scale_mode_q", bd.SCALE_MXFP4_SEARCH, bd.E_UNSUPPORTED),
@@ -282,3 +282,14 @@ def test_page_errors_reject_before_launch():
     assert call(mu=None) == bd.E_INVALID
     assert call(out=FAKE + 4) == bd.E_INVALID
     assert call(r.replace(scale_mode_v=bd.SCALE_MXFP4_SEARCH)) == bd.E_UNSUPPORTED
+
+
+def test_running_max_variant_combinations():
+    nv = bd.recipe_default_nvfp4(tau=1.0)
+    bd.recipe_validate(nv.replace(p_running_max=1))
+    for r in (bd.recipe_default_mxfp4(tau=1.0).replace(p_running_max=1),
+              nv.replace(p_running_max=1, query_terms=1),
+              nv.replace(p_running_max=1, scale_mode_p=bd.SCALE_AMAX6)):
+        with pytest.raises(bd.Bdfp4Error) as ei:
+            bd.recipe_validate(r)
+        assert ei.value.status == bd.E_UNSUPPORTED

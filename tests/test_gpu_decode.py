@@ -3,7 +3,8 @@ quantized operands and the same split plan: max-abs <= 2e-3 and relative L2
 <= 1e-3 on float32 outputs. Covers the tiny 2K case, ragged batches (sink
 only, sink + tail, several partitions with a ragged last one), sink lengths,
 the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode,
-rotated values (NVFP4 and MXFP4, ragged batch included), the
+rotated values (NVFP4 and MXFP4, ragged batch included), P normalised by
+the running block maximum (ragged batches with sink 16 and 112 included), the
 32K Qwen3-4B-shaped layer with a 77-token tail, the full 128K layer in the
 benchmark's launch configuration (two KV heads sampled), 16 sequences of
 2K..16K tokens (two sampled), determinism, paging
@@ -48,12 +49,13 @@ def test_tiny_2k_mxfp4():
 
 
 @pytest.mark.parametrize("variant", ["terms1", "c1", "tau0", "p_amax6", "k_amax6", "norot", "nosmooth", "rotv",
-                                     "rotv_mx"])
+                                     "rotv_mx", "runmax", "runmax_tau0"])
 def test_recipe_variants(variant):
     r = {"terms1": NV.with_(query_terms=1), "c1": NV.with_(c=1), "tau0": NV.with_(tau=0.0),
          "p_amax6": NV.with_(scale_mode_p=Q.AMAX6), "k_amax6": NV.with_(scale_mode_k=Q.AMAX6),
          "norot": NV.with_(rotation=False), "nosmooth": NV.with_(key_smoothing=False),
-         "rotv": NV.with_(rotate_v=True), "rotv_mx": MX.with_(rotate_v=True)}[variant]
+         "rotv": NV.with_(rotate_v=True), "rotv_mx": MX.with_(rotate_v=True),
+         "runmax": NV.with_(p_running_max=True), "runmax_tau0": NV.with_(p_running_max=True, tau=0.0)}[variant]
     wl = synth.decode_workload("v", 3, [1500, 777], 8, 2, "qwen", extra_pages=1)
     _run(r, wl, 2, variant)
 
@@ -70,6 +72,13 @@ def test_ragged_batch_rotated_values():
     # whose merged output is rotated back
     wl = synth.decode_workload("r", 6, [1, 100, 300, 2049, 640], 8, 2, "qwen", extra_pages=2)
     _run(NV.with_(rotate_v=True), wl, 3, "ragged rotate_v")
+
+
+@pytest.mark.parametrize("sink", [16, 112])
+def test_ragged_batch_running_max(sink):
+    # leading blocks of sink slots only (no running maximum yet), ragged tails
+    wl = synth.decode_workload("r", 7, [1, 100, 300, 2049, 640], 8, 2, "qwen", extra_pages=2, sink_tokens=sink)
+    _run(NV.with_(p_running_max=True, sink_tokens=sink), wl, 3, f"ragged running max sink={sink}")
 
 
 def test_ragged_batch_mxfp4():

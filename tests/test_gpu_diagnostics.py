@@ -74,7 +74,8 @@ def _from_c(rc) -> RC.Recipe:
     return RC.Recipe(sink_tokens=rc.sink_tokens, rotation=bool(rc.rotation), key_smoothing=bool(rc.key_smoothing),
                      scale_mode_k=mode[rc.scale_mode_k], scale_mode_v=mode[rc.scale_mode_v],
                      scale_mode_q=mode[rc.scale_mode_q], scale_mode_p=mode[rc.scale_mode_p],
-                     query_terms=rc.query_terms, c=rc.c, tau=float(rc.tau), rotate_v=bool(rc.rotate_v))
+                     query_terms=rc.query_terms, c=rc.c, tau=float(rc.tau), rotate_v=bool(rc.rotate_v),
+                     p_running_max=bool(rc.p_running_max))
 
 
 def test_ablation_report_matches_oracle():
