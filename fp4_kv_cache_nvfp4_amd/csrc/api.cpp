@@ -237,8 +237,10 @@ bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cach
   if (!r->key_smoothing && key_shift != nullptr)
     return fail(BDFP4_E_INVALID, "key_shift given but key_smoothing is off");
   if (key_shift && !aligned16(key_shift)) return fail(BDFP4_E_INVALID, "key_shift must be 16-byte aligned");
-  if ((int64_t)n_pages * cache->num_kv_heads > 0x7FFFFFFF)
-    return fail(BDFP4_E_INVALID, "too many pages in one call");
+  // one 256-thread workgroup per (page, KV head): the grid's work-items
+  // along x must stay below 2^32
+  if ((int64_t)n_pages * cache->num_kv_heads >= ((int64_t)1 << 24))
+    return fail(BDFP4_E_INVALID, "too many pages in one call (n_pages * num_kv_heads must be < 2^24)");
   bdfp4::WriterLaunch L;
   L.k = k_bf16;
   L.v = v_bf16;

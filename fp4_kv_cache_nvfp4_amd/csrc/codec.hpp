@@ -147,6 +147,17 @@ __device__ __forceinline__ uint32_t e2m1_pair(float x0, float x1, float s, float
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quot(x0, m, r), quot(x1, m, r), s, 0) & 0xFFu;
 }
 
+// The same two codes written into byte `byte` of old (the other bytes of
+// old are kept; the select must be a constant).
+__device__ __forceinline__ uint32_t e2m1_pair_into(uint32_t old, float q0, float q1, float s, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, s, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, s, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, s, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, s, 3);
+  }
+}
+
 typedef float e2m1_f32x2_t __attribute__((ext_vector_type(2)));
 
 // Signed grid values (exact float32) of the two E2M1 codes in byte `byte`
@@ -214,6 +225,55 @@ __device__ __forceinline__ float quant_block(const float* x, float s, uint32_t* 
   return lvl[kLv - 1];
 }
 
+// The same for a scale value s that is either 0 or a normal float32, as every
+// E4M3 value is (the least nonzero one is 2^-9): every pair takes the exact-quotient
+// route, written by the down-convert straight into its byte of the packed
+// word (the convert leaves the other three bytes as they were); a zero scale
+// selects all-zero codes afterwards. The error term |x| - s |g| is one FMA,
+// since s |g| is exact (at most 6 significant bits), so it rounds exactly as
+// the subtraction of the rounded product does.
+// kPow2: s is a power of two 2^E with E >= -126 (a normal E8M0 scale), so the
+// quotient by the significand is x itself and the convert alone is exact.
+template <int N, bool kSse, bool kPow2 = false>
+__device__ __forceinline__ float quant_block_normal(const float* x, float s, uint32_t* packed) {
+  static_assert(N % 8 == 0, "whole packed words");
+  constexpr int kLv = N == 32 ? 6 : (N == 16 ? 5 : 4);
+  constexpr int kW = N / 8;
+  const float m = significand(s);               // 1 for s = 0
+  const float r = rcp_significand(sig_index(s));
+  const bool live = s > 0.0f;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    uint32_t word = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float x0 = x[8 * w + 2 * b], x1 = x[8 * w + 2 * b + 1];
+      word = kPow2 ? e2m1_pair_into(word, x0, x1, s, b) : e2m1_pair_into(word, quot(x0, m, r), quot(x1, m, r), s, b);
+    }
+    packed[w] = (kPow2 || live) ? word : 0u;
+  }
+  if (!kSse) return 0.0f;
+  float lvl[kLv];
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    const e2m1_f32x2_t gp = e2m1_grid_pair(packed[i >> 3], (i & 7) >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ie = i + e;
+      const float d = __builtin_fmaf(-__builtin_fabsf(gp[e]), s, __builtin_fabsf(x[ie]));
+      float v = __fmul_rn(d, d);
+      int k = 0;
+#pragma unroll
+      for (int bit = 1; bit < N; bit <<= 1, ++k) {
+        if ((ie & bit) == 0) break;
+        v = __fadd_rn(lvl[k], v);
+      }
+      lvl[k] = v;
+    }
+  }
+  return lvl[kLv - 1];
+}
+
 // Scale code of an aligned 16-value block of p' = c p with block maximum
 // a >= 0: E4M3(a / 2) when kUnder and a < tau (amax2_or_amax6), otherwise
 // E4M3(a / 6) (amax6).
@@ -235,14 +295,14 @@ __device__ __forceinline__ uint32_t nv_block(const float* x, uint32_t* packed) {
   const float a = absmax16(x);
   const uint32_t c6 = e4m3_encode(div6(a));
   if (!kFourSix) {
-    quant_block<16, false>(x, e4m3_value(c6), packed);
+    quant_block_normal<16, false>(x, e4m3_value(c6), packed);
     return c6;
   }
   const uint32_t c4 = e4m3_encode(a * 0.25f);
   uint32_t p6[2], p4[2];
-  const float err6 = quant_block<16, true>(x, e4m3_value(c6), p6);
+  const float err6 = quant_block_normal<16, true>(x, e4m3_value(c6), p6);
   __builtin_amdgcn_sched_barrier(0);   // keep the two candidates from interleaving
-  const float err4 = quant_block<16, true>(x, e4m3_value(c4), p4);
+  const float err4 = quant_block_normal<16, true>(x, e4m3_value(c4), p4);
   const bool take4 = err4 < err6;
   packed[0] = take4 ? p4[0] : p6[0];
   packed[1] = take4 ? p4[1] : p6[1];
@@ -263,9 +323,17 @@ __device__ __forceinline__ uint32_t mx_block(const float* x, uint32_t* packed) {
   ehi = ehi < -127 ? -127 : (ehi > 127 ? 127 : ehi);
   const int elo = ehi - 1 < -127 ? -127 : ehi - 1;
   uint32_t phi[4], plo[4];
-  const float err_hi = quant_block<32, true>(x, pow2_f32(ehi), phi);
-  __builtin_amdgcn_sched_barrier(0);   // keep the two candidates from interleaving
-  const float err_lo = quant_block<32, true>(x, pow2_f32(elo), plo);
+  float err_hi, err_lo;
+  if (elo >= -126) {
+    // both scales normal powers of two: the direct convert
+    err_hi = quant_block_normal<32, true, true>(x, pow2_f32(ehi), phi);
+    __builtin_amdgcn_sched_barrier(0);   // keep the two candidates from interleaving
+    err_lo = quant_block_normal<32, true, true>(x, pow2_f32(elo), plo);
+  } else {
+    // a candidate at the float32 subnormal 2^-127: the threshold search
+    err_hi = quant_block<32, true>(x, pow2_f32(ehi), phi);
+    err_lo = quant_block<32, true>(x, pow2_f32(elo), plo);
+  }
   const bool take_lo = (err_lo < err_hi) && (elo < ehi);
 #pragma unroll
   for (int w = 0; w < 4; ++w) packed[w] = take_lo ? plo[w] : phi[w];
@@ -332,13 +400,18 @@ __device__ __forceinline__ float sum16(float v) {
 
 // Cross-lane butterfly stage: the lane whose selector bit is clear keeps
 // own + partner, the other partner - own (the (a+b, a-b) pair of the stage).
+// Written as partner + (+-own): the upper lane's p - x is p + (-x) exactly,
+// and the DPP read folds into the addition.
+// All sign flips are formed first, so that no DPP read follows closely on
+// the write of its register.
 template <int N, int kCtrl>
 __device__ __forceinline__ void fwht_xlane(float* x, bool upper) {
+  const uint32_t flip = upper ? 0x80000000u : 0u;
+  float own[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float p = dpp_f32<kCtrl>(x[i]);
-    x[i] = upper ? __fsub_rn(p, x[i]) : __fadd_rn(x[i], p);
-  }
+  for (int i = 0; i < N; ++i) own[i] = __uint_as_float(__float_as_uint(x[i]) ^ flip);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = __fadd_rn(dpp_f32<kCtrl>(x[i]), own[i]);
 }
 
 // Rotation of a 128-element row held as 32 consecutive elements per lane in

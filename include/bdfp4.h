@@ -154,7 +154,8 @@ bdfp4_status bdfp4_cache_bytes(const bdfp4_recipe* r, int32_t num_pages,
  * Keys: x = float32(k) - mu, y = H x / sqrt(128) (fast Walsh-Hadamard,
  * stages h = 1..64, float32), then scale_mode_k. Values: scale_mode_v on
  * float32(v), no rotation. Codes and scales are bit-exact functions of the
- * inputs. n_pages = 0 is a no-op. */
+ * inputs. n_pages = 0 is a no-op; n_pages * num_kv_heads >= 2^24 (more than
+ * one call's grid holds) -> E_INVALID. */
 bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cache,
                                   const void* k_bf16, const void* v_bf16,
                                   const int32_t* page_ids, int32_t n_pages,

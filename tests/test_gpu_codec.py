@@ -66,6 +66,28 @@ def test_rows_bit_exact(mode, rotation, shift, terms):
         assert np.array_equal(gs[:, t], sc.astype(np.uint8)), f"scales term {t}"
 
 
+@pytest.mark.parametrize("mode", [Q.AMAX6, Q.FOUR_SIX, Q.MXFP4_SEARCH])
+def test_rows_bit_exact_near_float32_underflow(mode):
+    # block maxima around 2^-126: MXFP4 candidates at the float32 subnormal
+    # 2^-127 (the threshold search), beside normal power-of-two candidates;
+    # E4M3 scales of such blocks are zero
+    rng = np.random.default_rng(5)
+    n = 300
+    x = rng.standard_normal((n, 128)).astype(np.float32) * np.float32(2.0 ** -122)
+    x[1::3] *= np.float32(2.0 ** -4)
+    x[2::3] *= np.float32(2.0 ** -7)
+    u = synth.f32_to_bf16(x)
+    cmode = {Q.AMAX6: bd.SCALE_AMAX6, Q.FOUR_SIX: bd.SCALE_FOUR_SIX, Q.MXFP4_SEARCH: bd.SCALE_MXFP4_SEARCH}[mode]
+    nb = 4 if mode == Q.MXFP4_SEARCH else 8
+    codes = torch.zeros((n, 1, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((n, 1, nb), dtype=torch.uint8, device="cuda")
+    bd.quantize_rows(dev_bf16(u), None, 0, cmode, 1, codes, scales)
+    torch.cuda.synchronize()
+    nib, sc = Q.quantize(W.key_rows(F.bf16_to_f32(u), None, False), mode)
+    assert np.array_equal(codes.cpu().numpy()[:, 0], _pack_logical(nib))
+    assert np.array_equal(scales.cpu().numpy()[:, 0], sc.astype(np.uint8))
+
+
 def _p_blocks(seed, n):
     rng = np.random.default_rng(seed)
     p = np.exp(-rng.exponential(2.0, size=(n, 16)))
