@@ -25,14 +25,18 @@
 //    wave then issues its first two K page loads;
 //  * prologue: wave g rotates (128-point Hadamard, float32) and quantizes
 //    query row g as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32), two
-//    elements per lane; the dequantized terms are exact in 16 bits and become
-//    the A operands of v_mfma_f32_16x16x32_{f16,bf16}: row 2g + t holds term
-//    t of head g and rows 8..15 repeat rows 0..7. q . mu (raw float32 query,
-//    key means) seeds the term-1 rows of the accumulator.
+//    elements per lane. NVFP4: the dequantized terms are exact in 16 bits
+//    and become the A operands of v_mfma_f32_16x16x32_f16; MXFP4: the codes
+//    and E8M0 scale codes themselves are the A operand of the scaled FP4
+//    MFMA. Row 2g + t holds term t of head g and rows 8..15 repeat rows
+//    0..7. q . mu (raw float32 query, key means) seeds the term-1 rows of the
+//    accumulator.
 //  * pass 1 (QK^T): the wave streams its K pages with two pages in flight;
 //    per 16-token tile a lane holds 16 code bytes (one coalesced 1 KiB run
 //    per wave) and the page's scales come in one 16-byte load per lane. Four
-//    MFMAs give both terms of all four heads; their sum, the raw logit
+//    f16 MFMAs (NVFP4) or one v_mfma_scale_f32_16x16x128_f8f6f4 (MXFP4: the
+//    page's code bytes and E8M0 scales used as they are) give both terms of
+//    all four heads; their sum, the raw logit
 //    q . mu + q_hat . k_hat, goes to the wave's LDS rows [head][token]. Sink
 //    tokens fill whole tiles of the first page and get -inf.
 //  * the partition maximum of each head (DPP within 16 lanes, then lanes).
@@ -52,10 +56,13 @@
 // is the code of the exact ratio p' / s (see quot and e2m1_pair).
 //
 // Operand construction. The scaled FP4 converts of gfx950 apply only the
-// exponent of their float32 scale. MXFP4 scales are powers of two and convert
-// exactly to bf16 in one step. For NVFP4 the codes are converted with scale 1
-// to f16 and multiplied, two at a time, by their E4M3 scales converted to f16
-// by the hardware E4M3 convert; the product has at most 6 significant bits and
+// exponent of their float32 scale. MXFP4 scales are powers of two: K and the
+// query enter the scaled FP4 MFMA as codes, and V converts exactly to bf16 in
+// one step (its E8M0 scales run along the channels, not along the token sum
+// whose blocks the MFMA's scales would have to follow). For NVFP4 the codes
+// are converted with scale 1 to f16 and multiplied, two at a time, by their
+// E4M3 scales converted to f16 by the hardware E4M3 convert; the product has
+// at most 6 significant bits and
 // lies in [2^-10, 2688], so it is exact in f16. The NVFP4 V page stores tokens
 // t, t+1 of one channel in a byte, so a converted pair is directly one 32-bit
 // word of the PV B operand.
@@ -122,6 +129,31 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+// D += (A 2^(sa - 127)) (B 2^(sb - 127)) on a 16x16x128 tile of E2M1 codes
+// (v_mfma_scale_f32_16x16x128_f8f6f4, both operands FP4): lane l supplies
+// row / column l & 15, channels 32 (l >> 4) .. +32 as 16 bytes (element 2i in
+// the low nibble) and the E8M0 code of that 32-channel block; sa is byte 0
+// of its word, sb byte kSel of its word. The products are exact, the sums
+// float32.
+template <int kSel>
+__device__ __forceinline__ f32x4_t mfma_fp4_scaled(u32x4_t a, uint32_t sa, u32x4_t b, uint32_t sb, f32x4_t c) {
+  const i32x8_t a8 = {(int32_t)a[0], (int32_t)a[1], (int32_t)a[2], (int32_t)a[3], 0, 0, 0, 0};
+  const i32x8_t b8 = {(int32_t)b[0], (int32_t)b[1], (int32_t)b[2], (int32_t)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, (int32_t)sa, kSel, (int32_t)sb);
+}
+
+__device__ __forceinline__ f32x4_t mfma_fp4_scaled_byte(int sel, u32x4_t a, uint32_t sa, u32x4_t b, uint32_t sb,
+                                                        f32x4_t c) {
+  switch (sel) {
+    case 0: return mfma_fp4_scaled<0>(a, sa, b, sb, c);
+    case 1: return mfma_fp4_scaled<1>(a, sa, b, sb, c);
+    case 2: return mfma_fp4_scaled<2>(a, sa, b, sb, c);
+    default: return mfma_fp4_scaled<3>(a, sa, b, sb, c);
+  }
+}
+
 // 16-bit operand bits of an exactly representable float32 value.
 template <bool kMx>
 __device__ __forceinline__ uint32_t op16(float v) {
@@ -143,6 +175,8 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
 struct Smem {
   float logit[4][4 * kWaveTok];             // per wave: [head][token] raw logits; then its o [head][128]
   uint16_t qhat[2][4][kD];                  // 16-bit dequantized query terms [term][head][channel]
+  uint8_t qcode[2][4][kD / 2];              // MXFP4: E2M1 codes of the query terms [term][head][byte]
+  uint32_t qsc[2][4][4];                    // MXFP4: their E8M0 scale codes [term][head][32-channel block]
   uint32_t pst[4][16][16];                  // per wave: P_hat staging [row][token pair]; rows 4..15 stay 0
   float qmu[4];
   float red[4][4];                          // per wave, per head: partition maximum (raw logit)
@@ -395,6 +429,10 @@ __device__ __forceinline__ void query_prologue(const DecodeLaunch& P, uint32_t q
       const bool take_lo = (elo_err < ehi_err) && (elo < ehi) && a > 0.0f;
       s = a > 0.0f ? pow2_f32(take_lo ? elo : ehi) : 0.0f;
       pk = a > 0.0f ? (take_lo ? plo : phi) : 0u;
+      // the codes and the E8M0 code (in [0, 254]; an all-zero block's codes
+      // are zero whatever its scale) are the scaled FP4 MFMA's A operand
+      sm.qcode[term][g][i] = (uint8_t)pk;
+      if ((i & 15) == 0) sm.qsc[term][g][i >> 4] = (uint32_t)((take_lo ? elo : ehi) + 127);
     } else {
       // 16-element block = 8 lanes
       a = max8(a);
@@ -408,7 +446,7 @@ __device__ __forceinline__ void query_prologue(const DecodeLaunch& P, uint32_t q
       const float gv = __fmul_rn(e2m1_grid(nib & 7u), s);
       deq[k] = (nib & 8u) ? -gv : gv;
     }
-    reinterpret_cast<uint32_t*>(&sm.qhat[term][g][0])[i] = op16<kMx>(deq[0]) | (op16<kMx>(deq[1]) << 16);
+    if (!kMx) reinterpret_cast<uint32_t*>(&sm.qhat[term][g][0])[i] = op16<kMx>(deq[0]) | (op16<kMx>(deq[1]) << 16);
     x0 = __fsub_rn(x0, deq[0]);
     x1 = __fsub_rn(x1, deq[1]);
   }
@@ -537,11 +575,20 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if ((qr & 1) < kTerms) {
+    if (!kMx && (qr & 1) < kTerms) {
       const uint4 t = *reinterpret_cast<const uint4*>(&sm.qhat[qr & 1][qr >> 1][32 * kg + 8 * c]);
       v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     }
     aq[c] = v;
+  }
+  // MXFP4: the query's E2M1 codes (channels 32 kg .. +32) and E8M0 code,
+  // one scaled FP4 MFMA per 16-token tile
+  u32x4_t aq4 = {0u, 0u, 0u, 0u};
+  uint32_t sa4 = 127u;
+  if (kMx && (qr & 1) < kTerms) {
+    const uint4 t = *reinterpret_cast<const uint4*>(&sm.qcode[qr & 1][qr >> 1][16 * kg]);
+    aq4 = (u32x4_t){t.x, t.y, t.z, t.w};
+    sa4 = sm.qsc[qr & 1][qr >> 1][kg];
   }
   // D lane l holds rows 4 (l >> 4) + i: lanes 0..15 (and 32..47) heads 0, 1,
   // lanes 16..31 (and 48..63) heads 2, 3; term 1 in i = 0, 2, term 2 in
@@ -566,15 +613,12 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int t = 0; t < 8; ++t) {
       const int local = pi * kPage + t * 16;                    // first token of the tile - 128 p0
       u32x4_t bk[4];
+      f32x4_t acc = acc0;
       if (kMx) {
-        const uint32_t sb = (word_of(cur.sc, t >> 2) >> (8 * (t & 3))) & 0xFFu;
-        const float sv = __uint_as_float(sb << 23);             // E8M0: only the exponent field is used
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t cw = word_of(cur.code[t], c);
-          bk[c] = (u32x4_t){cvt_bf16_pair(cw, sv, 0), cvt_bf16_pair(cw, sv, 1), cvt_bf16_pair(cw, sv, 2),
-                            cvt_bf16_pair(cw, sv, 3)};
-        }
+        // the page's codes are the B operand as they are; byte t & 3 of
+        // scale word t >> 2 is this lane's (token, channel block) E8M0 code
+        const uint4 cw = cur.code[t];
+        acc = mfma_fp4_scaled_byte(t & 3, aq4, sa4, (u32x4_t){cw.x, cw.y, cw.z, cw.w}, word_of(cur.sc, t >> 2), acc);
       } else {
         const f16x2_t sp2 = e4m3_pair_f16(word_of(cur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
         const f16x2_t slo = {sp2[0], sp2[0]}, shi = {sp2[1], sp2[1]};
@@ -586,9 +630,10 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
                             u32_of(grid_f16_pair(cw, 2) * sc), u32_of(grid_f16_pair(cw, 3) * sc)};
         }
       }
-      f32x4_t acc = acc0;
+      if (!kMx) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc = mfma<kMx>(aq[c], bk[c], acc);
+        for (int c = 0; c < 4; ++c) acc = mfma<kMx>(aq[c], bk[c], acc);
+      }
       const bool sink = t < skip;                               // uniform: a sink tile of page 0
       const float ta = sink ? kNegInf : __fadd_rn(acc[0], acc[1]);
       const float tb = sink ? kNegInf : __fadd_rn(acc[2], acc[3]);
