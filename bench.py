@@ -83,6 +83,9 @@ def writer_bytes(tokens: int, hkv: int, mx: bool) -> int:
 
 # ----------------------------------------------------------------- timing
 
+LAST_PERCENTILES = {"p10": None, "p90": None}   # of the per-launch durations of the last time_launches
+
+
 def time_launches(fns, steps: int, warmup: int, graph: bool = False):
     """Run `warmup` untimed steps, then exactly `steps` timed steps of the
     launches in `fns` on the current stream. Returns (ms per step, mean ms per
@@ -136,6 +139,7 @@ def time_launches(fns, steps: int, warmup: int, graph: bool = False):
             evs.append((a, b))
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
+    LAST_PERCENTILES["p10"], LAST_PERCENTILES["p90"] = (float(v) for v in np.percentile(per, [10, 90]))
     return ms_step, float(np.mean(per)), wall, float(np.median(per))
 
 
@@ -459,7 +463,8 @@ def main():
         nb = (bf16_decode_bytes(args.context, 32, 8) if a == "bf16"
               else decode_bytes(args.context, 32, 8, 16, a == "mxfp4"))
         res[a] = {"ms_per_step": ms, "us_per_layer": ms * 1e3 / args.layers, "us_kernel_events": per * 1e3,
-                  "us_kernel_events_median": med * 1e3, "wall_ms_per_step": wall,
+                  "us_kernel_events_median": med * 1e3, "us_kernel_events_p10": LAST_PERCENTILES["p10"] * 1e3,
+                  "us_kernel_events_p90": LAST_PERCENTILES["p90"] * 1e3, "wall_ms_per_step": wall,
                   "bytes_per_layer": nb, "GBps": nb * args.layers / (ms * 1e-3) / 1e9,
                   "kernel_GBps": nb / (per * 1e-3) / 1e9}
         print(f"[bench] {a}: {ms * 1e3:.1f} us/step, {res[a]['GBps']:.0f} GB/s, kernel "
@@ -519,7 +524,7 @@ def main():
                    "pages_per_partition": ppp, "partitions": parts, "graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": "bdfp4::decode_kernel<false,2,true>",
+                     "kernel": "bdfp4::decode_kernel<false,2,true,false>",
                      "bytes_per_launch": h["bytes_per_layer"], "us_per_launch": round(us_launch, 3),
                      "us_per_launch_single_events": round(h["us_kernel_events"], 3),
                      "read_ceiling": ceiling,

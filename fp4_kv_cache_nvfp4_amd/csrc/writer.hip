@@ -178,8 +178,12 @@ __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows,
   }
 }
 
+// At least 3 (MXFP4) / 4 (NVFP4) waves per SIMD: the MXFP4 body would take
+// 171 VGPRs (2 waves) unbounded and fits 168 without spilling; NVFP4 fits
+// 4 waves as it is (at 5 it would spill).
 template <int kKMode, int kVMode>
-__global__ void __launch_bounds__(256) writer_kernel(WriterArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kKMode == 3 ? 3 : 4)))
+writer_kernel(WriterArgs a) {
   __shared__ __align__(16) uint8_t s_codes[8192];
   __shared__ __align__(16) uint8_t s_scales[1024];
   const int ph = blockIdx.x;       // input page * hkv + head
