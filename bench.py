@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny 2K and the 32K single-layer decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,33 +184,55 @@ def bench_batched(args):
     over one shuffled pool (32 query / 8 KV heads), the library's plan for
     the batch: one launch per step. Bytes = the sum of every sequence's
     decode bytes."""
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    return bench_workload(args, synth.batched(0),
+                          "16 sequences, L ~ U{2048..16384} (seed 0), shared shuffled pool")
+
+
+def bench_small_configs(args):
+    """The two single-layer decode shapes beside the 128K one: the tiny 2K
+    single-KV-head case (4 query heads; launch-bound, so its µs is the
+    figure) and the Qwen3-4B-shaped 32K layer (256 full pages in a permuted
+    pool plus a 77-token BF16 tail), each with the library's plan."""
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    return {"tiny_2k_1kv": bench_workload(args, synth.tiny(0), "1 sequence, L = 2048, 1 KV head / 4 query heads"),
+            "qwen3_4b_32k_layer": bench_workload(args, synth.qwen_32k(0),
+                                                 "1 sequence, L = 32,845 (256 pages + 77-token tail), 8 KV / 32 query heads")}
+
+
+def bench_workload(args, wl, what: str):
+    """NVFP4 decode of a seeded numpy workload (pages written by the HIP
+    writer, then one launch per step, the library's plan)."""
     import torch
 
     import fp4_kv_cache_nvfp4_amd as bd
-    from fp4_kv_cache_nvfp4_amd import synth
 
-    wl = synth.batched(0)
     r = bd.recipe_default_nvfp4(tau=1.0)
     B, msl = wl.batch, int(wl.seq_lens.max())
-    ppp, parts = bd.decode_plan(B, 8, msl, 0)
+    hq, hkv = int(wl.q.shape[1]), int(wl.num_kv_heads)
+    ppp, parts = bd.decode_plan(B, hkv, msl, 0)
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     k, v, ids = wl.writer_inputs()
-    cache = bd.PagedCache.allocate(r, wl.num_pages, 8)
+    cache = bd.PagedCache.allocate(r, wl.num_pages, hkv)
     mu = t(wl.key_shift)
     bd.quantize_pages(r, cache, t16(k), t16(v), t(ids), mu)
     sk, sv, tk, tv = wl.sink_tail()
-    ws = bd.alloc_workspace(bd.decode_workspace_size(B, 32, 8, msl, ppp))
-    out = torch.empty((B, 32, 128), dtype=torch.float32, device="cuda")
+    ws = bd.alloc_workspace(bd.decode_workspace_size(B, hq, hkv, msl, ppp))
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     call = bd.DecodeCall(r, cache, t16(wl.q), t(wl.block_tables), t(wl.seq_lens), msl, t16(sk), t16(sv),
                          t16(tk), t16(tv), mu, wl.sigma, ppp, ws, out)
     ms, per, _, med = time_launches([call], max(args.steps, 20), args.warmup)
-    nbytes = sum(decode_bytes(int(L), 32, 8, 16, False) for L in wl.seq_lens)
+    if not torch.isfinite(out).all():
+        raise RuntimeError(f"{what}: non-finite decode output")
+    nbytes = sum(decode_bytes(int(L), hq, hkv, 16, False) for L in wl.seq_lens)
     del cache
     torch.cuda.empty_cache()
-    return {"workload": "16 sequences, L ~ U{2048..16384} (seed 0), shared shuffled pool",
-            "tokens": int(wl.seq_lens.sum()), "pages_per_partition": ppp, "max_partitions": parts,
-            "us": round(ms * 1e3, 3), "bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+    return {"workload": what, "tokens": int(wl.seq_lens.sum()), "pages_per_partition": ppp,
+            "max_partitions": parts, "us": round(ms * 1e3, 3), "us_kernel_events_median": round(med * 1e3, 3),
+            "bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
@@ -484,6 +507,11 @@ def main():
     if not args.no_batched:
         batched = bench_batched(args)
         print(f"[bench] batched: {batched}", file=sys.stderr, flush=True)
+    small = {}
+    if not args.no_small:
+        small = bench_small_configs(args)
+        for k, v in small.items():
+            print(f"[bench] {k}: {v['us']:.2f} us, {v['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     append = {}
     if not args.no_append:
         for batch in (1, 64):
@@ -533,6 +561,7 @@ def main():
         "arms": {a: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in res[a].items()} for a in res},
         "writer_131072x8": writer,
         "batched_16x_2k_16k": batched,
+        "single_layer_configs": small,
         "append_x8_heads": append,
         "calibration_diagnostics": calibration,
     }

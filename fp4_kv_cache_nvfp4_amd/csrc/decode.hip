@@ -518,8 +518,37 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 // workgroup's partial (returned; the caller stores it). With bf16 the
 // workgroup also computes the (sequence, KV head)'s BF16 partition while its
 // first K page loads and folds it into the same partial.
+// What a wave of an FP4 workgroup reads before anything else, issued at the
+// start of the kernel so that these loads, the sequence length and the
+// kernel arguments share one memory round trip instead of following each
+// other: lane i's block-table entry of the wave's partition (page p0 + i,
+// for i < pages_per_partition inside the table's row, else 0), the wave's
+// query row (two bf16 per lane) and the key means (from a zero row without
+// smoothing, so the load is unconditional and no branch waits on it).
+struct Early {
+  int pid;
+  uint32_t qw;
+  float2 mu;
+};
+
+// Key means of a call without key smoothing: zero (static storage), so the
+// key-mean load is the same unconditional load either way.
+__device__ float g_zero_means[kD];
+
+__device__ __forceinline__ Early early_loads(const DecodeLaunch& P, int b, int h, int sp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Early E;
+  const int pg = (4 * sp + wave) * P.ppp + lane;
+  E.pid = (lane < P.ppp && pg < P.max_pages_per_seq) ? P.block_tables[(size_t)b * P.max_pages_per_seq + pg] : 0;
+  const uint16_t* qrow = P.q + ((size_t)b * P.hq + h * kGroup + wave) * kD;
+  E.qw = reinterpret_cast<const uint32_t*>(qrow)[lane];
+  const float* mp = P.key_smoothing ? P.key_shift + h * kD : g_zero_means;
+  E.mu = reinterpret_cast<const float2*>(mp)[lane];
+  return E;
+}
+
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax>
-__device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16) {
+__device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16, const Early& E) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_full = L / kPage;
@@ -527,19 +556,17 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   const int npg = max(0, min(n_full, p0 + P.ppp) - p0);         // its pages, 0 .. pages_per_partition
   const size_t hkv = P.hkv;
 
-  // physical pages of the partition: lane i < npg holds page p0 + i
-  int pid = 0;
-  if (lane < npg) pid = P.block_tables[(size_t)b * P.max_pages_per_seq + p0 + lane];
+  // physical pages of the partition: lane i < npg holds page p0 + i (read
+  // before the sequence length was known; lanes past npg are dropped here)
+  int pid = lane < npg ? E.pid : 0;
   const bool bad_lane = lane < npg && (pid < 0 || pid >= P.num_pages);
   const bool bad = __ballot(bad_lane) != 0;
   if (bad_lane) pid = 0;                                        // keep addresses inside the cache
   auto blk_of = [&](int pi) -> size_t { return (size_t)__builtin_amdgcn_readlane(pid, pi) * hkv + h; };
 
   // the query row of this wave and the key means
-  const uint32_t qw =
-      reinterpret_cast<const uint32_t*>(P.q + ((size_t)b * P.hq + h * kGroup + wave) * kD)[lane];
-  const float2 mu = P.key_smoothing ? reinterpret_cast<const float2*>(P.key_shift + h * kD)[lane]
-                                    : make_float2(0.0f, 0.0f);
+  const uint32_t qw = E.qw;
+  const float2 mu = E.mu;
   if (tid < 8) sm.rcp[tid] = rcp_significand((uint32_t)tid);
   {
     uint32_t* pz = &sm.pst[0][0][0];       // rows 4 .. 15 of every wave's staging tile
@@ -868,6 +895,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   const int BH = P.batch * P.hkv;
   const int bh = (int)blockIdx.x % BH, sp = (int)blockIdx.x / BH;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
+  const Early E = early_loads(P, b, h, sp);
   const int L = P.seq_lens[b];
   if (L < 1 || L > P.max_seq_len || L / kPage > P.max_pages_per_seq) {
     if (sp == 0) poison_rows(P.out, P.hq, b, h);
@@ -886,7 +914,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     return;
   }
   if (sp >= nwg) return;
-  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax>(A, sm, b, h, sp, L, sp == 0);
+  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax>(A, sm, b, h, sp, L, sp == 0, E);
   write_partial(partial_writer(C, bh, sp), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
