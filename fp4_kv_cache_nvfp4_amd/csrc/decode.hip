@@ -242,27 +242,32 @@ __device__ Partial bf16_partition(const DecArgs& A, Smem& sm, int b, int h, int 
     }
     aq[c] = v;
   }
-  // B: token 16 tile + row of each of this wave's tiles, same channels
+  // B: token 16 tile + row of each of this wave's tiles, same channels.
+  // Whole tiles are taken or skipped by a wave-uniform test (a skipped
+  // tile's logits are masked below); inside a taken tile a row past nb reads
+  // row nb - 1 instead (masked too), so no load sits behind a per-lane branch
   u32x4_t bk[kBfTilesPerWave][4];
 #pragma unroll
   for (int k = 0; k < kBfTilesPerWave; ++k) {
-    const int j = 16 * (wave + 4 * k) + row;
+    const int t16 = 16 * (wave + 4 * k);
+    const int j = min(t16 + row, nb - 1);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (j < nb) {
+    for (int c = 0; c < 4; ++c) bk[k][c] = (u32x4_t){0u, 0u, 0u, 0u};
+    if (t16 < nb) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
         const uint4 t = *reinterpret_cast<const uint4*>(row_of(P.sink_k, P.tail_k, j) + 32 * c + 8 * kg);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+        bk[k][c] = (u32x4_t){t.x, t.y, t.z, t.w};
       }
-      bk[k][c] = v;
     }
   }
-  // V: channels 2 lane, 2 lane + 1 of tokens wave + 4 m
+  // V: channels 2 lane, 2 lane + 1 of tokens wave + 4 m (a wave-uniform test)
   uint32_t vv[kBfVPerThread];
 #pragma unroll
   for (int m = 0; m < kBfVPerThread; ++m) {
     const int j = wave + 4 * m;
-    vv[m] = j < nb ? reinterpret_cast<const uint32_t*>(row_of(P.sink_v, P.tail_v, j))[lane] : 0u;
+    vv[m] = 0u;
+    if (j < nb) vv[m] = reinterpret_cast<const uint32_t*>(row_of(P.sink_v, P.tail_v, j))[lane];
   }
   // logits: lanes 0..15 hold token 16 tile + lane, heads 0..3 in acc[0..3]
   const float sigma = P.softmax_scale;
