@@ -589,9 +589,17 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   // the slot about to be used.
   KPage kb0, kb1;
   VPage vb0, vb1;
-  load_k<kMx>(kb0, P, blk_of(0), lane);
+  // A workgroup that also computes the BF16 partition does so before it
+  // requests its first K pages, so that waiting for the partition's rows
+  // does not also wait for those pages (every workgroup of the grid requests
+  // its first pages at once, and they take several µs to drain)
   Partial bfp;
-  if (bf16) bfp = bf16_partition(A, sm, b, h, L, n_full);
+  if (bf16) {
+    bfp = bf16_partition(A, sm, b, h, L, n_full);
+    load_k<kMx>(kb0, P, blk_of(0), lane);
+  } else {
+    load_k<kMx>(kb0, P, blk_of(0), lane);
+  }
   load_k<kMx>(kb1, P, blk_of(1), lane);
   query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
