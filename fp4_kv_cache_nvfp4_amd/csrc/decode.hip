@@ -14,8 +14,8 @@
 // (sequence, KV head); each wave owns one partition of pages_per_partition
 // (1..4) consecutive full pages. The BF16 partition (sink + tail tokens,
 // exact float32 attention of the raw query) of (sequence, KV head) j is
-// computed by workgroup j, among the first dispatched, while its own first
-// K page loads. Every partition computes, for the 4 query heads of its KV
+// computed by workgroup j, among the first dispatched, before it requests
+// its first K pages. Every partition computes, for the 4 query heads of its KV
 // head, m = max logit, l = sum exp(t - m) and o = sum P_hat v_hat; a
 // workgroup merges its four waves in LDS, stores one partial and takes a
 // ticket; the last of a (sequence, KV head) merges all of them (merge.hpp).
@@ -516,13 +516,6 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// The four FP4 partitions 4 sp + w (w = wave) of one (sequence, KV head):
-// each wave streams its own pages_per_partition consecutive pages through
-// pass 1, its own maximum and pass 2 with no workgroup barrier in between;
-// the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
-// workgroup's partial (returned; the caller stores it). With bf16 the
-// workgroup also computes the (sequence, KV head)'s BF16 partition while its
-// first K page loads and folds it into the same partial.
 // What a wave of an FP4 workgroup reads before anything else, issued at the
 // start of the kernel so that these loads, the sequence length and the
 // kernel arguments share one memory round trip instead of following each
@@ -552,6 +545,13 @@ __device__ __forceinline__ Early early_loads(const DecodeLaunch& P, int b, int h
   return E;
 }
 
+// The four FP4 partitions 4 sp + w (w = wave) of one (sequence, KV head):
+// each wave streams its own pages_per_partition consecutive pages through
+// pass 1, its own maximum and pass 2 with no workgroup barrier in between;
+// the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
+// workgroup's partial (returned; the caller stores it). With bf16 the
+// workgroup first computes the (sequence, KV head)'s BF16 partition, then
+// requests its first K pages, and folds the partition into the same partial.
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax>
 __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16, const Early& E) {
   const DecodeLaunch& P = A.L;
@@ -895,8 +895,8 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
 // Workgroup j works for (sequence, KV head) j % (B Hkv) as its FP4 workgroup
 // sp = j / (B Hkv): the first B Hkv workgroups of the grid, dispatched first
 // and the oldest on their CUs, are the sp = 0 workgroups of every (sequence,
-// KV head), and those also compute the BF16 partition (while their first K
-// page loads) and fold it into their partial. Workgroup sp stores its
+// KV head), and those also compute the BF16 partition (before requesting
+// their first K pages) and fold it into their partial. Workgroup sp stores its
 // partial in slot sp and takes the (sequence, KV head)'s ticket; the last of
 // the nwg merges them all. A sequence without a full page has only the BF16
 // partition, written straight to the output by its sp = 0 workgroup.
