@@ -8,11 +8,12 @@
 //  * pass 1: QK^T with v_mfma_f32_16x16x32_bf16; A = the 4 bf16 query rows
 //    (exact operands), B = 16 tokens per tile, a lane holding 32 consecutive
 //    channels of one token (one 64-byte run; the wave reads 4 KiB contiguous
-//    per tile). Logits to LDS, tokens at or past L masked.
+//    per tile), the page's 8 tiles requested together. Logits to LDS, tokens
+//    at or past L masked.
 //  * partition max; p = exp(t - m) in float32 (not rounded to bf16).
 //  * pass 2: PV on the vector ALU in float32: each wave takes a quarter of the
 //    partition's tokens, each lane two channels for all 4 heads; one 256-byte
-//    coalesced V row per token per wave.
+//    coalesced V row per token per wave, a page's 32 rows requested together.
 #include "codec.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -92,13 +93,20 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
     int phys = bt[pi];
     if (phys < 0 || phys >= P.num_pages) { bad = true; phys = 0; }
     const uint16_t* kp = P.k_pages + ((size_t)phys * P.hkv + h) * (kPage * kD);
-#pragma unroll 2
+    // the page's 8 tiles requested together (one memory round trip per page)
+    uint4 kw[8][4];
+#pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint4* src = reinterpret_cast<const uint4*>(kp + (size_t)(16 * t + row) * kD + 32 * kg);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kw[t][c] = src[c];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 w = src[c];
+        const uint4 w = kw[t][c];
         const u32x4_t v = {w.x, w.y, w.z, w.w};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[c], __builtin_bit_cast(bf16x8_t, v), acc, 0, 0, 0);
       }
@@ -164,15 +172,25 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args A) {
     if (phys < 0 || phys >= P.num_pages) phys = 0;
     const uint16_t* vp = P.v_pages + ((size_t)phys * P.hkv + h) * (kPage * kD);
     const int tmax = min(kPage, L - (p0 + pi) * kPage);
-#pragma unroll 4
-    for (int t = wave; t < tmax; t += 4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + (size_t)t * kD + 2 * lane);
-      const float4 p = *reinterpret_cast<const float4*>(&sm.logit[(pi * kPage + t) * 4]);
-      const float v0 = bf16_lo(w), v1 = bf16_hi(w);
-      o[0][0] = fmaf(p.x, v0, o[0][0]); o[0][1] = fmaf(p.x, v1, o[0][1]);
-      o[1][0] = fmaf(p.y, v0, o[1][0]); o[1][1] = fmaf(p.y, v1, o[1][1]);
-      o[2][0] = fmaf(p.z, v0, o[2][0]); o[2][1] = fmaf(p.z, v1, o[2][1]);
-      o[3][0] = fmaf(p.w, v0, o[3][0]); o[3][1] = fmaf(p.w, v1, o[3][1]);
+    // the wave's 32 rows of the page (tokens wave + 4 i) requested together;
+    // a row at or past tmax reads row tmax - 1 (in the page) and is skipped
+    uint32_t vw[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int t = min(wave + 4 * i, tmax - 1);
+      vw[i] = *reinterpret_cast<const uint32_t*>(vp + (size_t)t * kD + 2 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int t = wave + 4 * i;
+      if (t < tmax) {
+        const float4 p = *reinterpret_cast<const float4*>(&sm.logit[(pi * kPage + t) * 4]);
+        const float v0 = bf16_lo(vw[i]), v1 = bf16_hi(vw[i]);
+        o[0][0] = fmaf(p.x, v0, o[0][0]); o[0][1] = fmaf(p.x, v1, o[0][1]);
+        o[1][0] = fmaf(p.y, v0, o[1][0]); o[1][1] = fmaf(p.y, v1, o[1][1]);
+        o[2][0] = fmaf(p.z, v0, o[2][0]); o[2][1] = fmaf(p.z, v1, o[2][1]);
+        o[3][0] = fmaf(p.w, v0, o[3][0]); o[3][1] = fmaf(p.w, v1, o[3][1]);
+      }
     }
   }
 #pragma unroll
