@@ -460,8 +460,8 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of the decode is described in DESIGN.md, not built.", file=sys.stderr)
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of the decode is not built.", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -57,7 +57,7 @@ bdfp4_status check_kv_recipe(const bdfp4_recipe* r) {
     return fail(BDFP4_E_INVALID, "scale_mode_v %d is not a value scale mode", vm);
   if (!is_nv_kv(r) && !is_mx_kv(r))
     return fail(BDFP4_E_UNSUPPORTED,
-                "K/V scale modes (%d, %d): this build has kernels for (four_six|amax6, amax6) and "
+                "K/V scale modes (%d, %d): this library has kernels for (four_six|amax6, amax6) and "
                 "(mxfp4_search, mxfp4_search)", km, vm);
   return BDFP4_OK;
 }
@@ -96,9 +96,9 @@ bdfp4_status check_recipe(const bdfp4_recipe* r) {
   if (qm == BDFP4_SCALE_NONE)
     return fail(BDFP4_E_UNSUPPORTED, "an unquantized query has no FP4 decode kernel");
   if (is_nv_kv(r) && qm != BDFP4_SCALE_AMAX6)
-    return fail(BDFP4_E_UNSUPPORTED, "NVFP4 pages take an amax6 query in this build");
+    return fail(BDFP4_E_UNSUPPORTED, "NVFP4 pages take an amax6 query in this library");
   if (is_mx_kv(r) && qm != BDFP4_SCALE_MXFP4_SEARCH)
-    return fail(BDFP4_E_UNSUPPORTED, "MXFP4 pages take an mxfp4_search query in this build");
+    return fail(BDFP4_E_UNSUPPORTED, "MXFP4 pages take an mxfp4_search query in this library");
   if (r->p_running_max && (!is_nv_kv(r) || r->query_terms != 2 || pm != BDFP4_SCALE_AMAX2_OR_AMAX6))
     return fail(BDFP4_E_UNSUPPORTED,
                 "p_running_max has a kernel for NVFP4 pages, two query terms and amax2_or_amax6 P only");

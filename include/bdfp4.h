@@ -132,7 +132,7 @@ bdfp4_status bdfp4_recipe_default_mxfp4(bdfp4_recipe* r);
 /* Host-only check of a recipe, mirroring probability_environment: c not in
  * {1, 8} -> E_INVALID; tau NaN ("calibrate") -> E_UNCALIBRATED; tau not finite
  * or outside [0, 448] -> E_INVALID; other fields outside their ranges ->
- * E_INVALID; combinations this build has no kernel for (mixed NVFP4/MXFP4
+ * E_INVALID; combinations this library has no kernel for (mixed NVFP4/MXFP4
  * tensors, NONE modes) -> E_UNSUPPORTED. */
 bdfp4_status bdfp4_recipe_validate(const bdfp4_recipe* r);
 
@@ -266,7 +266,7 @@ bdfp4_status bdfp4_decode_workspace_size(int32_t batch, int32_t num_q_heads,
 /* Paged FP4 decode attention ("Decode interface -> Paged attention kernel").
  *   q_bf16:        [batch][num_q_heads][128] bf16; query head g reads KV head
  *                  g / (num_q_heads / num_kv_heads). num_q_heads / num_kv_heads
- *                  must be 4 (GQA group of this build).
+ *                  must be 4 (the GQA group this library supports).
  *   block_tables:  int32 [batch][max_pages_per_seq] physical page of each
  *                  logical page.
  *   seq_lens:      int32 [batch] context length L (tokens), device memory.
