@@ -5,8 +5,8 @@ only, sink + tail, several partitions with a ragged last one), sink lengths,
 the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode,
 rotated values (NVFP4 and MXFP4, ragged batch included), P normalised by
 the running block maximum (ragged batches with sink 16 and 112 included), the
-32K Qwen3-4B-shaped layer with a 77-token tail, the full 128K layer in the
-benchmark's launch configuration (two KV heads sampled), 16 sequences of
+32K Qwen3-4B-shaped layer with a 77-token tail and the full 128K layer in the
+benchmark's launch configuration (two KV heads sampled), each for NVFP4 and MXFP4, 16 sequences of
 2K..16K tokens (two sampled), determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
 and the BF16-KV baseline arm."""
@@ -86,11 +86,12 @@ def test_ragged_batch_mxfp4():
     _run(MX, wl, 3, "ragged mxfp4")
 
 
-def test_qwen_32k_layer():
+@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+def test_qwen_32k_layer(r):
     """32 query / 8 KV heads, 256 full pages + 77-token tail, permuted pool."""
     wl = synth.qwen_32k(0)
     ppp, _ = bd.decode_plan(1, 8, int(wl.seq_lens[0]), 0)
-    _run(NV, wl, ppp, f"qwen 32k ppp={ppp}")
+    _run(r, wl, ppp, f"qwen 32k ppp={ppp}")
 
 
 def test_determinism_and_paging_invariance():
@@ -167,7 +168,8 @@ def test_bf16_baseline(ppp):
     assert_close(out.cpu().numpy().astype(np.float64), ref, f"bf16 baseline ppp={ppp}")
 
 
-def test_full_128k_layer_sampled_heads():
+@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+def test_full_128k_layer_sampled_heads(r):
     """The headline shape in the launch configuration the benchmark times:
     batch 1, 131,072 tokens, 32 query / 8 KV heads, the library's own split
     plan. The HIP writer and decode run on all 8 KV heads; the oracle writes
@@ -177,13 +179,13 @@ def test_full_128k_layer_sampled_heads():
     wl = synth.decode_workload("full128k", 11, [L], 32, 8, "qwen")
     ppp, parts = bd.decode_plan(1, 8, L, 0)
     assert (ppp, parts) == (4, 256)                    # 512 workgroups, as the benchmark launches
-    got = gpu_decode(NV, wl, gpu_write(NV, wl), ppp)
+    got = gpu_decode(r, wl, gpu_write(r, wl), ppp)
     rows = [4 * h + g for h in heads for g in range(4)]
     k, v, ids = wl.writer_inputs()
-    cache = OW.empty_cache(wl.num_pages, len(heads), NV)
-    OW.write_pages(NV, cache, k[:, heads], v[:, heads], ids, wl.key_shift[heads])
+    cache = OW.empty_cache(wl.num_pages, len(heads), r)
+    OW.write_pages(r, cache, k[:, heads], v[:, heads], ids, wl.key_shift[heads])
     sk, sv, tk, tv = wl.sink_tail()
-    ref = OD.decode(NV, cache, wl.q[:, rows], wl.block_tables, wl.seq_lens, sk[:, heads], sv[:, heads],
+    ref = OD.decode(r, cache, wl.q[:, rows], wl.block_tables, wl.seq_lens, sk[:, heads], sv[:, heads],
                     tk[:, heads], tv[:, heads], wl.key_shift[heads], wl.sigma, ppp)
     assert_close(got[:, rows], ref, "128k layer, KV heads 0 and 5")
 
