@@ -94,36 +94,38 @@ def test_qwen_32k_layer(r):
     _run(r, wl, ppp, f"qwen 32k ppp={ppp}")
 
 
-def test_determinism_and_paging_invariance():
+@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+def test_determinism_and_paging_invariance(r):
     wl = synth.decode_workload("d", 6, [3000, 1234], 8, 2, "qwen", extra_pages=4)
-    host = oracle_write(NV, wl)
-    cache = cache_to_dev(NV, host, 2)
-    a, b = gpu_decode(NV, wl, cache, 2, repeat=2)
+    host = oracle_write(r, wl)
+    cache = cache_to_dev(r, host, 2)
+    a, b = gpu_decode(r, wl, cache, 2, repeat=2)
     assert np.array_equal(a, b)
     # move every physical page to a new slot and remap the tables
     perm = np.random.default_rng(0).permutation(wl.num_pages)
     moved = {k: np.empty_like(v) for k, v in host.items()}
     for k in host:
         moved[k][perm] = host[k]
-    c = gpu_decode(NV, wl, cache_to_dev(NV, moved, 2), 2, block_tables=perm[wl.block_tables].astype(np.int32))
+    c = gpu_decode(r, wl, cache_to_dev(r, moved, 2), 2, block_tables=perm[wl.block_tables].astype(np.int32))
     assert np.array_equal(a, c)
 
 
-def test_invalid_inputs_give_nan_rows():
+@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+def test_invalid_inputs_give_nan_rows(r):
     wl = synth.decode_workload("n", 8, [700, 600, 500], 8, 2, "tiny", extra_pages=1)
-    host = oracle_write(NV, wl)
-    cache = cache_to_dev(NV, host, 2)
-    ref = oracle_decode(NV, wl, host, 2)
+    host = oracle_write(r, wl)
+    cache = cache_to_dev(r, host, 2)
+    ref = oracle_decode(r, wl, host, 2)
     sl = wl.seq_lens.copy()
     sl[1] = 0                                   # empty sequence
     bt = wl.block_tables.copy()
     bt[2, 1] = wl.num_pages + 7                 # page outside the pool
-    got = gpu_decode(NV, wl, cache, 2, max_seq_len=700, seq_lens=sl, block_tables=bt)
+    got = gpu_decode(r, wl, cache, 2, max_seq_len=700, seq_lens=sl, block_tables=bt)
     assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
     assert_close(got[0], ref[0], "valid row next to invalid ones")
     # a length above max_seq_len is rejected on the device too
     sl2 = wl.seq_lens.copy()
-    got2 = gpu_decode(NV, wl, cache, 2, max_seq_len=600, seq_lens=sl2)
+    got2 = gpu_decode(r, wl, cache, 2, max_seq_len=600, seq_lens=sl2)
     assert np.all(np.isnan(got2[0])) and np.all(np.isfinite(got2[1:]))
 
 
