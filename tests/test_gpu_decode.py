@@ -9,7 +9,7 @@ the running block maximum (ragged batches with sink 16 and 112 included), the
 benchmark's launch configuration (two KV heads sampled), each for NVFP4 and MXFP4, 16 sequences of
 2K..16K tokens (two sampled), determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
-and the BF16-KV baseline arm."""
+16 seeded random shapes and recipes, and the BF16-KV baseline arm."""
 import numpy as np
 import pytest
 import torch
@@ -79,6 +79,30 @@ def test_ragged_batch_running_max(sink):
     # leading blocks of sink slots only (no running maximum yet), ragged tails
     wl = synth.decode_workload("r", 7, [1, 100, 300, 2049, 640], 8, 2, "qwen", extra_pages=2, sink_tokens=sink)
     _run(NV.with_(p_running_max=True, sink_tokens=sink), wl, 3, f"ragged running max sink={sink}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes(seed):
+    # seeded random shapes: batch, lengths (ragged pages, sequences shorter
+    # than the sink or a page), KV heads, sink, pages per partition, recipe
+    # (NVFP4 / MXFP4, one or two query terms, tau, c), the HIP writer's pages
+    rng = np.random.default_rng(1000 + seed)
+    batch = int(rng.integers(1, 5))
+    hkv = int(rng.choice([1, 2, 3]))
+    sink = int(rng.choice([0, 16, 48, 112]))
+    lens = [int(x) for x in rng.integers(1, 3000, size=batch)]
+    ppp = int(rng.integers(1, 5))
+    base = MX if rng.random() < 0.4 else NV
+    r = base.with_(sink_tokens=sink, query_terms=int(rng.choice([1, 2])), tau=float(rng.choice([0.0, 0.5, 1.0, 4.0])),
+                   c=int(rng.choice([1, 8])))
+    wl = synth.decode_workload("rand", 2000 + seed, lens, 4 * hkv, hkv, "qwen",
+                               extra_pages=int(rng.integers(0, 3)), sink_tokens=sink)
+    what = f"random seed={seed}: B={batch} L={lens} hkv={hkv} sink={sink} ppp={ppp} {'mx' if base is MX else 'nv'}"
+    print(f"[decode] {what}", flush=True)
+    host = oracle_write(r, wl)
+    ref = oracle_decode(r, wl, host, ppp)
+    got = gpu_decode(r, wl, gpu_write(r, wl), ppp)
+    assert_close(got, ref, what)
 
 
 def test_ragged_batch_mxfp4():
