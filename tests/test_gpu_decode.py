@@ -6,7 +6,8 @@ the MXFP4 recipe, one query term, c = 1, tau = 0 and the amax6 P mode,
 rotated values (NVFP4 and MXFP4, ragged batch included), P normalised by
 the running block maximum (ragged batches with sink 16 and 112 included), the
 32K Qwen3-4B-shaped layer with a 77-token tail and the full 128K layer in the
-benchmark's launch configuration (two KV heads sampled), each for NVFP4 and MXFP4, 16 sequences of
+benchmark's launch configuration (two KV heads sampled), each for NVFP4 and MXFP4, long contexts at one
+page per partition (the final merge over several batches of partials), 16 sequences of
 2K..16K tokens (two sampled), determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
 16 seeded random shapes and recipes, and the BF16-KV baseline arm."""
@@ -214,6 +215,20 @@ def test_full_128k_layer_sampled_heads(r):
     ref = OD.decode(r, cache, wl.q[:, rows], wl.block_tables, wl.seq_lens, sk[:, heads], sv[:, heads],
                     tk[:, heads], tv[:, heads], wl.key_shift[heads], wl.sigma, ppp)
     assert_close(got[:, rows], ref, "128k layer, KV heads 0 and 5")
+
+
+@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+def test_many_workgroups_per_head(r):
+    """One page per partition over long contexts: 250 and 75 workgroups per
+    (sequence, KV head), so the final merge takes its partials in several
+    batches of 64 (64 + 64 + 64 + 58 and 64 + 11) and rescales the earlier
+    batches; a 50-token and a 1-token tail, sink 16, every output row
+    compared."""
+    lens = [128 * 1000 + 50, 128 * 300 + 1]
+    wl = synth.decode_workload("many_wgs", 23, lens, 4, 1, "qwen")
+    ppp, parts = bd.decode_plan(2, 1, max(lens), 1)
+    assert (ppp, parts) == (1, 1000)
+    _run(r, wl, ppp, f"many workgroups per head, L={lens}, ppp=1")
 
 
 def test_batched_16_sequences_sampled():
