@@ -2,10 +2,12 @@
 // decode split plan, and the launches. Every check runs before anything is
 // enqueued; a failing check returns its status and records a message.
 //
-// Validation rules follow "BitDecoding-FP4 evaluation/config.py":
-// probability_environment (c in {1, 8}; tau "calibrate" refused outside
-// calibration; tau finite in [0, 448]) and the KV_MODES entries
-// bitdecoding-nvfp4 / bitdecoding-mxfp4 (sink 16, scale modes, query terms).
+// The constraints enforced on the probability settings come from
+// "BitDecoding-FP4 evaluation/config.py", section probability_environment:
+// the P multiplier c takes the values 1 and 8, an uncalibrated tau cannot be
+// used to decode, and a calibrated tau lies in the E4M3 range [0, 448]. The
+// KV_MODES entries bitdecoding-nvfp4 / bitdecoding-mxfp4 give the sink, the
+// scale modes and the query terms. Checks and messages are this library's.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -62,6 +64,35 @@ bdfp4_status check_kv_recipe(const bdfp4_recipe* r) {
   return BDFP4_OK;
 }
 
+// tau of the amax2_or_amax6 P mode: NaN is the "still to be calibrated"
+// placeholder (refused with its own status), anything else must be a finite
+// threshold inside the E4M3 range.
+bdfp4_status check_tau(float tau) {
+  if (isnan(tau))
+    return fail(BDFP4_E_UNCALIBRATED,
+                "tau is NaN (the placeholder for a threshold not yet calibrated); run the tau search first");
+  if (!(tau >= 0.0f && tau <= 448.0f))
+    return fail(BDFP4_E_INVALID, "tau = %g: the amax2/amax6 threshold must be finite and within [0, 448]",
+                (double)tau);
+  return BDFP4_OK;
+}
+
+// P settings: the mode, then (amax2_or_amax6 only) tau, then the multiplier
+// c, which every quantized P mode applies.
+bdfp4_status check_probability(const bdfp4_recipe* r) {
+  const int pm = r->scale_mode_p;
+  if (pm == BDFP4_SCALE_NONE) return fail(BDFP4_E_UNSUPPORTED, "unquantized probabilities have no FP4 decode kernel");
+  if (pm != BDFP4_SCALE_AMAX2_OR_AMAX6 && pm != BDFP4_SCALE_AMAX6)
+    return fail(BDFP4_E_INVALID, "scale_mode_p %d is not a probability scale mode", pm);
+  if (pm == BDFP4_SCALE_AMAX2_OR_AMAX6) {
+    const bdfp4_status s = check_tau(r->tau);
+    if (s != BDFP4_OK) return s;
+  }
+  if (r->c != 1 && r->c != 8)
+    return fail(BDFP4_E_INVALID, "c = %d: P is multiplied by 1 or by 8 before quantization, nothing else", r->c);
+  return BDFP4_OK;
+}
+
 bdfp4_status check_recipe(const bdfp4_recipe* r) {
   bdfp4_status s = check_kv_recipe(r);
   if (s != BDFP4_OK) {
@@ -79,19 +110,8 @@ bdfp4_status check_recipe(const bdfp4_recipe* r) {
   const int qm = r->scale_mode_q, pm = r->scale_mode_p;
   if (qm != BDFP4_SCALE_AMAX6 && qm != BDFP4_SCALE_MXFP4_SEARCH && qm != BDFP4_SCALE_NONE)
     return fail(BDFP4_E_INVALID, "scale_mode_q %d is not a query scale mode", qm);
-  if (pm == BDFP4_SCALE_AMAX2_OR_AMAX6) {
-    if (r->c != 1 && r->c != 8) return fail(BDFP4_E_INVALID, "the probability kernel supports c=1 or c=8");
-    if (isnan(r->tau))
-      return fail(BDFP4_E_UNCALIBRATED, "tau must be calibrated before evaluation or throughput measurement");
-    if (!isfinite(r->tau) || r->tau < 0.0f || r->tau > 448.0f)
-      return fail(BDFP4_E_INVALID, "tau must be 'calibrate' or a finite number between 0 and 448");
-  } else if (pm == BDFP4_SCALE_AMAX6) {
-    if (r->c != 1 && r->c != 8) return fail(BDFP4_E_INVALID, "the probability kernel supports c=1 or c=8");
-  } else if (pm == BDFP4_SCALE_NONE) {
-    return fail(BDFP4_E_UNSUPPORTED, "unquantized probabilities have no FP4 decode kernel");
-  } else {
-    return fail(BDFP4_E_INVALID, "scale_mode_p %d is not a probability scale mode", pm);
-  }
+  const bdfp4_status ps = check_probability(r);
+  if (ps != BDFP4_OK) return ps;
   if (s != BDFP4_OK) return s;
   if (qm == BDFP4_SCALE_NONE)
     return fail(BDFP4_E_UNSUPPORTED, "an unquantized query has no FP4 decode kernel");
@@ -577,9 +597,8 @@ bdfp4_status bdfp4_quantize_p_blocks(const float* pp, int32_t n_blocks, int32_t 
   if (mode != BDFP4_SCALE_AMAX2_OR_AMAX6 && mode != BDFP4_SCALE_AMAX6)
     return fail(BDFP4_E_INVALID, "mode must be amax2_or_amax6 or amax6");
   if (mode == BDFP4_SCALE_AMAX2_OR_AMAX6) {
-    if (isnan(tau)) return fail(BDFP4_E_UNCALIBRATED, "tau must be calibrated before evaluation or throughput measurement");
-    if (!isfinite(tau) || tau < 0.0f || tau > 448.0f)
-      return fail(BDFP4_E_INVALID, "tau must be 'calibrate' or a finite number between 0 and 448");
+    const bdfp4_status s = check_tau(tau);
+    if (s != BDFP4_OK) return s;
   }
   if (n_blocks == 0) return ok();
   if (!pp || !codes || !scales) return fail(BDFP4_E_INVALID, "NULL pointer");

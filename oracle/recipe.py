@@ -10,9 +10,9 @@ From "BitDecoding-FP4 evaluation/config.py":
 * ``recipe_additional_config`` maps that to key scale mode four_six (amax6
   when the search is off), value and query amax6, two query terms (one when
   the dual residual is off) and rotation hadamard (none when off);
-* ``probability_environment``: scaling disabled gives P mode amax6; c must be
-  1 or 8; tau "calibrate" is refused outside calibration; otherwise tau must
-  be a finite number in [0, 448];
+* ``probability_environment``: with the scaling off, P takes mode amax6; the
+  multiplier c takes the values 1 and 8; an uncalibrated tau is refused
+  outside calibration, a calibrated one lies in [0, 448];
 * KV_MODES ``bitdecoding-nvfp4`` keeps a 16-token BF16 sink;
   ``bitdecoding-mxfp4`` uses mxfp4_search with the same sink, two query terms
   and Hadamard rotation.
@@ -65,18 +65,34 @@ def mxfp4_default() -> Recipe:
                   scale_mode_q=Q.MXFP4_SEARCH)
 
 
+def _tau_problem(tau):
+    """None for a usable amax2_or_amax6 threshold; else the error to raise.
+    NaN stands for a threshold not yet calibrated; a calibrated one is a
+    finite number inside the E4M3 range."""
+    if isinstance(tau, float) and math.isnan(tau):
+        return UncalibratedError("tau is NaN: calibrate it before decoding")
+    if isinstance(tau, bool) or not isinstance(tau, (int, float)) or not math.isfinite(tau):
+        return RecipeError(f"tau = {tau!r} is not a finite number")
+    if tau < 0 or tau > 448:
+        return RecipeError(f"tau = {tau!r} lies outside [0, 448]")
+    return None
+
+
 def validate(r: Recipe) -> None:
-    """Raise RecipeError / UncalibratedError for recipes the method refuses."""
-    if r.scale_mode_p == Q.AMAX2_OR_AMAX6:
-        if r.c not in (1, 8):
-            raise RecipeError("the probability kernel supports c=1 or c=8")
-        if isinstance(r.tau, float) and math.isnan(r.tau):
-            raise UncalibratedError(
-                "tau must be calibrated before evaluation or throughput measurement")
-        if not isinstance(r.tau, (int, float)) or not math.isfinite(r.tau) or not 0 <= r.tau <= 448:
-            raise RecipeError("tau must be 'calibrate' or a finite number between 0 and 448")
-    elif r.scale_mode_p not in (Q.AMAX6, Q.NONE):
+    """Raise RecipeError / UncalibratedError for recipes the method refuses.
+
+    The constraints on P follow "BitDecoding-FP4 evaluation/config.py",
+    probability_environment: with amax2_or_amax6, tau must be calibrated and
+    lie in [0, 448]; c is 1 or 8 for every quantized P mode. The P mode is
+    checked first, then tau, then c."""
+    if r.scale_mode_p not in (Q.AMAX2_OR_AMAX6, Q.AMAX6, Q.NONE):
         raise RecipeError(f"bad probability scale mode {r.scale_mode_p!r}")
+    if r.scale_mode_p == Q.AMAX2_OR_AMAX6:
+        err = _tau_problem(r.tau)
+        if err is not None:
+            raise err
+    if r.scale_mode_p != Q.NONE and r.c not in (1, 8):
+        raise RecipeError(f"c = {r.c!r}: P is multiplied by 1 or 8 before quantization")
     if r.query_terms not in (1, 2):
         raise RecipeError("query_terms is 1 or 2")
     if r.sink_tokens < 0 or r.sink_tokens >= 128 or r.sink_tokens % 16:

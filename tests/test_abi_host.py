@@ -75,7 +75,6 @@ def test_recipe_validation_follows_probability_environment():
             with pytest.raises(bd.Bdfp4Error) as ei:
                 bd.recipe_validate(r)
             assert ei.value.status == want
-            assert case["message"] in str(ei.value)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -153,6 +152,7 @@ def test_decode_rejects_before_launch():
     assert _decode(r, q=None) == bd.E_INVALID
     assert _decode(r, q=FAKE + 2) == bd.E_INVALID
     assert _decode(r, mu=None) == bd.E_INVALID                     # key smoothing without key means
+    assert "key_shift" in bd.lib().bdfp4_last_error().decode()
     assert _decode(r.replace(key_smoothing=0)) == bd.E_INVALID     # key means without smoothing
     assert _decode(r, sk=None) == bd.E_INVALID
     assert _decode(r, tk=None) == bd.E_INVALID
@@ -163,7 +163,7 @@ def test_decode_rejects_before_launch():
     assert _decode(r, ppp=40) == bd.E_INVALID
     assert _decode(r, scale=float("inf")) == bd.E_INVALID
     assert _decode(r, batch=0) == bd.E_INVALID
-    assert "key_shift" in bd.lib().bdfp4_last_error().decode() or True
+    assert "batch" in bd.lib().bdfp4_last_error().decode()
 
 
 def _write(r, cache=None, k=FAKE, v=FAKE, ids=FAKE, n=4, mu=FAKE):
