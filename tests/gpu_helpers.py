@@ -18,6 +18,11 @@ from oracle import writer as W
 # quantized operands and partitioning
 MAX_ABS = 2e-3
 REL_L2 = 1e-3
+# beside it, an element-wise bound scaled to each output row's magnitude:
+# |got - ref| <= ROW_SCALED * max |ref row|. At long contexts an output row
+# averages many value rows and its entries shrink towards 1e-3, where the
+# absolute bound above no longer constrains anything.
+ROW_SCALED = 2e-3
 
 _MODE = {Q.NONE: bd.SCALE_NONE, Q.AMAX6: bd.SCALE_AMAX6, Q.FOUR_SIX: bd.SCALE_FOUR_SIX,
          Q.MXFP4_SEARCH: bd.SCALE_MXFP4_SEARCH, Q.AMAX2_OR_AMAX6: bd.SCALE_AMAX2_OR_AMAX6}
@@ -114,8 +119,16 @@ def errors(got: np.ndarray, ref: np.ndarray):
     return float(np.max(np.abs(d))), float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
 
 
+def row_scaled_error(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over output rows (last axis = channels) of max |got - ref| / max |ref|."""
+    d = np.abs(got - ref).reshape(-1, ref.shape[-1]).max(axis=1)
+    m = np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=1)
+    return float(np.max(d / np.maximum(m, 1e-30)))
+
+
 def assert_close(got, ref, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     mx, rel = errors(got, ref)
-    print(f"[parity] {what}: max_abs={mx:.3e} rel_l2={rel:.3e}", flush=True)
-    assert mx <= MAX_ABS and rel <= REL_L2, (what, mx, rel)
+    rs = row_scaled_error(got, ref)
+    print(f"[parity] {what}: max_abs={mx:.3e} rel_l2={rel:.3e} row_scaled={rs:.3e}", flush=True)
+    assert mx <= MAX_ABS and rel <= REL_L2 and rs <= ROW_SCALED, (what, mx, rel, rs)
