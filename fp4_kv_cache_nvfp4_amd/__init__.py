@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
         "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
+        "bdfp4_decode_attention_noalloc": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, P],
         "bdfp4_bf16_decode_attention": [P, I32, I32, I32, P, P, I32, P, I32, P, I32, F32, I32, P, SZ, P, P],
         "bdfp4_quantize_rows": [P, I32, P, I32, I32, I32, P, P, P],
         "bdfp4_quantize_p_blocks": [P, I32, I32, F32, P, P, P],
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int32
+    L.bdfp4_decode_noalloc_max_workspace.argtypes = []
+    L.bdfp4_decode_noalloc_max_workspace.restype = ctypes.c_size_t
     L.bdfp4_status_string.argtypes = [ctypes.c_int32]
     L.bdfp4_status_string.restype = ctypes.c_char_p
     L.bdfp4_last_error.argtypes = []
@@ -327,6 +330,23 @@ def decode_attention(r: Recipe, cache: PagedCache, q, block_tables, seq_lens, ma
         _ptr(seq_lens), int(max_seq_len), _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v),
         _ptr(key_shift), float(softmax_scale), int(pages_per_partition), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _ptr(out), _stream(stream)))
+
+
+def decode_attention_noalloc(r: Recipe, cache: PagedCache, q, block_tables, seq_lens, max_seq_len: int,
+                             sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale: float,
+                             pages_per_partition: int, out, stream=None) -> None:
+    """decode_attention on the library's own per-GPU workspace array
+    (bdfp4_decode_attention_noalloc): no workspace argument, no allocation."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    c = cache.struct()
+    _check(lib().bdfp4_decode_attention_noalloc(
+        ctypes.byref(r), ctypes.byref(c), _ptr(q), B, Hq, _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(seq_lens), int(max_seq_len), _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v),
+        _ptr(key_shift), float(softmax_scale), int(pages_per_partition), _ptr(out), _stream(stream)))
+
+
+def decode_noalloc_max_workspace() -> int:
+    return int(lib().bdfp4_decode_noalloc_max_workspace())
 
 
 def bf16_decode_attention(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len: int,

@@ -459,13 +459,16 @@ static bdfp4_status check_workspace(int32_t batch, int32_t hkv, int32_t max_seq_
   return BDFP4_OK;
 }
 
-bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
-                                    int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
-                                    int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
-                                    const void* sink_k, const void* sink_v, const void* tail_k,
-                                    const void* tail_v, const float* key_shift, float softmax_scale,
-                                    int32_t pages_per_partition, void* workspace, size_t workspace_bytes_in,
-                                    float* out, void* stream) {
+// The FP4 decode behind both entry points. With noalloc the workspace
+// arguments are ignored and the library's own per-GPU scratch array is used
+// instead, once the plan's workspace is known to fit in it.
+static bdfp4_status decode_impl(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+                                int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                const void* sink_k, const void* sink_v, const void* tail_k, const void* tail_v,
+                                const float* key_shift, float softmax_scale, int32_t pages_per_partition,
+                                void* workspace, size_t workspace_bytes_in, float* out, void* stream,
+                                bool noalloc) {
   if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
   bdfp4_status s = check_recipe(r);
   if (s != BDFP4_OK) return s;
@@ -488,8 +491,20 @@ bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* ca
   if (max_seq_len / 128 > max_pages_per_seq)
     return fail(BDFP4_E_INVALID, "max_seq_len needs %d pages but block tables hold %d", max_seq_len / 128,
                 max_pages_per_seq);
-  if ((s = check_workspace(batch, cache->num_kv_heads, max_seq_len, ppp, workspace, workspace_bytes_in)) != BDFP4_OK)
+  if (noalloc) {
+    const size_t need = workspace_bytes(batch, cache->num_kv_heads, max_seq_len, ppp);
+    if (need > bdfp4::kNoAllocScratchBytes)
+      return fail(BDFP4_E_WORKSPACE,
+                  "this call needs %zu bytes of workspace; the allocation-free decode has %zu "
+                  "(use bdfp4_decode_attention with a caller workspace)",
+                  need, bdfp4::kNoAllocScratchBytes);
+    const hipError_t e = bdfp4::noalloc_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess) return hip_status(e, "scratch set-up");
+    workspace_bytes_in = bdfp4::kNoAllocScratchBytes;
+  } else if ((s = check_workspace(batch, cache->num_kv_heads, max_seq_len, ppp, workspace, workspace_bytes_in)) !=
+             BDFP4_OK) {
     return s;
+  }
   bdfp4::DecodeLaunch L;
   L.sink = r->sink_tokens;
   L.rotation = r->rotation;
@@ -530,6 +545,32 @@ bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* ca
   L.out = out;
   return hip_status(bdfp4::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
+
+bdfp4_status bdfp4_decode_attention(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+                                    int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                                    int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                    const void* sink_k, const void* sink_v, const void* tail_k,
+                                    const void* tail_v, const float* key_shift, float softmax_scale,
+                                    int32_t pages_per_partition, void* workspace, size_t workspace_bytes_in,
+                                    float* out, void* stream) {
+  return decode_impl(r, cache, q_bf16, batch, num_q_heads, block_tables, max_pages_per_seq, seq_lens, max_seq_len,
+                     sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale, pages_per_partition, workspace,
+                     workspace_bytes_in, out, stream, false);
+}
+
+bdfp4_status bdfp4_decode_attention_noalloc(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+                                            int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                                            int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                            int32_t max_seq_len, const void* sink_k, const void* sink_v,
+                                            const void* tail_k, const void* tail_v, const float* key_shift,
+                                            float softmax_scale, int32_t pages_per_partition, float* out,
+                                            void* stream) {
+  return decode_impl(r, cache, q_bf16, batch, num_q_heads, block_tables, max_pages_per_seq, seq_lens, max_seq_len,
+                     sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale, pages_per_partition, nullptr, 0, out,
+                     stream, true);
+}
+
+size_t bdfp4_decode_noalloc_max_workspace(void) { return bdfp4::kNoAllocScratchBytes; }
 
 bdfp4_status bdfp4_bf16_decode_attention(const void* q_bf16, int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, const void* k_pages, const void* v_pages,

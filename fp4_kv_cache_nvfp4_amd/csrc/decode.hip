@@ -66,6 +66,8 @@
 // lies in [2^-10, 2688], so it is exact in f16. The NVFP4 V page stores tokens
 // t, t+1 of one channel in a byte, so a converted pair is directly one 32-bit
 // word of the PV B operand.
+#include <mutex>
+
 #include "codec.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -934,6 +936,56 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     merge_out(C, b, h, nwg, P.rotate_v != 0);
     reset_ticket(ticket);
   }
+}
+
+// ------------------------------------------------------------ allocation-free entry
+
+// Workspace of bdfp4_decode_attention_noalloc: device memory of fixed size
+// in this file, one copy per GPU, held until the process ends. Host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// current device (the array's name in host code is not a device address).
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_zeroed[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    // the ticket words must start at zero (every call leaves them zero);
+    // a fill kernel rather than a memset, so a captured first call holds
+    // only kernel nodes
+    const int n = (int)(kTicketBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256u), 0, stream,
+                       static_cast<uint32_t*>(g_scratch_ptr[dev]), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_zeroed[dev] = true;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {

@@ -136,6 +136,13 @@ constexpr size_t kTicketBytes = (size_t)kMaxSeqHeads * kTicketStride * sizeof(ui
 
 inline int32_t workspace_slot_stride(int32_t parts) { return parts + 2; }
 
+// The allocation-free decode's workspace: a device array of this many bytes
+// (tickets, then partials) that the library keeps per GPU. noalloc_scratch
+// returns its address on the current device; the first call on a device also
+// enqueues the zeroing of its ticket words on `stream`.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 inline size_t workspace_bytes_for(int32_t batch, int32_t hkv, int32_t parts) {
   return kTicketBytes + (size_t)batch * hkv * workspace_slot_stride(parts) * kPartialFloats * sizeof(float);
 }

@@ -4,9 +4,11 @@
  *
  * C ABI. Every pointer argument is a plain device pointer (allocated by the
  * caller, for example as a torch tensor) unless the comment says "host".
- * The library never allocates or frees memory, keeps no pointer after a call
- * returns and holds no state between calls. Launches are asynchronous on the
- * given stream (a hipStream_t passed as void*; NULL is the null stream).
+ * The library never allocates or frees memory and keeps no pointer after a
+ * call returns. Its one piece of state is the fixed workspace array of
+ * bdfp4_decode_attention_noalloc (one per GPU, in the library's static device
+ * memory). Launches are asynchronous on the given stream (a hipStream_t
+ * passed as void*; NULL is the null stream).
  *
  * Errors: every entry point validates its recipe, shapes, pointers and
  * alignment on the host before enqueuing anything. On any error it returns a
@@ -299,6 +301,30 @@ bdfp4_status bdfp4_decode_attention(
     const void* tail_v, const float* key_shift, float softmax_scale,
     int32_t pages_per_partition, void* workspace, size_t workspace_bytes,
     float* out, void* stream);
+
+/* bdfp4_decode_attention without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Arguments, results and errors are
+ * those of bdfp4_decode_attention (the same kernels). The tickets and
+ * partials live in a static device array of the library,
+ * bdfp4_decode_noalloc_max_workspace() bytes (16 MiB) per GPU, held until the
+ * process ends; its address on the current device is looked up on the first
+ * call there, which also enqueues the zeroing of its ticket words on
+ * `stream`. The call allocates nothing. A call whose plan needs more
+ * workspace than the array holds (bdfp4_decode_workspace_size) returns
+ * BDFP4_E_WORKSPACE and enqueues nothing. Every call on one GPU shares that
+ * array: calls that may overlap in time on one GPU (two streams, two host
+ * threads) race and must be serialized by the caller. */
+bdfp4_status bdfp4_decode_attention_noalloc(
+    const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+    int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+    int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+    const void* sink_k, const void* sink_v, const void* tail_k,
+    const void* tail_v, const float* key_shift, float softmax_scale,
+    int32_t pages_per_partition, float* out, void* stream);
+
+/* Size in bytes of the allocation-free decode's workspace array. */
+size_t bdfp4_decode_noalloc_max_workspace(void);
 
 /* BF16-KV paged decode (the unquantized baseline arm, kv_cache_dtype "auto"
  * in KV_MODES): exact softmax attention over all L tokens of BF16 pages

@@ -293,3 +293,28 @@ def test_running_max_variant_combinations():
         with pytest.raises(bd.Bdfp4Error) as ei:
             bd.recipe_validate(r)
         assert ei.value.status == bd.E_UNSUPPORTED
+
+
+def test_noalloc_decode_rejects_before_launch():
+    """The allocation-free decode validates like the workspace entry point
+    and refuses a plan larger than its fixed array, enqueuing nothing (no GPU
+    is touched on these paths)."""
+    r = bd.recipe_default_nvfp4(tau=1.0)
+    L = bd.lib()
+    cap = bd.decode_noalloc_max_workspace()
+    assert cap == 16 << 20
+
+    def call(r, batch, hkv, maxp, maxlen, ppp, q=FAKE):
+        c = _cache(num_kv_heads=hkv)
+        return L.bdfp4_decode_attention_noalloc(ctypes.byref(r), ctypes.byref(c), q, batch, 4 * hkv, FAKE, maxp,
+                                                FAKE, maxlen, FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, ppp, FAKE, None)
+
+    # 64 sequences x 8 KV heads x 128K tokens at one page per partition need
+    # far more than the array holds
+    assert bd.decode_workspace_size(64, 32, 8, 131072, 1) > cap
+    assert call(r, 64, 8, 1024, 131072, 1) == bd.E_WORKSPACE
+    assert "allocation-free" in L.bdfp4_last_error().decode()
+    # argument errors are reported first, as by bdfp4_decode_attention
+    assert call(bd.recipe_default_nvfp4(), 1, 1, 16, 2048, 4) == bd.E_UNCALIBRATED
+    assert call(r, 1, 1, 16, 2048, 4, q=None) == bd.E_INVALID
+    assert call(r, 1, 1, 16, 2048, 40) == bd.E_INVALID
