@@ -549,12 +549,14 @@ __device__ __forceinline__ Early early_loads(const DecodeLaunch& P, int b, int h
 
 // The four FP4 partitions 4 sp + w (w = wave) of one (sequence, KV head):
 // each wave streams its own pages_per_partition consecutive pages through
-// pass 1, its own maximum and pass 2 with no workgroup barrier in between;
+// pass 1, its own maximum and pass 2 with no workgroup barrier in between
+// (kSlots = 1, 2 or 4 page slots per kind, the plan's pages_per_partition
+// rounded up, so that no slot is loaded for a page the plan never has);
 // the four (m, l, o) are then merged by log-sum-exp in LDS and stored as the
 // workgroup's partial (returned; the caller stores it). With bf16 the
 // workgroup first computes the (sequence, KV head)'s BF16 partition, then
 // requests its first K pages, and folds the partition into the same partial.
-template <bool kMx, int kTerms, bool kUnder, bool kRunMax>
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots>
 __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16, const Early& E) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -579,16 +581,18 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     uint32_t* pz = &sm.pst[0][0][0];       // rows 4 .. 15 of every wave's staging tile
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
-  // The wave reads a stream of eight slots, K pages 0..3 then V pages 0..3
-  // (slots of pages >= npg are empty), keeping the next slot in flight while
-  // one is used: K page i lands in kb[i % 2], V page j in vb[j % 2], and the
-  // load of a slot is issued once the slot two before it (same buffer) has
-  // been used. One page in flight per wave measured faster than two: with
+  // The wave reads a stream of 2 kSlots slots, K pages 0..kSlots-1 then V
+  // pages 0..kSlots-1, keeping the next slot in flight while one is used:
+  // K page i lands in kb[i % 2], V page j in vb[j % 2], and the load of a
+  // slot is issued once the slot two before it (same buffer) has been used
+  // (with one page per partition, K and V page 0 are both requested at the
+  // start). One page in flight per wave measured faster than two: with
   // 8 waves per CU the memory pipe is already full, and deeper queues only
   // delay the waves dispatched second. The loads are unconditional (a slot
-  // past npg reads physical page 0, which always exists, and is never used)
-  // so the compiler can count the loads in flight exactly and wait only for
-  // the slot about to be used.
+  // of a page past npg, in the partition that ends the sequence, reads
+  // physical page 0, which always exists, and is never used) so the compiler
+  // can count the loads in flight exactly and wait only for the slot about
+  // to be used.
   KPage kb0, kb1;
   VPage vb0, vb1;
   // A workgroup that also computes the BF16 partition does so before it
@@ -602,7 +606,10 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   } else {
     load_k<kMx>(kb0, P, blk_of(0), lane);
   }
-  load_k<kMx>(kb1, P, blk_of(1), lane);
+  if constexpr (kSlots == 1)
+    load_v<kMx>(vb0, P, blk_of(0), lane);
+  else
+    load_k<kMx>(kb1, P, blk_of(1), lane);
   query_prologue<kMx, kTerms>(P, qw, mu, sm, wave, lane);
   __syncthreads();
 
@@ -695,15 +702,25 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     ma = __builtin_fmaxf(ma, pa);
     mb = __builtin_fmaxf(mb, pb);
   };
-  static_assert(kMaxPpw == 4, "the stream below is unrolled for up to 4 pages");
-  if (npg > 0) k_page(kb0, 0);
-  load_k<kMx>(kb0, P, blk_of(2), lane);
-  if (npg > 1) k_page(kb1, 1);
-  load_k<kMx>(kb1, P, blk_of(3), lane);
-  if (npg > 2) k_page(kb0, 2);
-  load_v<kMx>(vb0, P, blk_of(0), lane);
-  if (npg > 3) k_page(kb1, 3);
-  load_v<kMx>(vb1, P, blk_of(1), lane);
+  static_assert(kMaxPpw == 4 && (kSlots == 1 || kSlots == 2 || kSlots == 4),
+                "the stream below is unrolled for 1, 2 or 4 pages");
+  if constexpr (kSlots == 1) {
+    if (npg > 0) k_page(kb0, 0);
+  } else if constexpr (kSlots == 2) {
+    if (npg > 0) k_page(kb0, 0);
+    load_v<kMx>(vb0, P, blk_of(0), lane);
+    if (npg > 1) k_page(kb1, 1);
+    load_v<kMx>(vb1, P, blk_of(1), lane);
+  } else {
+    if (npg > 0) k_page(kb0, 0);
+    load_k<kMx>(kb0, P, blk_of(2), lane);
+    if (npg > 1) k_page(kb1, 1);
+    load_k<kMx>(kb1, P, blk_of(3), lane);
+    if (npg > 2) k_page(kb0, 2);
+    load_v<kMx>(vb0, P, blk_of(0), lane);
+    if (npg > 3) k_page(kb1, 3);
+    load_v<kMx>(vb1, P, blk_of(1), lane);
+  }
   // the partition maximum of each head (rows of 16 lanes hold heads 2 hp, 2 hp + 1)
   ma = max16(ma);
   mb = max16(mb);
@@ -807,12 +824,19 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
       }
     }
   };
-  if (npg > 0) v_page(vb0, 0);
-  load_v<kMx>(vb0, P, blk_of(2), lane);
-  if (npg > 1) v_page(vb1, 1);
-  load_v<kMx>(vb1, P, blk_of(3), lane);
-  if (npg > 2) v_page(vb0, 2);
-  if (npg > 3) v_page(vb1, 3);
+  if constexpr (kSlots == 1) {
+    if (npg > 0) v_page(vb0, 0);
+  } else if constexpr (kSlots == 2) {
+    if (npg > 0) v_page(vb0, 0);
+    if (npg > 1) v_page(vb1, 1);
+  } else {
+    if (npg > 0) v_page(vb0, 0);
+    load_v<kMx>(vb0, P, blk_of(2), lane);
+    if (npg > 1) v_page(vb1, 1);
+    load_v<kMx>(vb1, P, blk_of(3), lane);
+    if (npg > 2) v_page(vb0, 2);
+    if (npg > 3) v_page(vb1, 3);
+  }
   // ---- this wave's (m, l, o) to LDS: o over its own logit rows (read above
   // by this wave only; its LDS instructions complete in order)
   lacc = sum16(lacc);                // rows of 16 lanes = heads
@@ -901,8 +925,10 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
 // their first K pages) and fold it into their partial. Workgroup sp stores its
 // partial in slot sp and takes the (sequence, KV head)'s ticket; the last of
 // the nwg merges them all. A sequence without a full page has only the BF16
-// partition, written straight to the output by its sp = 0 workgroup.
-template <bool kMx, int kTerms, bool kUnder, bool kRunMax>
+// partition, written straight to the output by its sp = 0 workgroup; a
+// sequence with one FP4 workgroup writes that workgroup's o / l directly (no
+// partial, ticket or merge: the merge of a single partial is that quotient).
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
@@ -929,7 +955,16 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     return;
   }
   if (sp >= nwg) return;
-  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax>(A, sm, b, h, sp, L, sp == 0, E);
+  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax, kSlots>(A, sm, b, h, sp, L, sp == 0, E);
+  if (nwg == 1) {
+    const int head = threadIdx.x >> 6, d = 2 * (threadIdx.x & 63);
+    const float l = of_head(mine.l[0], mine.l[1], mine.l[2], mine.l[3], head);
+    float o0 = mine.o0, o1 = mine.o1;
+    if (P.rotate_v) wave_rotate2(o0, o1);                // uniform per workgroup
+    float* out = P.out + ((size_t)b * P.hq + h * kGroup + head) * kD + d;
+    *reinterpret_cast<float2*>(out) = make_float2(o0 / l, o1 / l);
+    return;
+  }
   write_partial(partial_writer(C, bh, sp), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
   if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
@@ -993,12 +1028,20 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   A.L = L;
   const dim3 grid((unsigned)(L.batch * L.hkv * fp4_wgs(L.max_parts))), block(256u);
   const bool under = L.p_mode == 4;
-#define BDFP4_LAUNCH(MX, T, U) hipLaunchKernelGGL((decode_kernel<MX, T, U, false>), grid, block, 0, stream, A)
+  // page slots per kind: the plan's pages_per_partition rounded up to 1, 2, 4
+  const int slots = L.ppp <= 1 ? 1 : (L.ppp == 2 ? 2 : 4);
+#define BDFP4_LAUNCH_S(MX, T, U, R)                                                                  \
+  do {                                                                                               \
+    if (slots == 1) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 1>), grid, block, 0, stream, A); \
+    else if (slots == 2) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 2>), grid, block, 0, stream, A); \
+    else hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 4>), grid, block, 0, stream, A);            \
+  } while (0)
+#define BDFP4_LAUNCH(MX, T, U) BDFP4_LAUNCH_S(MX, T, U, false)
   if (L.run_max) {
     // the host admits the running-max variant only for NVFP4, two query
     // terms and amax2_or_amax6 P
     if (L.mx || L.terms != 2 || !under) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_kernel<false, 2, true, true>), grid, block, 0, stream, A);
+    BDFP4_LAUNCH_S(false, 2, true, true);
   } else if (L.mx) {
     if (L.terms == 2) { if (under) BDFP4_LAUNCH(true, 2, true); else BDFP4_LAUNCH(true, 2, false); }
     else { if (under) BDFP4_LAUNCH(true, 1, true); else BDFP4_LAUNCH(true, 1, false); }
@@ -1007,6 +1050,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     else { if (under) BDFP4_LAUNCH(false, 1, true); else BDFP4_LAUNCH(false, 1, false); }
   }
 #undef BDFP4_LAUNCH
+#undef BDFP4_LAUNCH_S
   return hipGetLastError();
 }
 
