@@ -84,7 +84,9 @@ def writer_bytes(tokens: int, hkv: int, mx: bool) -> int:
 
 # ----------------------------------------------------------------- timing
 
-LAST_PERCENTILES = {"p10": None, "p90": None}   # of the per-launch durations of the last time_launches
+LAST_PERCENTILES = {"p10": None, "p90": None, "n": 0}   # of the per-launch durations of the last time_launches
+PERCENTILE_LAUNCHES = 100      # launches timed one by one for the per-launch statistics
+ROTATE_BYTES = 2 << 30         # buffer copies cycled through per measurement, so none stays in the 256 MB MALL
 
 
 # Untimed launches before a bulk kernel (page writer, key means, page errors)
@@ -135,8 +137,9 @@ def time_launches(fns, steps: int, warmup: int, graph: bool = False):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ms_step = start.elapsed_time(end) / steps
-    # per-launch durations: events around each launch, same stream
-    n_ev = min(steps, 5)
+    # per-launch durations: events around each launch, same stream, over at
+    # least PERCENTILE_LAUNCHES launches
+    n_ev = max(1, -(-PERCENTILE_LAUNCHES // len(fns)))
     evs = []
     torch.cuda.synchronize()
     for _ in range(n_ev):
@@ -149,6 +152,7 @@ def time_launches(fns, steps: int, warmup: int, graph: bool = False):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
     LAST_PERCENTILES["p10"], LAST_PERCENTILES["p90"] = (float(v) for v in np.percentile(per, [10, 90]))
+    LAST_PERCENTILES["n"] = len(per)
     return ms_step, float(np.mean(per)), wall, float(np.median(per))
 
 
@@ -190,8 +194,8 @@ def build_layers(args, arms):
 def bench_batched(args):
     """NVFP4 decode of 16 sequences with lengths drawn from 2K..16K (seeded)
     over one shuffled pool (32 query / 8 KV heads), the library's plan for
-    the batch: one launch per step. Bytes = the sum of every sequence's
-    decode bytes."""
+    the batch: one launch per call, cycled over buffer copies. Bytes = the
+    sum of every sequence's decode bytes."""
     from fp4_kv_cache_nvfp4_amd import synth
 
     return bench_workload(args, synth.batched(0),
@@ -201,18 +205,25 @@ def bench_batched(args):
 def bench_small_configs(args):
     """The two single-layer decode shapes beside the 128K one: the tiny 2K
     single-KV-head case (4 query heads; launch-bound, so its µs is the
-    figure) and the Qwen3-4B-shaped 32K layer (256 full pages in a permuted
-    pool plus a 77-token BF16 tail), each with the library's plan."""
+    figure, measured on one resident buffer set) and the Qwen3-4B-shaped 32K
+    layer (256 full pages in a permuted pool plus a 77-token BF16 tail),
+    cycled over copies of its buffers, each with the library's plan."""
     from fp4_kv_cache_nvfp4_amd import synth
 
-    return {"tiny_2k_1kv": bench_workload(args, synth.tiny(0), "1 sequence, L = 2048, 1 KV head / 4 query heads"),
+    return {"tiny_2k_1kv": bench_workload(args, synth.tiny(0), "1 sequence, L = 2048, 1 KV head / 4 query heads",
+                                          rotate=False),
             "qwen3_4b_32k_layer": bench_workload(args, synth.qwen_32k(0),
                                                  "1 sequence, L = 32,845 (256 pages + 77-token tail), 8 KV / 32 query heads")}
 
 
-def bench_workload(args, wl, what: str):
-    """NVFP4 decode of a seeded numpy workload (pages written by the HIP
-    writer, then one launch per step, the library's plan)."""
+def bench_workload(args, wl, what: str, rotate: bool = True):
+    """NVFP4 decode of a seeded numpy workload: pages written by the HIP
+    writer, one launch per call, the library's plan. With rotate, every
+    buffer the decode reads (cache, query, tables, sink, tail, key means) is
+    copied until the copies hold at least ROTATE_BYTES, and the timed steps
+    cycle through them, so that the figure is an HBM figure and not one of
+    the 256 MB last-level cache; without it one buffer set is re-read and the
+    result says cache_resident."""
     import torch
 
     import fp4_kv_cache_nvfp4_amd as bd
@@ -221,27 +232,40 @@ def bench_workload(args, wl, what: str):
     B, msl = wl.batch, int(wl.seq_lens.max())
     hq, hkv = int(wl.q.shape[1]), int(wl.num_kv_heads)
     ppp, parts = bd.decode_plan(B, hkv, msl, 0)
+    nbytes = sum(decode_bytes(int(L), hq, hkv, 16, False) for L in wl.seq_lens)
+    copies = max(1, -(-ROTATE_BYTES // nbytes)) if rotate else 1
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     k, v, ids = wl.writer_inputs()
-    cache = bd.PagedCache.allocate(r, wl.num_pages, hkv)
-    mu = t(wl.key_shift)
-    bd.quantize_pages(r, cache, t16(k), t16(v), t(ids), mu)
+    kd, vd, idd = t16(k), t16(v), t(ids)
     sk, sv, tk, tv = wl.sink_tail()
     ws = bd.alloc_workspace(bd.decode_workspace_size(B, hq, hkv, msl, ppp))
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
-    call = bd.DecodeCall(r, cache, t16(wl.q), t(wl.block_tables), t(wl.seq_lens), msl, t16(sk), t16(sv),
-                         t16(tk), t16(tv), mu, wl.sigma, ppp, ws, out)
-    ms, per, _, med = time_launches([call], max(args.steps, 20), args.warmup)
+    calls = []
+    for _ in range(copies):
+        cache = bd.PagedCache.allocate(r, wl.num_pages, hkv)
+        mu = t(wl.key_shift)
+        bd.quantize_pages(r, cache, kd, vd, idd, mu)
+        calls.append(bd.DecodeCall(r, cache, t16(wl.q), t(wl.block_tables), t(wl.seq_lens), msl, t16(sk), t16(sv),
+                                   t16(tk), t16(tv), mu, wl.sigma, ppp, ws, out))
+    del kd, vd
+    torch.cuda.synchronize()
+    ms, per, _, med = time_launches(calls, max(args.steps, 20), args.warmup)
     if not torch.isfinite(out).all():
         raise RuntimeError(f"{what}: non-finite decode output")
-    nbytes = sum(decode_bytes(int(L), hq, hkv, 16, False) for L in wl.seq_lens)
-    del cache
+    us = ms * 1e3 / len(calls)
+    res = {"workload": what, "tokens": int(wl.seq_lens.sum()), "pages_per_partition": ppp,
+           "max_partitions": parts, "us": round(us, 3), "us_kernel_events_mean": round(per * 1e3, 3),
+           "us_kernel_events_median": round(med * 1e3, 3),
+           "us_kernel_events_p10": round(LAST_PERCENTILES["p10"] * 1e3, 3),
+           "us_kernel_events_p90": round(LAST_PERCENTILES["p90"] * 1e3, 3),
+           "kernel_events_n": LAST_PERCENTILES["n"],
+           "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "buffer_copies": copies, "bytes_cycled": nbytes * copies, "cache_resident": not rotate}
+    del calls
     torch.cuda.empty_cache()
-    return {"workload": what, "tokens": int(wl.seq_lens.sum()), "pages_per_partition": ppp,
-            "max_partitions": parts, "us": round(ms * 1e3, 3), "us_kernel_events_median": round(med * 1e3, 3),
-            "bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return res
 
 
 def bench_writer(args, mx: bool):
@@ -377,6 +401,96 @@ def cpu_baseline(args):
                       f"the full {L}-token context on oracle-written NVFP4 pages ({nbytes} algorithmic bytes per "
                       f"run), {dt:.1f} s; {cores} host cores visible, BLAS threads {blas_threads}",
             "seconds": round(dt, 2), "us_per_layer_equiv": round(dt / reps * 4 * 1e6, 1)}
+
+
+def _cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return None
+
+
+def _repeat(fn, min_seconds: float, max_reps: int = 1000):
+    reps, dt = 0, 0.0
+    while dt < min_seconds and reps < max_reps:
+        t0 = time.perf_counter()
+        fn()
+        dt += time.perf_counter() - t0
+        reps += 1
+    return reps, dt
+
+
+def cpu_baseline_decode(wl, ppp: int, what: str, min_seconds: float = 10.0):
+    """The oracle decode of a bounded sample of a decode workload (the same
+    recipe and shapes per KV head, fewer KV heads), on pages the oracle writer
+    quantized beforehand (untimed), repeated until min_seconds of CPU time."""
+    from oracle import decode as OD
+    from oracle import recipe as RC
+    from oracle import writer as W
+
+    r = RC.nvfp4_default().with_(tau=1.0)
+    cache = W.empty_cache(wl.num_pages, wl.num_kv_heads, r)
+    k, v, ids = wl.writer_inputs()
+    W.write_pages(r, cache, k, v, ids, wl.key_shift)
+    sk, sv, tk, tv = wl.sink_tail()
+    reps, dt = _repeat(lambda: OD.decode(r, cache, wl.q, wl.block_tables, wl.seq_lens, sk, sv, tk, tv,
+                                         wl.key_shift, wl.sigma, ppp), min_seconds)
+    hq, hkv = int(wl.q.shape[1]), int(wl.num_kv_heads)
+    nbytes = sum(decode_bytes(int(L), hq, hkv, 16, False) for L in wl.seq_lens)
+    cores = len(os.sched_getaffinity(0))
+    threads = _cpu_threads()
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": threads or cores, "kind": "oracle",
+            "us_per_decode": round(dt / reps * 1e6, 1),
+            "sample": f"{reps} runs of the oracle float64 decode of {what} ({nbytes} algorithmic bytes per run, "
+                      f"pages_per_partition {ppp}), {dt:.1f} s; {cores} host cores visible, BLAS threads {threads}"}
+
+
+def cpu_baseline_writer(min_seconds: float = 10.0, pages: int = 32):
+    """The oracle page writer (NVFP4: K four_six with rotation and centering,
+    V amax6) on a bounded sample of the prefill write: `pages` pages x 8 KV
+    heads of the same recipe of keys and values, repeated until min_seconds."""
+    from fp4_kv_cache_nvfp4_amd import synth
+    from oracle import recipe as RC
+    from oracle import writer as W
+
+    r = RC.nvfp4_default().with_(tau=1.0)
+    w = synth.write_workload(0, tokens=pages * 128, num_kv_heads=8)
+    cache = W.empty_cache(w.num_pages, 8, r)
+    reps, dt = _repeat(lambda: W.write_pages(r, cache, w.k_rows, w.v_rows, w.page_ids, w.key_shift), min_seconds)
+    nbytes = writer_bytes(pages * 128, 8, False)
+    cores = len(os.sched_getaffinity(0))
+    threads = _cpu_threads()
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": threads or cores, "kind": "oracle",
+            "tokens_per_s": round(pages * 128 * reps / dt, 1),
+            "sample": f"{reps} runs of the oracle NVFP4 page writer over {pages} pages x 8 KV heads "
+                      f"({pages * 128} tokens, {nbytes} algorithmic bytes per run), {dt:.1f} s; {cores} host cores "
+                      f"visible, BLAS threads {threads}"}
+
+
+def _plan(batch: int, hkv: int, max_seq_len: int):
+    """The library's split plan for these sizes (host call, no GPU), so the
+    oracle decodes with the partitioning the GPU arm uses."""
+    import fp4_kv_cache_nvfp4_amd as bd
+
+    return bd.decode_plan(batch, hkv, max_seq_len, 0)
+
+
+def cpu_baselines_beside():
+    """Oracle timings beside the configurations other than the headline."""
+    from fp4_kv_cache_nvfp4_amd import synth
+
+    out = {"writer_131072x8_sample": cpu_baseline_writer()}
+    out["tiny_2k_1kv"] = cpu_baseline_decode(synth.tiny(0), _plan(1, 1, 2048)[0],
+                                             "the tiny 2K single-KV-head workload (whole)")
+    out["qwen3_4b_32k_layer"] = cpu_baseline_decode(
+        synth.decode_workload("qwen3_4b_32k_sample", 0, [32845], 4, 1, "qwen"), _plan(1, 8, 32845)[0],
+        "1 of the 8 KV heads (4 query heads) of the 32,845-token layer")
+    bwl = synth.batched(0, num_kv_heads=1)
+    bppp, _ = _plan(bwl.batch, 8, int(bwl.seq_lens.max()))
+    out["batched_16x_2k_16k"] = cpu_baseline_decode(
+        bwl, bppp, "1 of the 8 KV heads (4 query heads) of the 16 sequences of 2K..16K tokens")
+    return out
 
 
 # ----------------------------------------------------------------- counter traffic
@@ -529,10 +643,19 @@ def main():
     if not args.no_calibration:
         calibration = bench_key_means(args)
         print(f"[bench] key means: {calibration}", file=sys.stderr, flush=True)
-    cpu = None
+    cpu, cpu_beside = None, None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(args)
+        print("[bench] cpu baselines beside the other configurations (oracle)", file=sys.stderr, flush=True)
+        cpu_beside = cpu_baselines_beside()
+        if writer:
+            writer["cpu_baseline"] = cpu_beside["writer_131072x8_sample"]
+        for k in ("tiny_2k_1kv", "qwen3_4b_32k_layer"):
+            if k in small:
+                small[k]["cpu_baseline"] = cpu_beside[k]
+        if batched is not None:
+            batched["cpu_baseline"] = cpu_beside["batched_16x_2k_16k"]
     traffic, traffic_src = counter_traffic()
     h = res["nvfp4"]
     # average launch duration over the timed region: the start/end events of

@@ -201,11 +201,17 @@ def qwen_128k_layer(layer: int) -> DecodeWorkload:
     return decode_workload("qwen3_4b_128k", layer, [131072], 32, 8, "qwen")
 
 
-def batched(seed: int = 0, n_seqs: int = 16, lo: int = 2048, hi: int = 16384) -> DecodeWorkload:
-    """16 sequences with L ~ U{lo..hi}, shared shuffled pool."""
+def batched_lengths(seed: int = 0, n_seqs: int = 16, lo: int = 2048, hi: int = 16384) -> np.ndarray:
+    """The sequence lengths of ``batched``: L ~ U{lo..hi}, seeded."""
     rng = np.random.Generator(np.random.PCG64(seed + 1_000_003))
-    lens = rng.integers(lo, hi + 1, size=n_seqs)
-    return decode_workload("batched_16x_2k_16k", seed, lens, 32, 8, "qwen")
+    return rng.integers(lo, hi + 1, size=n_seqs)
+
+
+def batched(seed: int = 0, n_seqs: int = 16, lo: int = 2048, hi: int = 16384, num_kv_heads: int = 8) -> DecodeWorkload:
+    """16 sequences with L ~ U{lo..hi}, shared shuffled pool, 4 query heads
+    per KV head."""
+    return decode_workload("batched_16x_2k_16k", seed, batched_lengths(seed, n_seqs, lo, hi), 4 * num_kv_heads,
+                           num_kv_heads, "qwen")
 
 
 @dataclass
