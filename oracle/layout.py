@@ -25,6 +25,8 @@ NVFP4 K scales (1024 B), token t, 16-block j (0..7):
     byte = (((j >> 1) * 16 + (t & 15)) * 8 + (t >> 4)) * 2 + (j & 1)
 MXFP4 K scales (512 B), token t, 32-block j (0..3):
     byte = (j * 16 + (t & 15)) * 8 + (t >> 4)
+NVFP4 K scales of the channel geometry (1024 B), token block b = t >> 4 (0..7), channel c:
+    byte = b * 128 + c
 NVFP4 V scales (1024 B), token t, block j (0..7):
     byte = (((t >> 5) * 4 + ((t >> 3) & 3)) * 8 + j) * 8 + (t & 7)
 MXFP4 V scales (512 B), token t, block j (0..3):
@@ -71,6 +73,29 @@ def k_scale_byte(t, j, mx: bool):
     if mx:
         return (j * 16 + (t & 15)) * 8 + (t >> 4)
     return (((j >> 1) * 16 + (t & 15)) * 8 + (t >> 4)) * 2 + (j & 1)
+
+
+def k_scale_byte_channel(b, c):
+    """K scale of token block b (16 tokens) and channel c, channel geometry."""
+    return b * 128 + c
+
+
+def pack_k_scales_channel(sc: np.ndarray) -> np.ndarray:
+    """sc: uint8 [..., 8 token blocks, 128 channels] -> bytes [..., 1024]."""
+    sc = np.asarray(sc, dtype=np.uint8)
+    assert sc.shape[-2:] == (PAGE // 16, D)
+    b = np.arange(PAGE // 16)[:, None]
+    c = np.arange(D)[None, :]
+    out = np.zeros(sc.shape[:-2] + (scale_bytes(False),), dtype=np.uint8)
+    out[..., k_scale_byte_channel(b, c).reshape(-1)] = sc.reshape(sc.shape[:-2] + (-1,))
+    return out
+
+
+def unpack_k_scales_channel(buf: np.ndarray) -> np.ndarray:
+    buf = np.asarray(buf, dtype=np.uint8)
+    b = np.arange(PAGE // 16)[:, None]
+    c = np.arange(D)[None, :]
+    return buf[..., k_scale_byte_channel(b, c)].astype(np.uint8)
 
 
 def v_scale_byte(t, j, mx: bool):

@@ -13,7 +13,8 @@ From "BitDecoding-FP4 evaluation/config.py":
 * ``probability_environment``: with the scaling off, P takes mode amax6; the
   multiplier c takes the values 1 and 8; an uncalibrated tau is refused
   outside calibration, a calibrated one lies in [0, 448];
-* KV_MODES ``bitdecoding-nvfp4`` keeps a 16-token BF16 sink;
+* KV_MODES ``bitdecoding-nvfp4`` keeps a 16-token BF16 sink and names a key
+  scale geometry, ``local`` unless overridden;
   ``bitdecoding-mxfp4`` uses mxfp4_search with the same sink, two query terms
   and Hadamard rotation.
 
@@ -25,6 +26,16 @@ import math
 from dataclasses import dataclass, replace
 
 from . import quant as Q
+
+
+# key scale geometries ("BitDecoding-FP4 evaluation/config.py", KV_MODES
+# bitdecoding-nvfp4 key_scale_geometry, default "local"; "kv-landlords
+# scripts/quant_ab.py", SCHEMES: keys quantized per "channel" as against per
+# "headdim"). local: an NVFP4 key block is 16 consecutive channels of one
+# token (the head-dim blocks every other tensor uses); channel: 16 consecutive
+# tokens of one channel, inside one frozen page.
+LOCAL = "local"
+CHANNEL = "channel"
 
 
 class RecipeError(ValueError):
@@ -49,6 +60,7 @@ class Recipe:
     tau: float = float("nan")
     rotate_v: bool = False          # recipe variant: values rotated as keys are, output rotated back
     p_running_max: bool = False     # recipe variant: P of each 16-token block against the running maximum
+    key_scale_geometry: str = "local"   # "local": K blocks of 16 channels of one token; "channel": 16 tokens of one channel
 
     def with_(self, **kw) -> "Recipe":
         return replace(self, **kw)
@@ -97,6 +109,10 @@ def validate(r: Recipe) -> None:
         raise RecipeError("query_terms is 1 or 2")
     if r.sink_tokens < 0 or r.sink_tokens >= 128 or r.sink_tokens % 16:
         raise RecipeError("sink_tokens is a multiple of 16 in [0, 112]")
+    if r.key_scale_geometry not in (LOCAL, CHANNEL):
+        raise RecipeError(f"bad key scale geometry {r.key_scale_geometry!r}")
+    if r.key_scale_geometry == CHANNEL and r.scale_mode_k not in (Q.FOUR_SIX, Q.AMAX6):
+        raise RecipeError("the channel key geometry takes NVFP4 key blocks (four_six or amax6)")
     for m, ok in ((r.scale_mode_k, (Q.FOUR_SIX, Q.AMAX6, Q.MXFP4_SEARCH, Q.NONE)),
                   (r.scale_mode_v, (Q.AMAX6, Q.MXFP4_SEARCH, Q.NONE)),
                   (r.scale_mode_q, (Q.AMAX6, Q.MXFP4_SEARCH, Q.NONE))):

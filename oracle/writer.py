@@ -17,6 +17,11 @@ the comment that the runner creates missing key means):
     y = rotate(x)                  (Hadamard; see rotation.py)
     codes, scales = quantize(y, scale_mode_k)
 
+With the channel key scale geometry (KV_MODES key_scale_geometry; quant_ab.py
+SCHEMES per-channel keys) the same y is quantized in blocks of 16 tokens of
+one channel instead of 16 channels of one token; its scales are stored
+[token block][channel].
+
 Value path: codes, scales = quantize(float32(v), scale_mode_v); the rotation
 is listed under key quantization only, so values are not rotated - except in
 the rotate_v recipe variant (the alternative reading: rotate V as well and
@@ -30,7 +35,7 @@ import numpy as np
 from . import layout
 from . import quant as Q
 from .formats import bf16_to_f32
-from .recipe import Recipe
+from .recipe import CHANNEL, Recipe
 from .rotation import rotate
 
 
@@ -44,6 +49,18 @@ def key_rows(k_f32: np.ndarray, mu, rotation: bool) -> np.ndarray:
 
 def quantize_k_rows(k_f32, mu, rotation: bool, mode: str):
     return Q.quantize(key_rows(k_f32, mu, rotation), mode)
+
+
+def quantize_k_page_channel(y: np.ndarray, mode: str):
+    """Channel key geometry: y [..., 128 tokens, 128 channels] float32 (the
+    centered, rotated keys of whole pages). Every channel's column is cut into
+    8 blocks of 16 consecutive tokens, each quantized with the key scale mode
+    exactly as a 16-channel block would be. Returns (nibbles [..., tok, ch],
+    e4m3 codes [..., 8 token blocks, ch])."""
+    y = np.asarray(y, dtype=np.float32)
+    cols = np.swapaxes(y, -1, -2)                 # [..., ch, tok]
+    nib, sc = Q.quantize(cols, mode)              # blocks of 16 along tokens
+    return np.swapaxes(nib, -1, -2), np.swapaxes(sc, -1, -2)
 
 
 def value_rows(v_f32, rotate_v: bool) -> np.ndarray:
@@ -85,15 +102,19 @@ def write_pages(recipe: Recipe, cache: dict, k_bf16: np.ndarray, v_bf16: np.ndar
         mu = np.asarray(key_shift, dtype=np.float32).reshape(1, 1, hkv, layout.D)
     kmx = recipe.scale_mode_k == Q.MXFP4_SEARCH
     vmx = recipe.scale_mode_v == Q.MXFP4_SEARCH
-    kn, ks = quantize_k_rows(k, mu, recipe.rotation, recipe.scale_mode_k)
     vn, vs = quantize_v_rows(v, recipe.scale_mode_v, recipe.rotate_v)
-    # [n, tok, h, ...] -> [n, h, tok, ...]
-    kn = kn.transpose(0, 2, 1, 3)
-    ks = ks.transpose(0, 2, 1, 3)
+    if recipe.key_scale_geometry == CHANNEL:
+        y = key_rows(k, mu, recipe.rotation).transpose(0, 2, 1, 3)     # [n, h, tok, ch]
+        kn, ks = quantize_k_page_channel(y, recipe.scale_mode_k)
+        cache["k_scales"][page_ids] = layout.pack_k_scales_channel(ks)
+    else:
+        kn, ks = quantize_k_rows(k, mu, recipe.rotation, recipe.scale_mode_k)
+        # [n, tok, h, ...] -> [n, h, tok, ...]
+        kn = kn.transpose(0, 2, 1, 3)
+        cache["k_scales"][page_ids] = layout.pack_scales(ks.transpose(0, 2, 1, 3), "k", kmx)
     vn = vn.transpose(0, 2, 1, 3)
     vs = vs.transpose(0, 2, 1, 3)
     cache["k_codes"][page_ids] = layout.pack_codes(kn, "k")
-    cache["k_scales"][page_ids] = layout.pack_scales(ks, "k", kmx)
     cache["v_codes"][page_ids] = layout.pack_codes(vn, "v", vmx)
     cache["v_scales"][page_ids] = layout.pack_scales(vs, "v", vmx)
     return cache
@@ -106,8 +127,12 @@ def read_page_head(recipe: Recipe, cache: dict, page: int, head: int):
     kmx = recipe.scale_mode_k == Q.MXFP4_SEARCH
     vmx = recipe.scale_mode_v == Q.MXFP4_SEARCH
     kn = layout.unpack_codes(cache["k_codes"][page, head], "k")
-    ks = layout.unpack_scales(cache["k_scales"][page, head], "k", kmx)
     vn = layout.unpack_codes(cache["v_codes"][page, head], "v", vmx)
     vs = layout.unpack_scales(cache["v_scales"][page, head], "v", vmx)
-    return (Q.dequantize(kn, ks, recipe.scale_mode_k),
-            Q.dequantize(vn, vs, recipe.scale_mode_v))
+    if recipe.key_scale_geometry == CHANNEL:
+        ks = layout.unpack_k_scales_channel(cache["k_scales"][page, head])     # [8, 128]
+        k_hat = Q.dequantize(kn.T, ks.T, recipe.scale_mode_k).T                # blocks along tokens
+    else:
+        ks = layout.unpack_scales(cache["k_scales"][page, head], "k", kmx)
+        k_hat = Q.dequantize(kn, ks, recipe.scale_mode_k)
+    return k_hat, Q.dequantize(vn, vs, recipe.scale_mode_v)
