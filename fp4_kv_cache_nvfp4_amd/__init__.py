@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libbdfp4.so")
 
 OK, E_INVALID, E_UNCALIBRATED, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
 SCALE_NONE, SCALE_AMAX6, SCALE_FOUR_SIX, SCALE_MXFP4_SEARCH, SCALE_AMAX2_OR_AMAX6 = 0, 1, 2, 3, 4
+KEY_GEOMETRY_LOCAL, KEY_GEOMETRY_CHANNEL = 0, 1
 
 
 class Bdfp4Error(RuntimeError):
@@ -43,6 +44,7 @@ class Recipe(ctypes.Structure):
         ("tau", ctypes.c_float),
         ("rotate_v", ctypes.c_int32),
         ("p_running_max", ctypes.c_int32),
+        ("key_scale_geometry", ctypes.c_int32),
     ]
 
     def replace(self, **kw) -> "Recipe":

@@ -61,6 +61,11 @@ bdfp4_status check_kv_recipe(const bdfp4_recipe* r) {
     return fail(BDFP4_E_UNSUPPORTED,
                 "K/V scale modes (%d, %d): this library has kernels for (four_six|amax6, amax6) and "
                 "(mxfp4_search, mxfp4_search)", km, vm);
+  if (r->key_scale_geometry != BDFP4_KEY_GEOMETRY_LOCAL && r->key_scale_geometry != BDFP4_KEY_GEOMETRY_CHANNEL)
+    return fail(BDFP4_E_INVALID, "key_scale_geometry must be 0 (local) or 1 (channel), got %d",
+                r->key_scale_geometry);
+  if (r->key_scale_geometry == BDFP4_KEY_GEOMETRY_CHANNEL && !is_nv_kv(r))
+    return fail(BDFP4_E_UNSUPPORTED, "the channel key geometry has kernels for NVFP4 keys (four_six or amax6) only");
   return BDFP4_OK;
 }
 
@@ -122,6 +127,8 @@ bdfp4_status check_recipe(const bdfp4_recipe* r) {
   if (r->p_running_max && (!is_nv_kv(r) || r->query_terms != 2 || pm != BDFP4_SCALE_AMAX2_OR_AMAX6))
     return fail(BDFP4_E_UNSUPPORTED,
                 "p_running_max has a kernel for NVFP4 pages, two query terms and amax2_or_amax6 P only");
+  if (r->p_running_max && r->key_scale_geometry == BDFP4_KEY_GEOMETRY_CHANNEL)
+    return fail(BDFP4_E_UNSUPPORTED, "p_running_max has no kernel for the channel key geometry");
   return BDFP4_OK;
 }
 
@@ -210,6 +217,7 @@ bdfp4_status bdfp4_recipe_default_nvfp4(bdfp4_recipe* r) {
   r->query_terms = 2;
   r->c = 8;
   r->tau = NAN;
+  r->key_scale_geometry = BDFP4_KEY_GEOMETRY_LOCAL;
   return ok();
 }
 
@@ -277,6 +285,7 @@ bdfp4_status bdfp4_quantize_pages(const bdfp4_recipe* r, const bdfp4_cache* cach
   L.rotate_v = r->rotate_v;
   L.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
   L.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
+  L.k_chan = r->key_scale_geometry == BDFP4_KEY_GEOMETRY_CHANNEL;
   return hip_status(bdfp4::launch_writer(L, static_cast<hipStream_t>(stream)), "page writer launch");
 }
 
@@ -321,6 +330,7 @@ bdfp4_status bdfp4_append_tokens(const bdfp4_recipe* r, const bdfp4_cache* cache
   L.w.rotate_v = r->rotate_v;
   L.w.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
   L.w.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
+  L.w.k_chan = r->key_scale_geometry == BDFP4_KEY_GEOMETRY_CHANNEL;
   L.k_new = k_new;
   L.v_new = v_new;
   L.positions = positions;
@@ -409,6 +419,7 @@ bdfp4_status bdfp4_page_errors(const bdfp4_recipe* r, const bdfp4_cache* cache, 
   L.rotate_v = r->rotate_v;
   L.k_mode = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX ? 2 : (r->scale_mode_k == BDFP4_SCALE_AMAX6 ? 1 : 3);
   L.v_mode = r->scale_mode_v == BDFP4_SCALE_AMAX6 ? 1 : 3;
+  L.k_chan = r->key_scale_geometry == BDFP4_KEY_GEOMETRY_CHANNEL;
   return hip_status(bdfp4::launch_page_errors(L, workspace, sums_out, static_cast<hipStream_t>(stream)),
                     "page errors launch");
 }
@@ -510,6 +521,7 @@ static bdfp4_status decode_impl(const bdfp4_recipe* r, const bdfp4_cache* cache,
   L.rotation = r->rotation;
   L.rotate_v = r->rotate_v;
   L.run_max = r->p_running_max;
+  L.k_chan = r->key_scale_geometry == BDFP4_KEY_GEOMETRY_CHANNEL;
   L.key_smoothing = r->key_smoothing;
   L.mx = is_mx_kv(r) ? 1 : 0;
   L.k_four_six = r->scale_mode_k == BDFP4_SCALE_FOUR_SIX;

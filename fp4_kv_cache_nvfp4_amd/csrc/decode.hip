@@ -187,6 +187,7 @@ struct Smem {
   int bad[4];                               // per wave: its block table names an invalid page
   int tick;
   float tmax[4][4][kWaveTok / 16];          // running-max variant: per wave, head, 16-token block: raw maximum
+  uint32_t ksc[4][256];                     // channel key geometry: per wave, the K page's scales [token block][channel]
 };
 
 // ------------------------------------------------------------ partials
@@ -556,7 +557,7 @@ __device__ __forceinline__ Early early_loads(const DecodeLaunch& P, int b, int h
 // workgroup's partial (returned; the caller stores it). With bf16 the
 // workgroup first computes the (sequence, KV head)'s BF16 partition, then
 // requests its first K pages, and folds the partition into the same partial.
-template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots>
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
 __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int L, bool bf16, const Early& E) {
   const DecodeLaunch& P = A.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -658,6 +659,10 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   auto k_page = [&](const KPage& cur, int pi) {
     const int skip = pi == 0 ? sink_tiles : 0;                  // uniform
     float pa = kNegInf, pb = kNegInf;
+    // channel key geometry: the page's 1 KiB of scales, [token block][channel],
+    // in this wave's LDS (the wave reads it back in order); tile t takes the
+    // 32 scales of its lanes' channels 32 kg .. +32 from block t
+    if (kChan) reinterpret_cast<uint4*>(&sm.ksc[wave][0])[lane] = cur.sc;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int local = pi * kPage + t * 16;                    // first token of the tile - 128 p0
@@ -668,6 +673,21 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
         // scale word t >> 2 is this lane's (token, channel block) E8M0 code
         const uint4 cw = cur.code[t];
         acc = mfma_fp4_scaled_byte(t & 3, aq4, sa4, (u32x4_t){cw.x, cw.y, cw.z, cw.w}, word_of(cur.sc, t >> 2), acc);
+      } else if (kChan) {
+        // the scale of channels 32 kg + 8 c + 2 b, +1 is the byte pair
+        // 8 c + 2 b of the lane's 32: dword 2 c + (b >> 1), half b & 1
+        const uint4 s_lo = *reinterpret_cast<const uint4*>(&sm.ksc[wave][32 * t + 8 * kg]);
+        const uint4 s_hi = *reinterpret_cast<const uint4*>(&sm.ksc[wave][32 * t + 8 * kg + 4]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t cw = word_of(cur.code[t], c);
+          const uint32_t sw0 = word_of(c < 2 ? s_lo : s_hi, (2 * c) & 3);
+          const uint32_t sw1 = word_of(c < 2 ? s_lo : s_hi, (2 * c + 1) & 3);
+          bk[c] = (u32x4_t){u32_of(grid_f16_pair(cw, 0) * e4m3_pair_f16(sw0, false)),
+                            u32_of(grid_f16_pair(cw, 1) * e4m3_pair_f16(sw0, true)),
+                            u32_of(grid_f16_pair(cw, 2) * e4m3_pair_f16(sw1, false)),
+                            u32_of(grid_f16_pair(cw, 3) * e4m3_pair_f16(sw1, true))};
+        }
       } else {
         const f16x2_t sp2 = e4m3_pair_f16(word_of(cur.sc, t >> 1), (t & 1) != 0);   // (s_lo, s_hi)
         const f16x2_t slo = {sp2[0], sp2[0]}, shi = {sp2[1], sp2[1]};
@@ -928,7 +948,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
 // partition, written straight to the output by its sp = 0 workgroup; a
 // sequence with one FP4 workgroup writes that workgroup's o / l directly (no
 // partial, ticket or merge: the merge of a single partial is that quotient).
-template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots>
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
@@ -955,7 +975,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     return;
   }
   if (sp >= nwg) return;
-  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax, kSlots>(A, sm, b, h, sp, L, sp == 0, E);
+  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax, kSlots, kChan>(A, sm, b, h, sp, L, sp == 0, E);
   if (nwg == 1) {
     const int head = threadIdx.x >> 6, d = 2 * (threadIdx.x & 63);
     const float l = of_head(mine.l[0], mine.l[1], mine.l[2], mine.l[3], head);
@@ -1030,18 +1050,25 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   const bool under = L.p_mode == 4;
   // page slots per kind: the plan's pages_per_partition rounded up to 1, 2, 4
   const int slots = L.ppp <= 1 ? 1 : (L.ppp == 2 ? 2 : 4);
-#define BDFP4_LAUNCH_S(MX, T, U, R)                                                                  \
-  do {                                                                                               \
-    if (slots == 1) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 1>), grid, block, 0, stream, A); \
-    else if (slots == 2) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 2>), grid, block, 0, stream, A); \
-    else hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 4>), grid, block, 0, stream, A);            \
+#define BDFP4_LAUNCH_S(MX, T, U, R, C)                                                                  \
+  do {                                                                                                  \
+    if (slots == 1) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 1, C>), grid, block, 0, stream, A);    \
+    else if (slots == 2) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 2, C>), grid, block, 0, stream, A); \
+    else hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 4, C>), grid, block, 0, stream, A);               \
   } while (0)
-#define BDFP4_LAUNCH(MX, T, U) BDFP4_LAUNCH_S(MX, T, U, false)
-  if (L.run_max) {
+#define BDFP4_LAUNCH(MX, T, U) BDFP4_LAUNCH_S(MX, T, U, false, false)
+#define BDFP4_LAUNCH_CH(T, U) BDFP4_LAUNCH_S(false, T, U, false, true)
+  if (L.k_chan) {
+    // the host admits the channel key geometry for NVFP4 pages without the
+    // running-maximum variant only
+    if (L.mx || L.run_max) return hipErrorInvalidValue;
+    if (L.terms == 2) { if (under) BDFP4_LAUNCH_CH(2, true); else BDFP4_LAUNCH_CH(2, false); }
+    else { if (under) BDFP4_LAUNCH_CH(1, true); else BDFP4_LAUNCH_CH(1, false); }
+  } else if (L.run_max) {
     // the host admits the running-max variant only for NVFP4, two query
     // terms and amax2_or_amax6 P
     if (L.mx || L.terms != 2 || !under) return hipErrorInvalidValue;
-    BDFP4_LAUNCH_S(false, 2, true, true);
+    BDFP4_LAUNCH_S(false, 2, true, true, false);
   } else if (L.mx) {
     if (L.terms == 2) { if (under) BDFP4_LAUNCH(true, 2, true); else BDFP4_LAUNCH(true, 2, false); }
     else { if (under) BDFP4_LAUNCH(true, 1, true); else BDFP4_LAUNCH(true, 1, false); }
@@ -1050,6 +1077,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     else { if (under) BDFP4_LAUNCH(false, 1, true); else BDFP4_LAUNCH(false, 1, false); }
   }
 #undef BDFP4_LAUNCH
+#undef BDFP4_LAUNCH_CH
 #undef BDFP4_LAUNCH_S
   return hipGetLastError();
 }

@@ -17,6 +17,7 @@ struct WriterLaunch {
   void* v_scales;
   int32_t num_pages, hkv, n_pages, rotation, rotate_v;
   int32_t k_mode, v_mode;  // 1 amax6, 2 four_six, 3 mxfp4_search
+  int32_t k_chan;          // channel key scale geometry (NVFP4 keys only)
 };
 
 hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream);
@@ -59,7 +60,7 @@ hipError_t launch_p_blocks(const float* pp, int n_blocks, int mode, float tau, u
 
 struct DecodeLaunch {
   // recipe
-  int32_t sink, rotation, key_smoothing, mx, k_four_six, p_mode, terms, c, rotate_v, run_max;
+  int32_t sink, rotation, key_smoothing, mx, k_four_six, p_mode, terms, c, rotate_v, run_max, k_chan;
   float tau;
   // cache
   const uint8_t* k_codes;

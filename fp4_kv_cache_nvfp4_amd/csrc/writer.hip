@@ -35,6 +35,7 @@ struct WriterArgs {
   int32_t n_pages;
   int32_t rotation;
   int32_t rotate_v;          // values rotated before quantization (recipe variant)
+  int32_t k_chan;            // channel key scale geometry (blocks of 16 tokens of one channel)
 };
 
 // Row t (token 0..127) of input page in_page of the bulk writer's
@@ -59,9 +60,18 @@ struct TailRows {
 // (= physical page * hkv + h); rows(t) is the address of the page's row t
 // (128 bf16). All 256 threads of the workgroup call it (it has barriers).
 // kKMode / kVMode: 1 amax6, 2 four_six, 3 mxfp4_search.
-template <int kKMode, int kVMode, bool is_v, class Rows>
+//
+// kChan: the channel key scale geometry ("BitDecoding-FP4
+// evaluation/config.py", KV_MODES key_scale_geometry; "kv-landlords
+// scripts/quant_ab.py", SCHEMES per-channel keys): a key block is 16 tokens of
+// one channel. Each wave puts its tile's centered, rotated rows in LDS
+// (float32 [token][channel], tbuf: 16 x 128 floats per wave), and lane l
+// quantizes the 16-token columns of channels 2l and 2l + 1 with the same
+// block quantizer; the codes keep the K page layout (a byte holds channels
+// 2l, 2l + 1 of one token), the scales are stored [token block][channel].
+template <int kKMode, int kVMode, bool is_v, bool kChan, class Rows>
 __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows, int h, size_t blk,
-                                          uint8_t* s_codes, uint8_t* s_scales) {
+                                          uint8_t* s_codes, uint8_t* s_scales, float* tbuf) {
   constexpr bool kKMx = kKMode == 3, kVMx = kVMode == 3;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -99,6 +109,39 @@ __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows,
         for (int i = 0; i < 32; ++i) x[i] = __fsub_rn(x[i], mu[i]);
       }
       if (a.rotation) rotate_row_quad(x, q);
+      if constexpr (kChan) {
+        float* tb = tbuf + wave * (16 * kD);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<float4*>(tb + n * kD + 32 * q + 4 * i) =
+              make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+        // the wave reads back its own LDS rows (a wave's LDS operations
+        // complete in order): the column of channels 2 lane, 2 lane + 1
+        float xa[16], xb[16];
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          const float2 v2 = *reinterpret_cast<const float2*>(tb + tt * kD + 2 * lane);
+          xa[tt] = v2.x;
+          xb[tt] = v2.y;
+        }
+        uint32_t pa[2], pb[2];
+        const uint32_t sa = nv_block<kKMode == 2>(xa, pa);
+        const uint32_t sb = nv_block<kKMode == 2>(xb, pb);
+        *reinterpret_cast<uint16_t*>(&s_scales[tile * kD + 2 * lane]) = (uint16_t)(sa | (sb << 8));
+        // token t's byte of channels 2 lane (low nibble), 2 lane + 1
+        uint8_t* cb = s_codes + tile * 1024 + (lane >> 4) * 256 + (lane & 15);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t ev = (pa[k] & 0x0F0F0F0Fu) | ((pb[k] & 0x0F0F0F0Fu) << 4);            // tokens 8k + 2m
+          const uint32_t od = ((pa[k] >> 4) & 0x0F0F0F0Fu) | (((pb[k] >> 4) & 0x0F0F0F0Fu) << 4);  // 8k + 2m + 1
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            cb[(8 * k + 2 * m) * 16] = (uint8_t)(ev >> (8 * m));
+            cb[(8 * k + 2 * m + 1) * 16] = (uint8_t)(od >> (8 * m));
+          }
+        }
+        continue;
+      }
       uint32_t pk[4];
       if (kKMx) {
         const uint32_t sc = mx_block(x, pk);
@@ -166,6 +209,12 @@ __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows,
     if (tid * 16 < sbytes)
       *reinterpret_cast<uint4*>(a.k_scales + blk * sbytes + tid * 16) =
           *reinterpret_cast<const uint4*>(&s_scales[tid * 16]);
+    if constexpr (kChan) {
+      uint4* dc = reinterpret_cast<uint4*>(a.k_codes + blk * 8192);
+      const uint4* sc4 = reinterpret_cast<const uint4*>(s_codes);
+      dc[tid] = sc4[tid];
+      dc[tid + 256] = sc4[tid + 256];
+    }
   } else {
     const int sbytes = kVMx ? 512 : 1024;
     uint4* dc = reinterpret_cast<uint4*>(a.v_codes + blk * 8192);
@@ -181,19 +230,20 @@ __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows,
 // At least 3 (MXFP4) / 4 (NVFP4) waves per SIMD: the MXFP4 body would take
 // 171 VGPRs (2 waves) unbounded and fits 168 without spilling; NVFP4 fits
 // 4 waves as it is (at 5 it would spill).
-template <int kKMode, int kVMode>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kKMode == 3 ? 3 : 4)))
+template <int kKMode, int kVMode, bool kChan>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kKMode == 3 || kChan ? 3 : 4)))
 writer_kernel(WriterArgs a) {
   __shared__ __align__(16) uint8_t s_codes[8192];
   __shared__ __align__(16) uint8_t s_scales[1024];
+  __shared__ __align__(16) float tbuf[kChan ? 4 * 16 * kD : 4];
   const int ph = blockIdx.x;       // input page * hkv + head
   const bool is_v = blockIdx.y != 0;
   const int in_page = ph / a.hkv, h = ph - in_page * a.hkv;
   const int dst = a.page_ids[in_page];
   if (dst < 0 || dst >= a.num_pages) return;
   const WriterRows rows{is_v ? a.v : a.k, in_page, a.hkv, h};
-  if (is_v) page_head<kKMode, kVMode, true>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales);
-  else page_head<kKMode, kVMode, false>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales);
+  if (is_v) page_head<kKMode, kVMode, true, kChan>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales, tbuf);
+  else page_head<kKMode, kVMode, false, kChan>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales, tbuf);
 }
 
 // Decode-time append with freeze-at-fill ("kv-landlords scripts/quant_ab.py"
@@ -216,10 +266,11 @@ struct AppendArgs {
   int32_t max_pages_per_seq, sink_tokens;
 };
 
-template <int kKMode, int kVMode>
+template <int kKMode, int kVMode, bool kChan>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   __shared__ __align__(16) uint8_t s_codes[8192];
   __shared__ __align__(16) uint8_t s_scales[1024];
+  __shared__ __align__(16) float tbuf[kChan ? 4 * 16 * kD : 4];
   const int hkv = a.w.hkv;
   const int bh = blockIdx.x, b = bh / hkv, h = bh - b * hkv;
   const bool is_v = blockIdx.y != 0;
@@ -238,8 +289,8 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   const int dst = a.block_tables[(size_t)b * a.max_pages_per_seq + pos / kPage];
   if (dst < 0 || dst >= a.w.num_pages) return;
   const TailRows rows{tail, nrow};
-  if (is_v) page_head<kKMode, kVMode, true>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales);
-  else page_head<kKMode, kVMode, false>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales);
+  if (is_v) page_head<kKMode, kVMode, true, kChan>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales, tbuf);
+  else page_head<kKMode, kVMode, false, kChan>(a.w, rows, h, (size_t)dst * hkv + h, s_codes, s_scales, tbuf);
 }
 
 // Quantization diagnostics ("kv-landlords scripts/quant_ab.py" compares cache
@@ -261,7 +312,7 @@ __device__ __forceinline__ double scale_f64(uint32_t code) {
   return (double)e4m3_value(code);                          // E4M3 (exact in float32)
 }
 
-template <bool kKMx, bool kVMx, bool is_v>
+template <bool kKMx, bool kVMx, bool is_v, bool kChan>
 __device__ __forceinline__ void page_error(const WriterArgs& a, int in_page, int h, size_t blk, uint8_t* s_codes,
                                            uint8_t* s_scales, double& err, double& ref) {
   constexpr bool kMx = is_v ? kVMx : kKMx;
@@ -304,8 +355,9 @@ __device__ __forceinline__ void page_error(const WriterArgs& a, int in_page, int
       if (!is_v) {
         cb = (t >> 4) * 1024 + (d >> 5) * 256 + (t & 15) * 16 + ((d & 31) >> 1);
         shift = 4 * (d & 1);
-        sb = kMx ? ((d >> 5) * 16 + (t & 15)) * 8 + (t >> 4)
-                 : ((((d >> 4) >> 1) * 16 + (t & 15)) * 8 + (t >> 4)) * 2 + ((d >> 4) & 1);
+        sb = kChan ? (t >> 4) * kD + d
+                   : (kMx ? ((d >> 5) * 16 + (t & 15)) * 8 + (t >> 4)
+                          : ((((d >> 4) >> 1) * 16 + (t & 15)) * 8 + (t >> 4)) * 2 + ((d >> 4) & 1));
       } else {
         const int g = (t >> 5) * 4 + ((t >> 3) & 3);
         if (kMx) {
@@ -326,7 +378,7 @@ __device__ __forceinline__ void page_error(const WriterArgs& a, int in_page, int
   }
 }
 
-template <bool kKMx, bool kVMx>
+template <bool kKMx, bool kVMx, bool kChan>
 __global__ void __launch_bounds__(256) page_error_kernel(WriterArgs a, double* part) {
   __shared__ __align__(16) uint8_t s_codes[8192];
   __shared__ __align__(16) uint8_t s_scales[1024];
@@ -338,8 +390,8 @@ __global__ void __launch_bounds__(256) page_error_kernel(WriterArgs a, double* p
   double err = 0.0, ref = 0.0;
   if (dst >= 0 && dst < a.num_pages) {
     const size_t blk = (size_t)dst * a.hkv + h;
-    if (is_v) page_error<kKMx, kVMx, true>(a, in_page, h, blk, s_codes, s_scales, err, ref);
-    else page_error<kKMx, kVMx, false>(a, in_page, h, blk, s_codes, s_scales, err, ref);
+    if (is_v) page_error<kKMx, kVMx, true, kChan>(a, in_page, h, blk, s_codes, s_scales, err, ref);
+    else page_error<kKMx, kVMx, false, kChan>(a, in_page, h, blk, s_codes, s_scales, err, ref);
   }
   s_e[threadIdx.x] = err;
   s_r[threadIdx.x] = ref;
@@ -399,6 +451,7 @@ static WriterArgs writer_args(const WriterLaunch& L) {
   a.n_pages = L.n_pages;
   a.rotation = L.rotation;
   a.rotate_v = L.rotate_v;
+  a.k_chan = L.k_chan;
   return a;
 }
 
@@ -406,12 +459,18 @@ hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
   if (L.n_pages == 0) return hipSuccess;
   const WriterArgs a = writer_args(L);
   const dim3 grid((unsigned)(L.n_pages * L.hkv), 2u), block(256u);
-  if (L.k_mode == 2 && L.v_mode == 1)
-    hipLaunchKernelGGL((writer_kernel<2, 1>), grid, block, 0, stream, a);
+  if (L.k_chan && L.k_mode == 2 && L.v_mode == 1)
+    hipLaunchKernelGGL((writer_kernel<2, 1, true>), grid, block, 0, stream, a);
+  else if (L.k_chan && L.k_mode == 1 && L.v_mode == 1)
+    hipLaunchKernelGGL((writer_kernel<1, 1, true>), grid, block, 0, stream, a);
+  else if (L.k_chan)
+    return hipErrorInvalidValue;
+  else if (L.k_mode == 2 && L.v_mode == 1)
+    hipLaunchKernelGGL((writer_kernel<2, 1, false>), grid, block, 0, stream, a);
   else if (L.k_mode == 1 && L.v_mode == 1)
-    hipLaunchKernelGGL((writer_kernel<1, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((writer_kernel<1, 1, false>), grid, block, 0, stream, a);
   else if (L.k_mode == 3 && L.v_mode == 3)
-    hipLaunchKernelGGL((writer_kernel<3, 3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((writer_kernel<3, 3, false>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -433,12 +492,19 @@ hipError_t launch_append(const AppendLaunch& L, hipStream_t stream) {
   a.sink_tokens = L.sink_tokens;
   const dim3 grid((unsigned)(L.batch * L.w.hkv), 2u), block(256u);
   const int km = L.w.k_mode, vm = L.w.v_mode;
-  if (km == 2 && vm == 1)
-    hipLaunchKernelGGL((append_kernel<2, 1>), grid, block, 0, stream, a);
+  const bool ch = L.w.k_chan != 0;
+  if (ch && km == 2 && vm == 1)
+    hipLaunchKernelGGL((append_kernel<2, 1, true>), grid, block, 0, stream, a);
+  else if (ch && km == 1 && vm == 1)
+    hipLaunchKernelGGL((append_kernel<1, 1, true>), grid, block, 0, stream, a);
+  else if (ch)
+    return hipErrorInvalidValue;
+  else if (km == 2 && vm == 1)
+    hipLaunchKernelGGL((append_kernel<2, 1, false>), grid, block, 0, stream, a);
   else if (km == 1 && vm == 1)
-    hipLaunchKernelGGL((append_kernel<1, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<1, 1, false>), grid, block, 0, stream, a);
   else if (km == 3 && vm == 3)
-    hipLaunchKernelGGL((append_kernel<3, 3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<3, 3, false>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -451,10 +517,14 @@ hipError_t launch_page_errors(const WriterLaunch& L, void* workspace, double* ou
   double* part = static_cast<double*>(workspace);
   const int n = L.n_pages * L.hkv;
   const dim3 grid((unsigned)n, 2u), block(256u);
-  if (L.k_mode == 3 && L.v_mode == 3)
-    hipLaunchKernelGGL((page_error_kernel<true, true>), grid, block, 0, stream, a, part);
+  if (L.k_chan && L.k_mode != 3 && L.v_mode != 3)
+    hipLaunchKernelGGL((page_error_kernel<false, false, true>), grid, block, 0, stream, a, part);
+  else if (L.k_chan)
+    return hipErrorInvalidValue;
+  else if (L.k_mode == 3 && L.v_mode == 3)
+    hipLaunchKernelGGL((page_error_kernel<true, true, false>), grid, block, 0, stream, a, part);
   else if (L.k_mode != 3 && L.v_mode != 3)
-    hipLaunchKernelGGL((page_error_kernel<false, false>), grid, block, 0, stream, a, part);
+    hipLaunchKernelGGL((page_error_kernel<false, false, false>), grid, block, 0, stream, a, part);
   else
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(page_error_total_kernel, dim3(2u), dim3(256u), 0, stream, part, n, out);

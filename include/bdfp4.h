@@ -94,7 +94,16 @@ typedef struct {
                             softmax) instead of the partition maximum, and
                             weights it back; NVFP4 K/V, two query terms and
                             AMAX2_OR_AMAX6 only (else E_UNSUPPORTED)          */
+  int32_t key_scale_geometry; /* BDFP4_KEY_GEOMETRY_LOCAL (default of both
+                            modes: a key block is 16 channels of one token)
+                            or BDFP4_KEY_GEOMETRY_CHANNEL (16 tokens of one
+                            channel, KV_MODES key_scale_geometry; quant_ab.py
+                            SCHEMES per-channel keys): NVFP4 keys (FOUR_SIX
+                            or AMAX6) and no p_running_max, else
+                            E_UNSUPPORTED                                     */
 } bdfp4_recipe;
+
+enum { BDFP4_KEY_GEOMETRY_LOCAL = 0, BDFP4_KEY_GEOMETRY_CHANNEL = 1 };
 
 /* The quantized paged cache. Each of the four arrays is dense
  * [num_pages][num_kv_heads][bytes per page-head]; the block of (page p, head h)
@@ -109,6 +118,8 @@ typedef struct {
  *     ((((t>>5)*4 + ((t>>3)&3))*16 + (d>>3))*8 + (t&7))*4 + ((d&7)>>1)
  *   K scales, NVFP4 (1024 B, j = d>>4): (((j>>1)*16 + (t&15))*8 + (t>>4))*2 + (j&1)
  *   K scales, MXFP4 (512 B, j = d>>5):  (j*16 + (t&15))*8 + (t>>4)
+ *   K scales, NVFP4, channel key geometry (1024 B, token block b = t>>4):
+ *     b*128 + d
  *   V scales, NVFP4 (1024 B): (((t>>5)*4 + ((t>>3)&3))*8 + j)*8 + (t&7)
  *   V scales, MXFP4 (512 B):  (((t>>5)*4 + ((t>>3)&3))*4 + j)*8 + (t&7)
  * All four pointers 16-byte aligned. */

@@ -46,6 +46,7 @@ def to_c(r: RC.Recipe) -> bd.Recipe:
     c.tau = float(r.tau)
     c.rotate_v = int(r.rotate_v)
     c.p_running_max = int(r.p_running_max)
+    c.key_scale_geometry = bd.KEY_GEOMETRY_CHANNEL if r.key_scale_geometry == RC.CHANNEL else bd.KEY_GEOMETRY_LOCAL
     return c
 
 

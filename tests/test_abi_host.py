@@ -85,6 +85,7 @@ def test_recipe_validation_follows_probability_environment():
     ("scale_mode_p", 7, bd.E_INVALID), ("scale_mode_p", bd.SCALE_NONE, bd.E_UNSUPPORTED),
     ("scale_mode_q", bd.SCALE_MXFP4_SEARCH, bd.E_UNSUPPORTED),
     ("scale_mode_v", bd.SCALE_MXFP4_SEARCH, bd.E_UNSUPPORTED),
+    ("key_scale_geometry", 2, bd.E_INVALID), ("key_scale_geometry", -1, bd.E_INVALID),
 ])
 def test_recipe_field_checks(field, value, status):
     r = bd.recipe_default_nvfp4(tau=1.0)
@@ -318,3 +319,18 @@ def test_noalloc_decode_rejects_before_launch():
     assert call(bd.recipe_default_nvfp4(), 1, 1, 16, 2048, 4) == bd.E_UNCALIBRATED
     assert call(r, 1, 1, 16, 2048, 4, q=None) == bd.E_INVALID
     assert call(r, 1, 1, 16, 2048, 40) == bd.E_INVALID
+
+
+def test_channel_key_geometry_support():
+    nv = bd.recipe_default_nvfp4(tau=1.0)
+    assert nv.key_scale_geometry == bd.KEY_GEOMETRY_LOCAL
+    assert bd.recipe_default_mxfp4(tau=1.0).key_scale_geometry == bd.KEY_GEOMETRY_LOCAL
+    bd.recipe_validate(nv.replace(key_scale_geometry=bd.KEY_GEOMETRY_CHANNEL))
+    bd.recipe_validate(nv.replace(key_scale_geometry=bd.KEY_GEOMETRY_CHANNEL, scale_mode_k=bd.SCALE_AMAX6))
+    for r in (bd.recipe_default_mxfp4(tau=1.0).replace(key_scale_geometry=bd.KEY_GEOMETRY_CHANNEL),
+              nv.replace(key_scale_geometry=bd.KEY_GEOMETRY_CHANNEL, p_running_max=1)):
+        with pytest.raises(bd.Bdfp4Error) as ei:
+            bd.recipe_validate(r)
+        assert ei.value.status == bd.E_UNSUPPORTED
+    # the cache sizes do not depend on the key geometry
+    assert bd.cache_bytes(nv.replace(key_scale_geometry=bd.KEY_GEOMETRY_CHANNEL), 3, 2) == bd.cache_bytes(nv, 3, 2)

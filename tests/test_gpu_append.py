@@ -25,6 +25,7 @@ RECIPES = {
     "nvfp4_plain": RC.nvfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
     "mxfp4": RC.mxfp4_default().with_(tau=1.0),
     "nvfp4_rotv": RC.nvfp4_default().with_(tau=1.0, rotate_v=True),
+    "nvfp4_chan": RC.nvfp4_default().with_(tau=1.0, key_scale_geometry=RC.CHANNEL),
 }
 
 

@@ -10,7 +10,9 @@ benchmark's launch configuration (two KV heads sampled), each for NVFP4 and MXFP
 page per partition (the final merge over several batches of partials), 16 sequences of
 2K..16K tokens (two sampled), determinism, paging
 invariance, invalid inputs (NaN rows), the end-to-end writer + decode path,
-16 seeded random shapes and recipes, and the BF16-KV baseline arm."""
+16 seeded random shapes and recipes, the channel key scale geometry (recipe
+variants, ragged batches at 1, 2 and 3 pages per partition, the 32K layer,
+6 seeded random shapes through the HIP writer) and the BF16-KV baseline arm."""
 import numpy as np
 import pytest
 import torch
@@ -50,13 +52,18 @@ def test_tiny_2k_mxfp4():
 
 
 @pytest.mark.parametrize("variant", ["terms1", "c1", "tau0", "p_amax6", "k_amax6", "norot", "nosmooth", "rotv",
-                                     "rotv_mx", "runmax", "runmax_tau0"])
+                                     "rotv_mx", "runmax", "runmax_tau0", "kchan", "kchan_amax6", "kchan_terms1",
+                                     "kchan_p_amax6"])
 def test_recipe_variants(variant):
     r = {"terms1": NV.with_(query_terms=1), "c1": NV.with_(c=1), "tau0": NV.with_(tau=0.0),
          "p_amax6": NV.with_(scale_mode_p=Q.AMAX6), "k_amax6": NV.with_(scale_mode_k=Q.AMAX6),
          "norot": NV.with_(rotation=False), "nosmooth": NV.with_(key_smoothing=False),
          "rotv": NV.with_(rotate_v=True), "rotv_mx": MX.with_(rotate_v=True),
-         "runmax": NV.with_(p_running_max=True), "runmax_tau0": NV.with_(p_running_max=True, tau=0.0)}[variant]
+         "runmax": NV.with_(p_running_max=True), "runmax_tau0": NV.with_(p_running_max=True, tau=0.0),
+         "kchan": NV.with_(key_scale_geometry=RC.CHANNEL),
+         "kchan_amax6": NV.with_(key_scale_geometry=RC.CHANNEL, scale_mode_k=Q.AMAX6),
+         "kchan_terms1": NV.with_(key_scale_geometry=RC.CHANNEL, query_terms=1),
+         "kchan_p_amax6": NV.with_(key_scale_geometry=RC.CHANNEL, scale_mode_p=Q.AMAX6)}[variant]
     wl = synth.decode_workload("v", 3, [1500, 777], 8, 2, "qwen", extra_pages=1)
     _run(r, wl, 2, variant)
 
@@ -106,12 +113,39 @@ def test_random_shapes(seed):
     assert_close(got, ref, what)
 
 
+@pytest.mark.parametrize("ppp", [1, 2, 3])
+def test_ragged_batch_channel_geometry(ppp):
+    # the channel key scale geometry over ragged lengths, every page-slot count
+    wl = synth.decode_workload("r", 8, [1, 100, 300, 2049, 640], 8, 2, "qwen", extra_pages=2)
+    _run(NV.with_(key_scale_geometry=RC.CHANNEL), wl, ppp, f"ragged channel geometry ppp={ppp}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_channel_geometry(seed):
+    rng = np.random.default_rng(3000 + seed)
+    batch = int(rng.integers(1, 4))
+    hkv = int(rng.choice([1, 2]))
+    sink = int(rng.choice([0, 16, 112]))
+    lens = [int(x) for x in rng.integers(1, 2600, size=batch)]
+    ppp = int(rng.integers(1, 5))
+    r = NV.with_(key_scale_geometry=RC.CHANNEL, sink_tokens=sink, query_terms=int(rng.choice([1, 2])),
+                 scale_mode_k=str(rng.choice([Q.FOUR_SIX, Q.AMAX6])), tau=float(rng.choice([0.0, 1.0, 4.0])))
+    wl = synth.decode_workload("randc", 4000 + seed, lens, 4 * hkv, hkv, "qwen", sink_tokens=sink)
+    what = f"random channel geometry seed={seed}: B={batch} L={lens} hkv={hkv} sink={sink} ppp={ppp}"
+    print(f"[decode] {what}", flush=True)
+    host = oracle_write(r, wl)
+    ref = oracle_decode(r, wl, host, ppp)
+    got = gpu_decode(r, wl, gpu_write(r, wl), ppp)
+    assert_close(got, ref, what)
+
+
 def test_ragged_batch_mxfp4():
     wl = synth.decode_workload("r", 5, [129, 1000, 4096 + 77], 12, 3, "qwen", extra_pages=2)
     _run(MX, wl, 3, "ragged mxfp4")
 
 
-@pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("r", [NV, MX, NV.with_(key_scale_geometry=RC.CHANNEL)],
+                         ids=["nvfp4", "mxfp4", "nvfp4_channel_geometry"])
 def test_qwen_32k_layer(r):
     """32 query / 8 KV heads, 256 full pages + 77-token tail, permuted pool."""
     wl = synth.qwen_32k(0)

@@ -1,6 +1,7 @@
 """GPU page writer parity through the C ABI: codes and scales of every
 written page bit-exact with the oracle (NVFP4 four_six / amax6, MXFP4, with
-and without rotation and centering), untouched pages left alone, invalid
+and without rotation and centering, the channel key scale geometry),
+untouched pages left alone, invalid
 destination pages skipped; at the full 131,072-token x 8-head prefill size,
 sampled page-heads checked one by one."""
 import numpy as np
@@ -26,6 +27,10 @@ RECIPES = {
     "mxfp4_plain": RC.mxfp4_default().with_(tau=1.0, rotation=False, key_smoothing=False),
     "nvfp4_rotv": RC.nvfp4_default().with_(tau=1.0, rotate_v=True),
     "mxfp4_rotv": RC.mxfp4_default().with_(tau=1.0, rotate_v=True),
+    "nvfp4_chan": RC.nvfp4_default().with_(tau=1.0, key_scale_geometry=RC.CHANNEL),
+    "nvfp4_chan_amax6": RC.nvfp4_default().with_(tau=1.0, key_scale_geometry=RC.CHANNEL, scale_mode_k=Q.AMAX6),
+    "nvfp4_chan_plain": RC.nvfp4_default().with_(tau=1.0, key_scale_geometry=RC.CHANNEL, rotation=False,
+                                                 key_smoothing=False),
 }
 
 
@@ -45,7 +50,7 @@ def test_writer_tiny_bit_exact(name):
     _compare(cache_to_host(gpu_write(r, wl)), oracle_write(r, wl))
 
 
-@pytest.mark.parametrize("name", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("name", ["nvfp4", "mxfp4", "nvfp4_chan"])
 def test_writer_multihead_permuted_bit_exact(name):
     r = RECIPES[name]
     wl = synth.decode_workload("w", 7, [128 * 11 + 5, 128 * 3], 32, 8, "qwen", extra_pages=3)
@@ -77,7 +82,7 @@ def test_writer_skips_invalid_page_ids():
     _compare(got, want)
 
 
-@pytest.mark.parametrize("name", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("name", ["nvfp4", "mxfp4", "nvfp4_chan"])
 def test_writer_full_prefill_sampled(name):
     """131,072 tokens x 8 KV heads in one launch; 24 sampled page-heads
     recomputed by the oracle one by one."""
