@@ -6,8 +6,8 @@ rotation, key smoothing, K four_six, two query terms, P amax2_or_amax6 with
 c and tau) and "kv-landlords scripts/quant_ab.py" compares cache schemes by
 reconstruction error; this driver measures each part's effect by switching
 it off alone, plus a plain NVFP4 cache (amax6 everywhere, no rotation or
-centering, one query term, tau = 0), the rotated-values variant and the MXFP4
-recipe. For every recipe:
+centering, one query term, tau = 0), the rotated-values variant, the channel
+key scale geometry and the MXFP4 recipe. For every recipe:
 
 * bdfp4_quantize_pages writes the layer's full pages;
 * bdfp4_page_errors gives the relative K error (centered, rotated domain)
@@ -16,7 +16,10 @@ recipe. For every recipe:
   attention over the same BF16 tokens) through bdfp4_error_sums gives the
   relative L2 output error.
 
-Inputs are the seeded synthetic decode layer (one sequence, Qwen3-4B shapes).
+Inputs are the seeded synthetic decode layer (one sequence, Qwen3-4B shapes),
+with the decode workload's mild key outliers or, with --keys write, the
+prefill write's large ones (+-10 on 8 channels per KV head), which the
+rotation and the centering exist for.
 `python -m fp4_kv_cache_nvfp4_amd.diagnostics [--context L]` prints JSON.
 """
 from __future__ import annotations
@@ -25,7 +28,7 @@ import argparse
 import json
 import math
 
-from . import (SCALE_AMAX6, alloc_workspace, bf16_decode_attention, decode_attention,
+from . import (KEY_GEOMETRY_CHANNEL, SCALE_AMAX6, alloc_workspace, bf16_decode_attention, decode_attention,
                decode_workspace_size, error_sums, page_errors, quantize_pages, recipe_default_mxfp4,
                recipe_default_nvfp4, PagedCache)
 from . import synth
@@ -39,6 +42,7 @@ ABLATIONS = {
     "c_1": {"c": 1},
     "p_amax6_tau_0": {"tau": 0.0},
     "rotate_v": {"rotate_v": 1},
+    "key_channel_geometry": {"key_scale_geometry": KEY_GEOMETRY_CHANNEL},
     "plain_nvfp4": {"scale_mode_k": SCALE_AMAX6, "rotation": 0, "key_smoothing": 0, "query_terms": 1,
                     "tau": 0.0},
     "bitdecoding-mxfp4": None,
@@ -52,10 +56,13 @@ def recipes(tau: float = 1.0) -> dict:
     return out
 
 
-def ablation_report(context: int = 32768, layer: int = 0, tau: float = 1.0, pages_per_partition: int = 0) -> dict:
+def ablation_report(context: int = 32768, layer: int = 0, tau: float = 1.0, pages_per_partition: int = 0,
+                    keys: str = "qwen") -> dict:
+    """keys: "qwen" (the decode layer's Student-t(3) offsets on 6 channels
+    per KV head) or "write" (the prefill write's +-10 offsets on 8)."""
     import torch
 
-    d = synth.torch_decode_layer(layer, seq_len=context)
+    d = synth.torch_decode_layer(layer, seq_len=context, outliers=keys)
     hq, hkv, L = d["num_q_heads"], d["num_kv_heads"], d["seq_len"]
     kp = synth.bf16_pages_from_tokens(d["k"], d["block_tables"], d["num_pages"])
     vp = synth.bf16_pages_from_tokens(d["v"], d["block_tables"], d["num_pages"])
@@ -80,7 +87,7 @@ def ablation_report(context: int = 32768, layer: int = 0, tau: float = 1.0, page
         report[name] = {"k_rel": math.sqrt(pe[0] / pe[1]), "v_rel": math.sqrt(pe[2] / pe[3]),
                         "out_rel_l2": math.sqrt(e / rr)}
         del cache
-    return {"context": L, "layer": layer, "tau": tau, "pages_per_partition": ppp, "recipes": report}
+    return {"context": L, "layer": layer, "tau": tau, "keys": keys, "pages_per_partition": ppp, "recipes": report}
 
 
 def main():
@@ -88,8 +95,10 @@ def main():
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--layer", type=int, default=0)
     ap.add_argument("--tau", type=float, default=1.0)
+    ap.add_argument("--keys", choices=["qwen", "write"], default="qwen",
+                    help="key outliers: the decode layer's Student-t(3) offsets or the prefill write's +-10")
     a = ap.parse_args()
-    print(json.dumps(ablation_report(a.context, a.layer, a.tau)))
+    print(json.dumps(ablation_report(a.context, a.layer, a.tau, keys=a.keys)))
 
 
 if __name__ == "__main__":

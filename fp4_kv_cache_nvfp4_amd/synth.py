@@ -241,22 +241,30 @@ def write_workload(seed: int = 0, tokens: int = 131072, num_kv_heads: int = 8,
 
 
 def torch_decode_layer(layer: int, seq_len: int = 131072, num_q_heads: int = 32, num_kv_heads: int = 8,
-                       sink_tokens: int = 16, device="cuda"):
+                       sink_tokens: int = 16, device="cuda", outliers: str = "qwen"):
     """One layer of the long-context decode drawn on the device with torch's
     generator (seed = layer): same recipe as ``decode_workload(..., "qwen")``
     (K, V, Q ~ N(0,1) in bf16; Student-t(3) offsets, formed as Z / sqrt(chi2_3 / 3),
     on 6 seeded key channels per KV head; mu = float32(mean of K in float64);
-    one sequence; random permutation of a pool of ceil(L/128) pages).
+    one sequence; random permutation of a pool of ceil(L/128) pages). With
+    outliers="write" the keys take the prefill write's outliers instead:
+    +-10 (seeded signs) on 8 seeded channels per KV head.
     Returns a dict of device tensors."""
     import torch
 
     g = torch.Generator(device=device)
     g.manual_seed(1_000_000 + layer)
     hkv = num_kv_heads
-    ch = torch.stack([torch.randperm(D, generator=g, device=device)[:6] for _ in range(hkv)])
-    z = torch.randn((hkv, 6), generator=g, device=device)
-    chi = (torch.randn((hkv, 6, 3), generator=g, device=device) ** 2).sum(-1)
-    off = z / torch.sqrt(chi / 3.0)
+    if outliers == "write":
+        ch = torch.stack([torch.randperm(D, generator=g, device=device)[:8] for _ in range(hkv)])
+        off = 10.0 * torch.where(torch.rand((hkv, 8), generator=g, device=device) < 0.5, -1.0, 1.0)
+    elif outliers == "qwen":
+        ch = torch.stack([torch.randperm(D, generator=g, device=device)[:6] for _ in range(hkv)])
+        z = torch.randn((hkv, 6), generator=g, device=device)
+        chi = (torch.randn((hkv, 6, 3), generator=g, device=device) ** 2).sum(-1)
+        off = z / torch.sqrt(chi / 3.0)
+    else:
+        raise ValueError(f"unknown key outlier recipe {outliers!r}")
     k = torch.randn((seq_len, hkv, D), generator=g, device=device)
     kf = k.view(seq_len, hkv, D)
     for h in range(hkv):

@@ -76,16 +76,18 @@ def _from_c(rc) -> RC.Recipe:
                      scale_mode_k=mode[rc.scale_mode_k], scale_mode_v=mode[rc.scale_mode_v],
                      scale_mode_q=mode[rc.scale_mode_q], scale_mode_p=mode[rc.scale_mode_p],
                      query_terms=rc.query_terms, c=rc.c, tau=float(rc.tau), rotate_v=bool(rc.rotate_v),
-                     p_running_max=bool(rc.p_running_max))
+                     p_running_max=bool(rc.p_running_max),
+                     key_scale_geometry=RC.CHANNEL if rc.key_scale_geometry == bd.KEY_GEOMETRY_CHANNEL else RC.LOCAL)
 
 
-def test_ablation_report_matches_oracle():
+@pytest.mark.parametrize("keys", ["qwen", "write"])
+def test_ablation_report_matches_oracle(keys):
     from fp4_kv_cache_nvfp4_amd import diagnostics as D
     from oracle import decode as OD
 
     L, layer = 1024 + 77, 3
-    rep = D.ablation_report(context=L, layer=layer)
-    d = synth.torch_decode_layer(layer, seq_len=L)               # the same seeded inputs
+    rep = D.ablation_report(context=L, layer=layer, keys=keys)
+    d = synth.torch_decode_layer(layer, seq_len=L, outliers=keys)   # the same seeded inputs
     k, v, q = _u16(d["k"]), _u16(d["v"]), _u16(d["q"])
     bt, sl = d["block_tables"].cpu().numpy(), d["seq_lens"].cpu().numpy()
     ids, n_full, mu = d["page_ids"].cpu().numpy(), d["n_full"], d["key_shift"].cpu().numpy()
@@ -103,7 +105,7 @@ def test_ablation_report_matches_oracle():
         want = {"k_rel": np.sqrt(pe[0] / pe[1]), "v_rel": np.sqrt(pe[2] / pe[3]),
                 "out_rel_l2": np.linalg.norm(out - ref) / np.linalg.norm(ref)}
         got = rep["recipes"][name]
-        print(f"[ablation] {name}: {got}", flush=True)
+        print(f"[ablation] keys={keys} {name}: {got}", flush=True)
         assert abs(got["k_rel"] - want["k_rel"]) <= 1e-9 * want["k_rel"], name
         assert abs(got["v_rel"] - want["v_rel"]) <= 1e-9 * want["v_rel"], name
         assert abs(got["out_rel_l2"] - want["out_rel_l2"]) <= 1e-3 * want["out_rel_l2"], name
