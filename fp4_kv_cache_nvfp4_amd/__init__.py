@@ -102,9 +102,12 @@ def lib() -> ctypes.CDLL:
         "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
         "bdfp4_decode_attention_noalloc": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, P],
+        "bdfp4_decode_attention_logits": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P,
+                                          P],
         "bdfp4_bf16_decode_attention": [P, I32, I32, I32, P, P, I32, P, I32, P, I32, F32, I32, P, SZ, P, P],
         "bdfp4_quantize_rows": [P, I32, P, I32, I32, I32, P, P, P],
         "bdfp4_quantize_p_blocks": [P, I32, I32, F32, P, P, P],
+        "bdfp4_decode_query_codes": [RP, P, I32, I32, I32, P, P, P],
         "bdfp4_stream_read": [P, SZ, P, SZ, I32, P],
     }
     for name, args in sig.items():
@@ -347,6 +350,20 @@ def decode_attention_noalloc(r: Recipe, cache: PagedCache, q, block_tables, seq_
         _ptr(key_shift), float(softmax_scale), int(pages_per_partition), _ptr(out), _stream(stream)))
 
 
+def decode_attention_logits(r: Recipe, cache: PagedCache, q, block_tables, seq_lens, max_seq_len: int,
+                            sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale: float,
+                            pages_per_partition: int, workspace, out, logits, stream=None) -> None:
+    """bdfp4_decode_attention_logits (debug): the decode, plus its raw FP4-token
+    logits in `logits` (float32 [B, Hkv, 4, 128 * max_pages_per_seq])."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    c = cache.struct()
+    _check(lib().bdfp4_decode_attention_logits(
+        ctypes.byref(r), ctypes.byref(c), _ptr(q), B, Hq, _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(seq_lens), int(max_seq_len), _ptr(sink_k), _ptr(sink_v), _ptr(tail_k), _ptr(tail_v),
+        _ptr(key_shift), float(softmax_scale), int(pages_per_partition), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(logits), _stream(stream)))
+
+
 def decode_noalloc_max_workspace() -> int:
     return int(lib().bdfp4_decode_noalloc_max_workspace())
 
@@ -366,6 +383,12 @@ def bf16_decode_attention(q, k_pages, v_pages, block_tables, seq_lens, max_seq_l
 def quantize_rows(rows, shift, rotation: int, mode: int, terms: int, codes, scales, stream=None) -> None:
     _check(lib().bdfp4_quantize_rows(_ptr(rows), int(rows.shape[0]) if rows is not None else 0, _ptr(shift),
                                      rotation, mode, terms, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def decode_query_codes(r: Recipe, q, num_kv_heads: int, codes, scales, stream=None) -> None:
+    """bdfp4_decode_query_codes: the decode prologue's query codes and scales."""
+    _check(lib().bdfp4_decode_query_codes(ctypes.byref(r), _ptr(q), int(q.shape[0]), int(q.shape[1]),
+                                          int(num_kv_heads), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def quantize_p_blocks(pp, mode: int, tau: float, codes, scales, stream=None) -> None:

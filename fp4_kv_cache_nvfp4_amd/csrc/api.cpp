@@ -479,7 +479,7 @@ static bdfp4_status decode_impl(const bdfp4_recipe* r, const bdfp4_cache* cache,
                                 const void* sink_k, const void* sink_v, const void* tail_k, const void* tail_v,
                                 const float* key_shift, float softmax_scale, int32_t pages_per_partition,
                                 void* workspace, size_t workspace_bytes_in, float* out, void* stream,
-                                bool noalloc) {
+                                bool noalloc, float* logits = nullptr) {
   if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
   bdfp4_status s = check_recipe(r);
   if (s != BDFP4_OK) return s;
@@ -555,6 +555,8 @@ static bdfp4_status decode_impl(const bdfp4_recipe* r, const bdfp4_cache* cache,
   L.counter_stride = bdfp4::kTicketStride;
   L.slot_stride = bdfp4::workspace_slot_stride(workspace_parts(max_seq_len, ppp));
   L.out = out;
+  L.dbg_logits = logits;
+  L.dbg_stride = 128 * max_pages_per_seq;
   return hip_status(bdfp4::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
@@ -583,6 +585,20 @@ bdfp4_status bdfp4_decode_attention_noalloc(const bdfp4_recipe* r, const bdfp4_c
 }
 
 size_t bdfp4_decode_noalloc_max_workspace(void) { return bdfp4::kNoAllocScratchBytes; }
+
+bdfp4_status bdfp4_decode_attention_logits(const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+                                           int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                           const void* sink_k, const void* sink_v, const void* tail_k,
+                                           const void* tail_v, const float* key_shift, float softmax_scale,
+                                           int32_t pages_per_partition, void* workspace, size_t workspace_bytes_in,
+                                           float* out, float* logits, void* stream) {
+  if (logits == nullptr) return fail(BDFP4_E_INVALID, "logits is NULL");
+  if (((uintptr_t)logits & 3) != 0) return fail(BDFP4_E_INVALID, "logits must be 4-byte aligned");
+  return decode_impl(r, cache, q_bf16, batch, num_q_heads, block_tables, max_pages_per_seq, seq_lens, max_seq_len,
+                     sink_k, sink_v, tail_k, tail_v, key_shift, softmax_scale, pages_per_partition, workspace,
+                     workspace_bytes_in, out, stream, false, logits);
+}
 
 bdfp4_status bdfp4_bf16_decode_attention(const void* q_bf16, int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, const void* k_pages, const void* v_pages,
@@ -642,6 +658,30 @@ bdfp4_status bdfp4_quantize_rows(const void* rows_bf16, int32_t n_rows, const fl
   return hip_status(bdfp4::launch_rows(rows_bf16, n_rows, shift, rotation, m, terms, codes, scales,
                                        static_cast<hipStream_t>(stream)),
                     "row quantizer launch");
+}
+
+bdfp4_status bdfp4_decode_query_codes(const bdfp4_recipe* r, const void* q_bf16, int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (r == nullptr) return fail(BDFP4_E_INVALID, "recipe is NULL");
+  bdfp4_status s = check_recipe(r);
+  if (s != BDFP4_OK) return s;
+  if (batch < 1 || num_kv_heads < 1 || (int64_t)batch * num_kv_heads > 0x7FFFFFFF)
+    return fail(BDFP4_E_INVALID, "batch and num_kv_heads must be positive");
+  if (num_q_heads != bdfp4::kGroup * num_kv_heads)
+    return fail(BDFP4_E_UNSUPPORTED, "num_q_heads must be 4 * num_kv_heads (got %d, %d)", num_q_heads, num_kv_heads);
+  if (!q_bf16 || !codes || !scales) return fail(BDFP4_E_INVALID, "NULL pointer");
+  if (!aligned16(q_bf16)) return fail(BDFP4_E_INVALID, "q must be 16-byte aligned");
+  bdfp4::DecodeLaunch L;
+  memset(&L, 0, sizeof L);
+  L.rotation = r->rotation;
+  L.mx = is_mx_kv(r) ? 1 : 0;
+  L.terms = r->query_terms;
+  L.q = static_cast<const uint16_t*>(q_bf16);
+  L.batch = batch;
+  L.hq = num_q_heads;
+  L.hkv = num_kv_heads;
+  return hip_status(bdfp4::launch_query_codes(L, codes, scales, static_cast<hipStream_t>(stream)),
+                    "query codes launch");
 }
 
 bdfp4_status bdfp4_quantize_p_blocks(const float* pp, int32_t n_blocks, int32_t mode, float tau, uint8_t* codes,

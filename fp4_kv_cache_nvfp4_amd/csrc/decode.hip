@@ -384,10 +384,13 @@ constexpr int kSwzXor16 = 0x401F;
 // in-lane, stages 2 .. 64 across lanes), then Q1 and the residual Q2,
 // dequantized into LDS as 16-bit MFMA operands. The quantizer is the one of
 // the page writer and the row quantizer (quant_block), so the codes are the
-// same functions of the rotated values.
-template <bool kMx, int kTerms>
+// same functions of the rotated values. With exp_codes / exp_scales (the
+// debug entry bdfp4_decode_query_codes, never the decode itself) the codes
+// and scale codes of each term are also written out: codes [term][64] (byte
+// i = elements 2i, 2i + 1), scales [term][nb].
+template <bool kMx, int kTerms, bool kExport = false>
 __device__ __forceinline__ void query_prologue(const DecodeLaunch& P, uint32_t qw, float2 mu, Smem& sm, int g,
-                                               int i) {
+                                               int i, uint8_t* exp_codes = nullptr, uint8_t* exp_scales = nullptr) {
   float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
   float dot = __builtin_fmaf(x1, mu.y, __fmul_rn(x0, mu.x));
   dot = sum16(dot);
@@ -441,11 +444,20 @@ __device__ __forceinline__ void query_prologue(const DecodeLaunch& P, uint32_t q
       // are zero whatever its scale) are the scaled FP4 MFMA's A operand
       sm.qcode[term][g][i] = (uint8_t)pk;
       if ((i & 15) == 0) sm.qsc[term][g][i >> 4] = (uint32_t)((take_lo ? elo : ehi) + 127);
+      if (kExport) {
+        exp_codes[term * 64 + i] = (uint8_t)pk;
+        if ((i & 15) == 0) exp_scales[term * 4 + (i >> 4)] = (uint8_t)((take_lo ? elo : ehi) + 127);
+      }
     } else {
       // 16-element block = 8 lanes
       a = max8(a);
-      s = e4m3_value(e4m3_encode(div6(a)));
+      const uint32_t sc = e4m3_encode(div6(a));
+      s = e4m3_value(sc);
       quant_block<2, false>(xx, s, &pk);
+      if (kExport) {
+        exp_codes[term * 64 + i] = (uint8_t)pk;
+        if ((i & 7) == 0) exp_scales[term * 8 + (i >> 3)] = (uint8_t)sc;
+      }
     }
     float deq[2];
 #pragma unroll
@@ -741,6 +753,13 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     if (npg > 3) k_page(kb1, 3);
     load_v<kMx>(vb1, P, blk_of(1), lane);
   }
+  // debug export of the raw logits q . mu + q_hat . k_hat of this partition
+  // (bdfp4_decode_attention_logits; null in every other call)
+  if (P.dbg_logits != nullptr) {
+    float* dst = P.dbg_logits + (size_t)(b * P.hkv + h) * kGroup * P.dbg_stride + (size_t)p0 * kPage;
+    for (int g = 0; g < kGroup; ++g)
+      for (int j = lane; j < npg * kPage; j += 64) dst[(size_t)g * P.dbg_stride + j] = lgw[g * kWaveTok + j];
+  }
   // the partition maximum of each head (rows of 16 lanes hold heads 2 hp, 2 hp + 1)
   ma = max16(ma);
   mb = max16(mb);
@@ -991,6 +1010,36 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
     merge_out(C, b, h, nwg, P.rotate_v != 0);
     reset_ticket(ticket);
   }
+}
+
+// ------------------------------------------------------------ debug: the decode's query codes
+
+// Workgroup (sequence, KV head), wave g = query head g of the group: the
+// decode's own query prologue on each query row, its codes and scale codes
+// written out ([row][term][64] and [row][term][nb], row = b * hq + query head).
+template <bool kMx, int kTerms>
+__global__ void __launch_bounds__(256) query_codes_kernel(DecodeLaunch P, uint8_t* codes, uint8_t* scales) {
+  __shared__ __align__(16) Smem sm;
+  const int bh = blockIdx.x, b = bh / P.hkv, h = bh - b * P.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row = (size_t)b * P.hq + h * kGroup + wave;
+  const uint32_t qw = reinterpret_cast<const uint32_t*>(P.q + row * kD)[lane];
+  const float2 mu = make_float2(0.0f, 0.0f);
+  constexpr int nb = kMx ? 4 : 8;
+  query_prologue<kMx, kTerms, true>(P, qw, mu, sm, wave, lane, codes + row * kTerms * 64,
+                                    scales + row * kTerms * nb);
+}
+
+hipError_t launch_query_codes(const DecodeLaunch& L, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const dim3 grid((unsigned)(L.batch * L.hkv)), block(256u);
+  if (L.mx) {
+    if (L.terms == 2) hipLaunchKernelGGL((query_codes_kernel<true, 2>), grid, block, 0, stream, L, codes, scales);
+    else hipLaunchKernelGGL((query_codes_kernel<true, 1>), grid, block, 0, stream, L, codes, scales);
+  } else {
+    if (L.terms == 2) hipLaunchKernelGGL((query_codes_kernel<false, 2>), grid, block, 0, stream, L, codes, scales);
+    else hipLaunchKernelGGL((query_codes_kernel<false, 1>), grid, block, 0, stream, L, codes, scales);
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ allocation-free entry

@@ -86,9 +86,16 @@ struct DecodeLaunch {
   float* partials;        // workspace partials
   int32_t counter_stride, slot_stride;
   float* out;
+  float* dbg_logits;      // debug: raw FP4-token logits [batch * hkv][4][dbg_stride], or null
+  int32_t dbg_stride;
 };
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+
+// The decode's query prologue alone (debug): codes [batch * hq][terms][64],
+// scales [batch * hq][terms][nb] of each query row (L.q, L.batch, L.hq, L.hkv,
+// L.mx, L.terms, L.rotation used).
+hipError_t launch_query_codes(const DecodeLaunch& L, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 struct Bf16DecodeLaunch {
   const uint16_t* q;

@@ -337,6 +337,22 @@ bdfp4_status bdfp4_decode_attention_noalloc(
 /* Size in bytes of the allocation-free decode's workspace array. */
 size_t bdfp4_decode_noalloc_max_workspace(void);
 
+/* Debug entry: bdfp4_decode_attention that also writes the raw logit
+ * q . mu + q_hat . k_hat (float32, before sigma) of every FP4 token, as the
+ * decode computes it before the partition maximum and P quantization:
+ *   logits: float32 [batch][num_kv_heads][4][128 * max_pages_per_seq], token
+ *           at its logical position; the sink slots of page 0 hold -inf;
+ *           BF16 tokens and positions past the full pages are not written.
+ * Used to count how often float32 logits change a P code or scale. */
+bdfp4_status bdfp4_decode_attention_logits(
+    const bdfp4_recipe* r, const bdfp4_cache* cache, const void* q_bf16,
+    int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+    int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+    const void* sink_k, const void* sink_v, const void* tail_k,
+    const void* tail_v, const float* key_shift, float softmax_scale,
+    int32_t pages_per_partition, void* workspace, size_t workspace_bytes,
+    float* out, float* logits, void* stream);
+
 /* BF16-KV paged decode (the unquantized baseline arm, kv_cache_dtype "auto"
  * in KV_MODES): exact softmax attention over all L tokens of BF16 pages
  * k_pages / v_pages [num_pages][num_kv_heads][128][128], same split plan and
@@ -360,6 +376,20 @@ bdfp4_status bdfp4_quantize_rows(const void* rows_bf16, int32_t n_rows,
                                  const float* shift, int32_t rotation,
                                  int32_t mode, int32_t terms, uint8_t* codes,
                                  uint8_t* scales, void* stream);
+
+/* Debug entry: the query quantization exactly as bdfp4_decode_attention
+ * performs it (the decode's own prologue: 128-point rotation when the recipe
+ * has it, then Q1 and, with two terms, Q2 of the residual; amax6 per 16 for
+ * NVFP4 pages, mxfp4_search per 32 for MXFP4 pages), for every query row.
+ *   q_bf16: [batch][num_q_heads][128]; num_q_heads = 4 * num_kv_heads.
+ *   codes:  uint8 [batch * num_q_heads][query_terms][64], element 2i in
+ *           bits 3..0 of byte i; scales: uint8 [batch * num_q_heads]
+ *           [query_terms][nb], nb = 8 (E4M3) or 4 (E8M0).
+ * The recipe is validated as for the decode (tau included). */
+bdfp4_status bdfp4_decode_query_codes(const bdfp4_recipe* r, const void* q_bf16,
+                                      int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, uint8_t* codes,
+                                      uint8_t* scales, void* stream);
 
 /* Debug/codec entry: the probability quantizer on n_blocks blocks of 16
  * non-negative float32 values p' (already multiplied by c).

@@ -1,7 +1,8 @@
 """GPU codec parity through the C ABI: the row quantizer (key / query path:
 shift, rotation, amax6 / four_six / mxfp4_search, two residual terms) and the
-probability quantizer (amax2_or_amax6 with tau, amax6) against the oracle,
-bit for bit, including ties, zero blocks, subnormal and saturating scales."""
+probability quantizer (amax2_or_amax6 with tau, amax6) and the decode's own
+query prologue (bdfp4_decode_query_codes) against the oracle, bit for bit,
+including ties, zero blocks, subnormal and saturating scales."""
 import numpy as np
 import pytest
 import torch
@@ -130,3 +131,32 @@ def test_stream_read_folds_every_word_once(nwords, wgs):
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     assert got == want
+
+
+@pytest.mark.parametrize("recipe", ["nvfp4", "nvfp4_terms1", "nvfp4_norot", "mxfp4", "mxfp4_terms1", "mxfp4_norot"])
+def test_decode_query_codes_bit_exact(recipe):
+    """The decode's own query prologue (bdfp4_decode_query_codes runs the same
+    device function the decode runs, two elements per lane with cross-lane
+    rotation stages) against the oracle's query quantizer, bit for bit."""
+    from oracle import recipe as RC
+    r = {"nvfp4": RC.nvfp4_default(), "nvfp4_terms1": RC.nvfp4_default().with_(query_terms=1),
+         "nvfp4_norot": RC.nvfp4_default().with_(rotation=False), "mxfp4": RC.mxfp4_default(),
+         "mxfp4_terms1": RC.mxfp4_default().with_(query_terms=1),
+         "mxfp4_norot": RC.mxfp4_default().with_(rotation=False)}[recipe].with_(tau=1.0)
+    from gpu_helpers import to_c
+    hkv, B = 8, 129                            # 129 x 32 query rows of every kind (the row mix above)
+    u = _rows(17, B * 4 * hkv).reshape(B, 4 * hkv, 128)
+    mode = r.scale_mode_q
+    nb = 4 if mode == Q.MXFP4_SEARCH else 8
+    T = r.query_terms
+    codes = torch.zeros((B * 4 * hkv, T, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((B * 4 * hkv, T, nb), dtype=torch.uint8, device="cuda")
+    bd.decode_query_codes(to_c(r), dev_bf16(u), hkv, codes, scales)
+    torch.cuda.synchronize()
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    y = W.key_rows(F.bf16_to_f32(u.reshape(-1, 128)), None, r.rotation)     # the query is rotated, not centered
+    want, _ = Q.quantize_query(y, mode, T)
+    for t, (nib, sc) in enumerate(want):
+        bad = np.argwhere(gc[:, t] != _pack_logical(nib))
+        assert bad.size == 0, f"codes term {t}: {len(bad)} bytes differ, first rows {bad[:3, 0].tolist()}"
+        assert np.array_equal(gs[:, t], sc.astype(np.uint8)), f"scales term {t}"

@@ -284,3 +284,65 @@ def test_batched_16_sequences_sampled():
     ref = OD.decode(NV, cache, wl.q[pick], wl.block_tables[pick], wl.seq_lens[pick], sk[pick], sv[pick],
                     tk[pick], tv[pick], wl.key_shift, wl.sigma, ppp)
     assert_close(got[pick], ref, f"batched 16 x 2k..16k ppp={ppp}, sequences {pick}")
+
+
+def test_p_flips_from_float32_logits():
+    """P code and scale flips: the decode's own float32 logits
+    (bdfp4_decode_attention_logits) and the oracle's float64 logits, both fed
+    through the oracle's P quantizer (same partitions, maxima, c and tau). The
+    float32 logits agree with the float64 ones to accumulation rounding, and
+    the fraction of P codes or block scales that this rounding changes is
+    reported and bounded."""
+    from oracle import formats as F
+    from oracle import writer as W
+    r = NV
+    cases = (("tiny 2K", synth.tiny(0), 1),
+             ("ragged", synth.decode_workload("pf", 21, [3000, 1234, 640], 8, 2, "qwen", extra_pages=2), 2))
+    for what, wl, ppp in cases:
+        host = oracle_write(r, wl)
+        cache = cache_to_dev(r, host, wl.num_kv_heads)
+        B, Hq, hkv = wl.batch, wl.num_q_heads, wl.num_kv_heads
+        maxp = wl.block_tables.shape[1]
+        msl = int(wl.seq_lens.max())
+        sk, sv, tk, tv = wl.sink_tail()
+        ws = bd.alloc_workspace(bd.decode_workspace_size(B, Hq, hkv, msl, ppp))
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+        lg = torch.full((B, hkv, 4, 128 * maxp), float("nan"), dtype=torch.float32, device="cuda")
+        bd.decode_attention_logits(to_c(r), cache, dev_bf16(wl.q), dev(wl.block_tables.astype(np.int32)),
+                                   dev(wl.seq_lens.astype(np.int32)), msl, dev_bf16(sk), dev_bf16(sv), dev_bf16(tk),
+                                   dev_bf16(tv), dev(wl.key_shift), wl.sigma, ppp, ws, out, lg)
+        torch.cuda.synchronize()
+        lg = lg.cpu().numpy().astype(np.float64)
+        q = F.bf16_to_f32(wl.q)
+        n_el = n_blk = flip_el = flip_blk = 0
+        worst = 0.0
+        for b in range(B):
+            L = int(wl.seq_lens[b])
+            n_full, _, parts = OD.split_plan(L, r.sink_tokens, ppp)
+            if n_full == 0:
+                continue
+            for h in range(hkv):
+                qg = q[b, 4 * h:4 * h + 4]
+                qhat = OD.query_hat(r, qg)
+                qmu = qg.astype(np.float64) @ wl.key_shift[h].astype(np.float64)
+                khat = np.concatenate([W.read_page_head(r, host, int(wl.block_tables[b, i]), h)[0]
+                                       for i in range(n_full)])
+                raw_o = qhat @ khat.T + qmu[:, None]
+                raw_g = lg[b, h, :, :n_full * 128]
+                for lo, hi in parts:
+                    d = np.abs(raw_g[:, lo:hi] - raw_o[:, lo:hi])
+                    worst = max(worst, float(np.max(d / np.maximum(1.0, np.abs(raw_o[:, lo:hi])))))
+                    res = []
+                    for raw in (raw_o, raw_g):
+                        t = wl.sigma * raw[:, lo:hi]
+                        p = np.exp(t - t.max(axis=1, keepdims=True))
+                        res.append(Q.quantize_p((float(r.c) * p).astype(np.float32), r.scale_mode_p,
+                                                np.float32(r.tau)))
+                    flip_el += int(np.count_nonzero(res[0][0] != res[1][0]))
+                    flip_blk += int(np.count_nonzero(res[0][1] != res[1][1]))
+                    n_el += res[0][0].size
+                    n_blk += res[0][1].size
+        print(f"[p flips] {what}: logits max rel diff {worst:.2e}; P codes {flip_el}/{n_el} differ, "
+              f"block scales {flip_blk}/{n_blk}", flush=True)
+        assert worst <= 1e-5, (what, worst)
+        assert flip_el <= 1e-3 * n_el and flip_blk <= 1e-3 * n_blk, (what, flip_el, flip_blk)
