@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "bdfp4_key_means_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_key_means": [P, I32, I32, P, SZ, P, P],
         "bdfp4_error_sums": [P, P, ctypes.c_int64, P, P],
+        "bdfp4_select_tau": [P, P, I32, ctypes.POINTER(F32), ctypes.POINTER(I32), P],
         "bdfp4_page_errors_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_page_errors": [RP, CP, P, P, P, I32, P, P, SZ, P, P],
         "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
@@ -260,18 +261,28 @@ def calibrate_tau(r: Recipe, candidates, reference, decode_args: dict, stream=No
     with decode_args) and the error sums of its output against `reference`
     (exact attention of the same calibration batch, e.g. from
     bf16_decode_attention), all on the device; one copy of the sums to the
-    host at the end. Returns (best tau, relative L2 error per candidate);
-    equal errors keep the earlier candidate."""
+    host at the end, where bdfp4_select_tau picks the candidate. Returns
+    (best tau, relative L2 error per candidate)."""
     import torch
     sums = torch.zeros((len(candidates), 2), dtype=torch.float64, device=reference.device)
     out = torch.empty_like(reference)
     for i, t in enumerate(candidates):
         decode_attention(r.replace(tau=float(t)), out=out, stream=stream, **decode_args)
         error_sums(out, reference, sums[i], stream)
-    s = sums.cpu().numpy()
-    errs = [math.sqrt(a / b) for a, b in s]
-    best = min(range(len(errs)), key=lambda i: (errs[i], i))
-    return float(candidates[best]), errs
+    return select_tau(sums.cpu().numpy(), candidates)
+
+
+def select_tau(sums, candidates):
+    """bdfp4_select_tau on host error sums [n][2]: (chosen tau, relative L2
+    error per candidate)."""
+    import numpy as np
+    s = np.ascontiguousarray(sums, dtype=np.float64).reshape(-1, 2)
+    c = np.ascontiguousarray(candidates, dtype=np.float32).reshape(-1)
+    errs = np.zeros(len(c), dtype=np.float64)
+    best, idx = ctypes.c_float(), ctypes.c_int32()
+    _check(lib().bdfp4_select_tau(s.ctypes.data, c.ctypes.data, len(c), ctypes.byref(best), ctypes.byref(idx),
+                                  errs.ctypes.data))
+    return float(best.value), [float(e) for e in errs]
 
 
 def page_errors(r: Recipe, cache: PagedCache, k, v, page_ids, key_shift=None, stream=None):

@@ -1,12 +1,14 @@
 """Build libbdfp4.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m fp4_kv_cache_nvfp4_amd.build
+    python -m fp4_kv_cache_nvfp4_amd.build [--sanitize]
 
 Compiles every source under csrc/ to an object and links the shared library
 fp4_kv_cache_nvfp4_amd/lib/libbdfp4.so. Flags that matter for results:
 -ffp-contract=off (no fused multiply-add where the codecs need separate
 roundings), correctly rounded float32 division, and packed-FP32 instructions
-disabled (the v_pk_*_f32 forms are kept out of every kernel).
+disabled (the v_pk_*_f32 forms are kept out of every kernel). With
+--sanitize it builds lib/libbdfp4_san.so instead, its host API under ASan and
+UBSan (see build_sanitized).
 """
 from __future__ import annotations
 
@@ -68,5 +70,55 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI
+# layer (each -fsanitize= after -Xarch_host: device code is built as usual).
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SAN_LIB = os.path.join(LIBDIR, "libbdfp4_san.so")
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """lib/libbdfp4_san.so: the library with its host API (api.cpp: every
+    recipe, shape, pointer and workspace check, the plan and the tau choice)
+    compiled under ASan and UBSan, linked with the regular device objects.
+    Load it after the sanitizer runtime (LD_PRELOAD of the clang ASan
+    runtime); the CPU test of the host ABI runs this way."""
+    if not all(os.path.exists(os.path.join(BUILD, s + ".o")) for s in SOURCES):
+        build(verbose=False)
+    obj = os.path.join(BUILD, "api.cpp.san.o")
+    cmd = [hipcc(), *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized api.cpp:\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "api.cpp"]
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime the sanitized library needs."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for c in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if c and os.path.exists(c):
+            r = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            p = r.stdout.strip()
+            if r.returncode == 0 and os.path.exists(p):
+                return p
+    raise RuntimeError("clang ASan runtime not found")
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "--sanitize":
+        build_sanitized()
+    else:
+        build()

@@ -377,6 +377,34 @@ bdfp4_status bdfp4_error_sums(const float* got, const float* ref, int64_t n, dou
                     "error sums launch");
 }
 
+bdfp4_status bdfp4_select_tau(const double* sums, const float* candidates, int32_t n, float* best_tau,
+                              int32_t* best_index, double* rel_errors) {
+  if (n < 1) return fail(BDFP4_E_INVALID, "n must be >= 1");
+  if (!sums || !candidates || !best_tau) return fail(BDFP4_E_INVALID, "NULL pointer");
+  int best = -1;
+  double best_err = 0.0;
+  bool any = false;
+  for (int32_t i = 0; i < n; ++i) {
+    const double e = sums[2 * i], r = sums[2 * i + 1];
+    if (e < 0.0 || r < 0.0) return fail(BDFP4_E_INVALID, "error sums of candidate %d are negative", i);
+    double rel;
+    if (isnan(e) || isnan(r)) rel = NAN;
+    else if (r == 0.0) rel = e == 0.0 ? 0.0 : INFINITY;
+    else rel = sqrt(e / r);
+    if (rel_errors) rel_errors[i] = rel;
+    if (isnan(rel)) continue;
+    any = true;
+    if (best < 0 || rel < best_err) {   // strict: a tie keeps the earlier candidate
+      best = i;
+      best_err = rel;
+    }
+  }
+  if (!any) return fail(BDFP4_E_INVALID, "every candidate's error is NaN");
+  *best_tau = candidates[best];
+  if (best_index) *best_index = best;
+  return ok();
+}
+
 bdfp4_status bdfp4_page_errors_workspace_size(int32_t n_pages, int32_t num_kv_heads, size_t* bytes) {
   if (!bytes) return fail(BDFP4_E_INVALID, "NULL output");
   if (n_pages < 1 || num_kv_heads < 1 || (int64_t)n_pages * num_kv_heads > 0x7FFFFFFF)

@@ -231,6 +231,21 @@ bdfp4_status bdfp4_key_means(const void* k_bf16, int32_t tokens, int32_t num_kv_
 bdfp4_status bdfp4_error_sums(const float* got, const float* ref, int64_t n, double* sums_out,
                               void* stream);
 
+/* The tau choice of the calibration search (host only; config.py
+ * probability_environment leaves tau to calibration and states no
+ * objective): candidate i's error is the relative L2 error
+ * sqrt(sums[2i] / sums[2i + 1]) of its decode output against exact
+ * attention (the two sums of bdfp4_error_sums, copied to the host; a zero
+ * reference sum gives 0 for a zero error, else +inf; a NaN error counts as
+ * +inf). The smallest error wins and ties keep the earlier candidate.
+ *   sums: host double [n][2]; candidates: host float [n]; n >= 1;
+ *   best_tau: host, the chosen candidate; best_index: host or NULL;
+ *   rel_errors: host double [n] or NULL, each candidate's error.
+ * E_INVALID for n < 1, NULL inputs, negative sums, or when every error is
+ * NaN. */
+bdfp4_status bdfp4_select_tau(const double* sums, const float* candidates, int32_t n, float* best_tau,
+                              int32_t* best_index, double* rel_errors);
+
 /* Quantization diagnostics ("kv-landlords scripts/quant_ab.py" compares
  * cache schemes by reconstruction error; the recipe ablations of
  * "BitDecoding-FP4 evaluation/config.py"): for n_pages pages written from

@@ -334,3 +334,21 @@ def test_channel_key_geometry_support():
         assert ei.value.status == bd.E_UNSUPPORTED
     # the cache sizes do not depend on the key geometry
     assert bd.cache_bytes(nv.replace(key_scale_geometry=bd.KEY_GEOMETRY_CHANNEL), 3, 2) == bd.cache_bytes(nv, 3, 2)
+
+
+def test_select_tau_host():
+    """bdfp4_select_tau: relative L2 errors sqrt(err / ref), the smallest
+    wins, ties keep the earlier candidate, NaN never wins, zero references."""
+    import numpy as np
+    cand = [0.0, 0.5, 1.0, 4.0]
+    sums = np.array([[4.0, 100.0], [1.0, 100.0], [1.0, 100.0], [9.0, 100.0]])
+    best, errs = bd.select_tau(sums, cand)
+    assert best == 0.5 and np.allclose(errs, [0.2, 0.1, 0.1, 0.3], rtol=0, atol=1e-15)
+    sums2 = np.array([[np.nan, 1.0], [0.0, 0.0], [1.0, 0.0], [0.25, 1.0]])
+    best, errs = bd.select_tau(sums2, cand)
+    assert best == 0.5 and errs[1] == 0.0 and errs[2] == float("inf") and np.isnan(errs[0])
+    with pytest.raises(bd.Bdfp4Error) as ei:
+        bd.select_tau(np.array([[np.nan, 1.0]]), [1.0])
+    assert ei.value.status == bd.E_INVALID
+    with pytest.raises(bd.Bdfp4Error):
+        bd.select_tau(np.array([[-1.0, 1.0]]), [1.0])
