@@ -146,11 +146,17 @@ bdfp4_status check_cache(const bdfp4_cache* c) {
   return BDFP4_OK;
 }
 
+// Pages per partition for the MI355X's 256 compute units. The smallest that
+// keeps the FP4 workgroups (four partitions each) within one per compute
+// unit, when one of up to 4 pages does: the grid then has room for the BF16
+// partitions' own workgroups. Longer contexts take about two FP4 workgroups
+// per compute unit (measured best from 8K to 128K tokens at batch 1, 8 KV
+// heads: 1 page up to 16K, 2 at 32K, 3 at 48K, 4 at 64K, 3 at 96K, 4 at 128K).
 int32_t auto_ppp(int32_t batch, int32_t hkv, int32_t max_seq_len) {
   const int64_t n_full = max_seq_len / 128;
   const int64_t work = (int64_t)batch * hkv * n_full;     // full page-heads
-  // about 512 FP4 workgroups of four partitions: 2 resident per CU
-  int64_t ppp = (work + 2047) / 2048;
+  int64_t ppp = (work + 1023) / 1024;                     // <= 256 workgroups
+  if (ppp > 4) ppp = (work + 2047) / 2048;                // about 512 workgroups
   if (ppp < 1) ppp = 1;
   if (ppp > 4) ppp = 4;
   return (int32_t)ppp;

@@ -66,6 +66,7 @@
 // lies in [2^-10, 2688], so it is exact in f16. The NVFP4 V page stores tokens
 // t, t+1 of one channel in a byte, so a converted pair is directly one 32-bit
 // word of the PV B operand.
+#include <atomic>
 #include <mutex>
 
 #include "codec.hpp"
@@ -957,57 +958,75 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   return r;
 }
 
-// Workgroup j works for (sequence, KV head) j % (B Hkv) as its FP4 workgroup
-// sp = j / (B Hkv): the first B Hkv workgroups of the grid, dispatched first
-// and the oldest on their CUs, are the sp = 0 workgroups of every (sequence,
-// KV head), and those also compute the BF16 partition (before requesting
-// their first K pages) and fold it into their partial. Workgroup sp stores its
-// partial in slot sp and takes the (sequence, KV head)'s ticket; the last of
-// the nwg merges them all. A sequence without a full page has only the BF16
-// partition, written straight to the output by its sp = 0 workgroup; a
-// sequence with one FP4 workgroup writes that workgroup's o / l directly (no
+// Workgroup j works for (sequence, KV head) bh = j % (B Hkv) in grid column
+// c = j / (B Hkv). A launch whose grid has room for one more column
+// (split_bf16: it still fits the chip at two workgroups per compute unit)
+// gives every BF16 partition (sink + tail) a workgroup of its own in column
+// 0, the first B Hkv workgroups of the grid (dispatched first), which runs
+// beside the FP4 workgroups instead of delaying one of them; FP4 workgroup
+// sp then sits in column sp + 1. Otherwise FP4 workgroup sp sits in column
+// sp, and workgroup 0 also computes the BF16 partition, before it requests
+// its first K pages, and folds it into its partial. FP4 workgroup sp stores
+// its partial in slot sp, a BF16 workgroup in slot nwg (nwg = the sequence's
+// FP4 workgroups), and each takes the (sequence, KV head)'s ticket; the last
+// merges all partials (the BF16 one as the merge's extra slot). Without BF16
+// workgroups a sequence with one FP4 workgroup writes its o / l directly (no
 // partial, ticket or merge: the merge of a single partial is that quotient).
+// A sequence without a full page has only the BF16 partition, written
+// straight to the output by column 0.
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
-__global__ void __launch_bounds__(256) decode_kernel(DecArgs A) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMx || kChan || kRunMax ? 2 : 3)))
+decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
   const MergeCtx C = merge_ctx(A);
   const int BH = P.batch * P.hkv;
-  const int bh = (int)blockIdx.x % BH, sp = (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x % BH, col = (int)blockIdx.x / BH;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
-  const Early E = early_loads(P, b, h, sp);
+  const int split = P.split_bf16;                          // 0 or 1, uniform per launch
+  const int sp = col - split;                              // FP4 workgroup of this column (-1: BF16)
+  const Early E = early_loads(P, b, h, sp < 0 ? 0 : sp);
   const int L = P.seq_lens[b];
   if (L < 1 || L > P.max_seq_len || L / kPage > P.max_pages_per_seq) {
-    if (sp == 0) poison_rows(P.out, P.hq, b, h);
+    if (col == 0) poison_rows(P.out, P.hq, b, h);
     return;
   }
   const int n_full = L / kPage;
   const int nwg = n_full > 0 ? fp4_wgs((n_full + P.ppp - 1) / P.ppp) : 0;   // FP4 workgroups of this sequence
-  if (nwg == 0) {
-    if (sp == 0) {
-      const Partial r = bf16_partition(A, sm, b, h, L, 0);
+  if (nwg == 0 || sp < 0) {
+    // the BF16 partition alone: the whole attention of a sequence without a
+    // full page, else its own workgroup (one call site for both)
+    if (col != 0) return;
+    Partial r = bf16_partition(A, sm, b, h, L, n_full);
+    if (nwg == 0) {
       const int head = threadIdx.x >> 6, d = 2 * (threadIdx.x & 63);
       const float l = of_head(r.l[0], r.l[1], r.l[2], r.l[3], head);
       float* out = P.out + ((size_t)b * P.hq + h * kGroup + head) * kD + d;
       *reinterpret_cast<float2*>(out) = make_float2(r.o0 / l, r.o1 / l);
+      return;
     }
-    return;
+    // with rotated values its o enters the merge in the rotated domain, like
+    // the FP4 partials
+    if (P.rotate_v) wave_rotate2(r.o0, r.o1);            // uniform per workgroup
+    write_partial(partial_writer(C, bh, nwg), r);
+  } else {
+    if (sp >= nwg) return;
+    const Partial mine =
+        fp4_wg<kMx, kTerms, kUnder, kRunMax, kSlots, kChan>(A, sm, b, h, sp, L, split == 0 && sp == 0, E);
+    if (split == 0 && nwg == 1) {
+      const int head = threadIdx.x >> 6, d = 2 * (threadIdx.x & 63);
+      const float l = of_head(mine.l[0], mine.l[1], mine.l[2], mine.l[3], head);
+      float o0 = mine.o0, o1 = mine.o1;
+      if (P.rotate_v) wave_rotate2(o0, o1);              // uniform per workgroup
+      float* out = P.out + ((size_t)b * P.hq + h * kGroup + head) * kD + d;
+      *reinterpret_cast<float2*>(out) = make_float2(o0 / l, o1 / l);
+      return;
+    }
+    write_partial(partial_writer(C, bh, sp), mine);
   }
-  if (sp >= nwg) return;
-  const Partial mine = fp4_wg<kMx, kTerms, kUnder, kRunMax, kSlots, kChan>(A, sm, b, h, sp, L, sp == 0, E);
-  if (nwg == 1) {
-    const int head = threadIdx.x >> 6, d = 2 * (threadIdx.x & 63);
-    const float l = of_head(mine.l[0], mine.l[1], mine.l[2], mine.l[3], head);
-    float o0 = mine.o0, o1 = mine.o1;
-    if (P.rotate_v) wave_rotate2(o0, o1);                // uniform per workgroup
-    float* out = P.out + ((size_t)b * P.hq + h * kGroup + head) * kD + d;
-    *reinterpret_cast<float2*>(out) = make_float2(o0 / l, o1 / l);
-    return;
-  }
-  write_partial(partial_writer(C, bh, sp), mine);
   uint32_t* ticket = C.counters + (size_t)bh * C.counter_stride;
-  if (take_ticket(ticket, 1, &sm.tick) == nwg - 1) {
-    merge_out(C, b, h, nwg, P.rotate_v != 0);
+  if (take_ticket(ticket, 1, &sm.tick) == nwg - 1 + split) {
+    merge_out(C, b, h, nwg, P.rotate_v != 0, split ? nwg : -1);
     reset_ticket(ticket);
   }
 }
@@ -1092,10 +1111,38 @@ hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
   return hipSuccess;
 }
 
+// Compute units of the current device (cached per device).
+static hipError_t device_cus(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   DecArgs A;
   A.L = L;
-  const dim3 grid((unsigned)(L.batch * L.hkv * fp4_wgs(L.max_parts))), block(256u);
+  // BF16 partition workgroups of their own when one more grid column still
+  // fits the chip at two workgroups per compute unit (with a full chip the
+  // extra column would wait for a free slot and end the kernel later)
+  int cus = 0;
+  const hipError_t ce = device_cus(&cus);
+  if (ce != hipSuccess) return ce;
+  const int wgs = fp4_wgs(L.max_parts);
+  A.L.split_bf16 = wgs >= 2 && (long long)L.batch * L.hkv * (wgs + 1) <= 2LL * cus ? 1 : 0;
+  // the FP4 workgroups of the longest sequence, after a column of BF16
+  // partition workgroups when the launch has them
+  const int cols = wgs + A.L.split_bf16;
+  const dim3 grid((unsigned)(L.batch * L.hkv * cols)), block(256u);
   const bool under = L.p_mode == 4;
   // page slots per kind: the plan's pages_per_partition rounded up to 1, 2, 4
   const int slots = L.ppp <= 1 ? 1 : (L.ppp == 2 ? 2 : 4);

@@ -179,11 +179,15 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 // slot past them reads 0 and needs no address select; its weight is 0. The
 // partials are always combined in slot order (lane order for l, slot order
 // for o), so the result does not depend on which workgroup merges: the
-// output is deterministic. With rotate_back (values stored rotated), the
-// merged o is rotated back before the division.
+// output is deterministic. With extra >= 0 the partial in slot `extra` (past
+// the n, the FP4 decode's BF16 partition) is merged too: its loads are
+// issued ahead of the first batch's, so they share that round trip, and it
+// is combined after the last batch. With rotate_back (values stored
+// rotated), the merged o is rotated back before the division.
 constexpr int kMergeBatch = 64;
 
-__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n, bool rotate_back) {
+__device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n, bool rotate_back,
+                                          int extra = -1) {
   // (sequence, KV head) and n as scalars: the buffer resource below must
   // live in scalar registers, or every load becomes a loop over distinct values
   const int bh = __builtin_amdgcn_readfirstlane(b * C.hkv + h);
@@ -194,6 +198,18 @@ __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n
   const __amdgpu_buffer_rsrc_t R =
       __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0, ns * kSlotBytes, kRawBufferWord3);
   const int o_off = (g * kD + 2 * lane) * 4;
+  // the extra partial, through a resource that covers its slot as well (the
+  // batches keep theirs: a slot past the n reads 0)
+  const int xs = __builtin_amdgcn_readfirstlane(extra);
+  float mx = ninf, lx = 0.0f;
+  float2 ox = make_float2(0.0f, 0.0f);
+  if (xs >= 0) {
+    const __amdgpu_buffer_rsrc_t RX =
+        __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0, (xs + 1) * kSlotBytes, kRawBufferWord3);
+    mx = cload1(RX, xs * kSlotBytes + (512 + g) * 4);
+    lx = cload1(RX, xs * kSlotBytes + (516 + g) * 4);
+    ox = cload2(RX, xs * kSlotBytes + o_off);
+  }
   float M = ninf, Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int i0 = 0; i0 < ns; i0 += kMergeBatch) {
     const int i = i0 + lane;
@@ -217,6 +233,14 @@ __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n
       o1 = fmaf(wk, ov[k].y, o1);
     }
     M = Mn;
+  }
+  if (xs >= 0) {
+    const float Mn = fmaxf(M, mx);
+    const float f = M == ninf ? 0.0f : __expf(M - Mn);
+    const float w = mx == ninf ? 0.0f : __expf(mx - Mn);
+    Ls = fmaf(Ls, f, w * lx);
+    o0 = fmaf(w, ox.x, o0 * f);
+    o1 = fmaf(w, ox.y, o1 * f);
   }
   if (rotate_back) wave_rotate2(o0, o1);                // uniform per workgroup
   float* out = C.out + ((size_t)b * C.hq + h * kGroup + g) * kD + 2 * lane;

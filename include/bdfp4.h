@@ -267,9 +267,12 @@ bdfp4_status bdfp4_page_errors(const bdfp4_recipe* r, const bdfp4_cache* cache,
 
 /* Split plan of bdfp4_decode_attention (host). pages_per_partition (1 .. 4)
  * is the number of consecutive full pages one FP4 partition covers; 0 picks
- * it from (batch, num_kv_heads, max_seq_len) so that about 512 workgroups of
- * four partitions are launched. The chosen value and the number of FP4
- * partitions of the longest sequence are returned. */
+ * it from (batch, num_kv_heads, max_seq_len) for the MI355X's 256 compute
+ * units: the smallest value that keeps the workgroups of four partitions
+ * within 256 when one of up to 4 pages does (the launch then also gives
+ * the BF16 partitions workgroups of their own), else about 512. The chosen
+ * value and the number of FP4 partitions of the longest sequence are
+ * returned. */
 bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads,
                                int32_t max_seq_len, int32_t pages_per_partition,
                                int32_t* pages_per_partition_out,

@@ -106,6 +106,12 @@ def test_sizes_and_plan():
     assert bd.decode_plan(1, 1, 100, 4) == (4, 0)
     ppp, parts = bd.decode_plan(1, 8, 131072, 0)
     assert ppp == 4 and parts == -(-1024 // ppp)
+    # the automatic plan: at most 256 FP4 workgroups of four partitions while
+    # 4 pages per partition suffice, else about 512
+    assert [bd.decode_plan(1, 8, L, 0) for L in (8192, 16384, 32768, 49152, 65536, 98304)] == \
+        [(1, 64), (1, 128), (2, 128), (3, 128), (4, 128), (3, 256)]
+    assert bd.decode_plan(16, 8, 16384, 0) == (4, 32)
+    assert bd.decode_plan(1, 1, 2048, 0) == (1, 16)
     ws = bd.decode_workspace_size(1, 32, 8, 131072, 4)
     assert ws == 16384 * 4 + 8 * (256 + 2) * 520 * 4
     # a partial last page adds a BF16-decode partition
