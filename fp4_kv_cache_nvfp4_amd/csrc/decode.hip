@@ -1128,30 +1128,45 @@ static hipError_t device_cus(int* cus) {
   return hipSuccess;
 }
 
+// One decode instantiation: BF16 partition workgroups of their own when one
+// more grid column still fits the chip at the kernel's occupancy (with a full
+// chip the extra column would wait for a free slot and end the kernel later;
+// the occupancy, from its registers and LDS, is asked once per
+// instantiation), then the launch.
+template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
+static hipError_t launch_one(DecArgs A, int cus, hipStream_t stream) {
+  static std::atomic<int> occupancy{0};
+  int per_cu = occupancy.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, decode_kernel<kMx, kTerms, kUnder, kRunMax, kSlots, kChan>, 256, 0);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) per_cu = 1;
+    occupancy.store(per_cu, std::memory_order_relaxed);
+  }
+  const long long bh = (long long)A.L.batch * A.L.hkv;
+  const int wgs = fp4_wgs(A.L.max_parts);
+  A.L.split_bf16 = wgs >= 2 && bh * (wgs + 1) <= (long long)per_cu * cus ? 1 : 0;
+  // the FP4 workgroups of the longest sequence, after a column of BF16
+  // partition workgroups when the launch has them
+  const dim3 grid((unsigned)(bh * (wgs + A.L.split_bf16))), block(256u);
+  hipLaunchKernelGGL((decode_kernel<kMx, kTerms, kUnder, kRunMax, kSlots, kChan>), grid, block, 0, stream, A);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   DecArgs A;
   A.L = L;
-  // BF16 partition workgroups of their own when one more grid column still
-  // fits the chip at two workgroups per compute unit (with a full chip the
-  // extra column would wait for a free slot and end the kernel later)
   int cus = 0;
   const hipError_t ce = device_cus(&cus);
   if (ce != hipSuccess) return ce;
-  const int wgs = fp4_wgs(L.max_parts);
-  A.L.split_bf16 = wgs >= 2 && (long long)L.batch * L.hkv * (wgs + 1) <= 2LL * cus ? 1 : 0;
-  // the FP4 workgroups of the longest sequence, after a column of BF16
-  // partition workgroups when the launch has them
-  const int cols = wgs + A.L.split_bf16;
-  const dim3 grid((unsigned)(L.batch * L.hkv * cols)), block(256u);
   const bool under = L.p_mode == 4;
   // page slots per kind: the plan's pages_per_partition rounded up to 1, 2, 4
   const int slots = L.ppp <= 1 ? 1 : (L.ppp == 2 ? 2 : 4);
-#define BDFP4_LAUNCH_S(MX, T, U, R, C)                                                                  \
-  do {                                                                                                  \
-    if (slots == 1) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 1, C>), grid, block, 0, stream, A);    \
-    else if (slots == 2) hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 2, C>), grid, block, 0, stream, A); \
-    else hipLaunchKernelGGL((decode_kernel<MX, T, U, R, 4, C>), grid, block, 0, stream, A);               \
-  } while (0)
+#define BDFP4_LAUNCH_S(MX, T, U, R, C)                                               \
+  return slots == 1   ? launch_one<MX, T, U, R, 1, C>(A, cus, stream)                  \
+         : slots == 2 ? launch_one<MX, T, U, R, 2, C>(A, cus, stream)                  \
+                      : launch_one<MX, T, U, R, 4, C>(A, cus, stream)
 #define BDFP4_LAUNCH(MX, T, U) BDFP4_LAUNCH_S(MX, T, U, false, false)
 #define BDFP4_LAUNCH_CH(T, U) BDFP4_LAUNCH_S(false, T, U, false, true)
   if (L.k_chan) {
@@ -1175,7 +1190,6 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
 #undef BDFP4_LAUNCH
 #undef BDFP4_LAUNCH_CH
 #undef BDFP4_LAUNCH_S
-  return hipGetLastError();
 }
 
 }  // namespace bdfp4
