@@ -177,8 +177,9 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 // workgroup reads its own partial back like the others (its stores completed
 // before it took the ticket). The resource covers exactly the n slots, so a
 // slot past them reads 0 and needs no address select; its weight is 0. The
-// partials are always combined in slot order (lane order for l, slot order
-// for o), so the result does not depend on which workgroup merges: the
+// partials are always combined in slot order (lane order for l, a fixed
+// tree over slot-ordered chains for o), so the result does not depend on
+// which workgroup merges: the
 // output is deterministic. With extra >= 0 the partial in slot `extra` (past
 // the n, the FP4 decode's BF16 partition) is merged too: its loads are
 // issued ahead of the first batch's, so they share that round trip, and it
@@ -224,14 +225,17 @@ __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n
     const float f = M == ninf ? 0.0f : __expf(M - Mn);     // rescale of the partials before
     const float w = ms == ninf ? 0.0f : __expf(ms - Mn);
     Ls = fmaf(Ls, f, wave_sum(w * lr));
-    o0 *= f;
-    o1 *= f;
+    // the batch's weighted sum in four independent FMA chains (slots k with
+    // k mod 4 = c), added in a fixed tree: a quarter of the dependent latency
+    float c0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const float wk = lane_f32(w, k);
-      o0 = fmaf(wk, ov[k].x, o0);
-      o1 = fmaf(wk, ov[k].y, o1);
+      c0[k & 3] = fmaf(wk, ov[k].x, c0[k & 3]);
+      c1[k & 3] = fmaf(wk, ov[k].y, c1[k & 3]);
     }
+    o0 = fmaf(o0, f, (c0[0] + c0[1]) + (c0[2] + c0[3]));
+    o1 = fmaf(o1, f, (c1[0] + c1[1]) + (c1[2] + c1[3]));
     M = Mn;
   }
   if (xs >= 0) {
