@@ -27,10 +27,16 @@ The pages give no formulas for the decode. Readings taken here, in order:
    contiguous range of pages_per_partition FP4 pages (the first one starts
    after the sink).
 5. Per partition s: m_s = max_j t_j, p_j = exp(t_j - m_s), l_s = sum_j p_j
-   (unquantized). FP4 partitions quantize p' = float32(c * p_j) per 16-token
-   block aligned to the logical token index with the P scale mode and use
-   P_hat = s * e2m1 / c; the BF16 partition uses P_hat = p.
-   o_s = sum_j P_hat_j * v_hat_j.
+   (unquantized). FP4 partitions quantize p'_j per 16-token block aligned to
+   the logical token index with the P scale mode and use P_hat = s * e2m1 / c;
+   the BF16 partition uses P_hat = p. o_s = sum_j P_hat_j * v_hat_j.
+   The pages fix no precision for p', and p' decides integers (the P codes
+   and block scales), so it is formed in float32, the precision in which the
+   decode forms it: with r_j = float32(q_hat . k_hat_j + q . mu) and
+   r_m = max_j r_j, p'_j = c * 2^a_j, a_j = fl32(fl32(r_j - r_m) * k) and
+   k = fl32(fl32(sigma) * fl32(log2 e)), 2^a_j taken in float64 and rounded
+   once to float32 (c is a power of two). Everything else about the
+   partition (m_s, l_s, P_hat's values, o_s) is float64.
 6. Merge: M = max_s m_s, L = sum_s l_s exp(m_s - M),
    out = sum_s o_s exp(m_s - M) / L (float output).
 
@@ -72,12 +78,22 @@ def query_hat(recipe: Recipe, q_f32: np.ndarray) -> np.ndarray:
     return qhat
 
 
-def _p_hat(recipe: Recipe, p: np.ndarray) -> np.ndarray:
-    """Quantized probabilities of one FP4 partition, p [G, n] float64 with n a
-    multiple of 16 (blocks aligned to logical token index)."""
-    if recipe.scale_mode_p == Q.NONE:
-        return p
-    pp = (float(recipe.c) * p).astype(np.float32)
+def p_prime(recipe: Recipe, sigma: float, raw: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """p' = c * 2^(fl32(fl32(r - ref) * fl32(fl32(sigma) * fl32(log2 e)))) in
+    float32 (reading 5): raw [G, n] logits without sigma (float64, rounded
+    to float32 here), ref [G] or [G, n] the float32 reference maximum."""
+    r32 = np.asarray(raw).astype(np.float32)
+    k = np.float32(np.float32(sigma) * np.float32(math.log2(math.e)))
+    ref32 = np.asarray(ref, dtype=np.float32)
+    if ref32.ndim == 1:
+        ref32 = ref32[:, None]
+    a = ((r32 - ref32).astype(np.float32) * k).astype(np.float32)
+    return (float(recipe.c) * np.exp2(a.astype(np.float64))).astype(np.float32)
+
+
+def _p_hat(recipe: Recipe, pp: np.ndarray) -> np.ndarray:
+    """Quantized probabilities of one FP4 partition from p' [G, n] float32
+    (n a multiple of 16, blocks aligned to logical token index)."""
     nib, sc = Q.quantize_p(pp, recipe.scale_mode_p, np.float32(recipe.tau))
     return Q.dequantize(nib, sc, Q.AMAX6) / float(recipe.c)
 
@@ -125,18 +141,23 @@ def attend_head(recipe: Recipe, q_f32: np.ndarray, seq_len: int,
         qhat = query_hat(recipe, q_f32)
         qmu = q64 @ np.asarray(mu, dtype=np.float64) if recipe.key_smoothing else np.zeros(G)
         for lo, hi in parts:
-            t = sigma * (qhat @ k_hat[lo:hi].T + qmu[:, None])
+            raw = qhat @ k_hat[lo:hi].T + qmu[:, None]
+            t = sigma * raw
             m = t.max(axis=1)
             p = np.exp(t - m[:, None])
-            if recipe.p_running_max:
+            r32 = raw.astype(np.float32)
+            if recipe.scale_mode_p == Q.NONE:
+                ph = p
+            elif recipe.p_running_max:
                 # recipe variant: each aligned 16-token block is normalised by
                 # the running maximum over the partition's blocks up to it (as
                 # a one-pass kernel would see it), quantized against that, and
                 # weighted back to the partition maximum
-                mrun = np.repeat(np.maximum.accumulate(t.reshape(G, -1, 16).max(axis=2), axis=1), 16, axis=1)
-                ph = _p_hat(recipe, np.exp(t - mrun)) * np.exp(mrun - m[:, None])
+                run = lambda x: np.repeat(np.maximum.accumulate(x.reshape(G, -1, 16).max(axis=2), axis=1), 16, axis=1)
+                mrun = run(t)
+                ph = _p_hat(recipe, p_prime(recipe, sigma, raw, run(r32))) * np.exp(mrun - m[:, None])
             else:
-                ph = _p_hat(recipe, p)
+                ph = _p_hat(recipe, p_prime(recipe, sigma, raw, r32.max(axis=1)))
             o = ph @ v_hat[lo:hi]
             if recipe.rotate_v:
                 # v_hat are rotated values: rotate this partition's output

@@ -18,11 +18,25 @@ from oracle import writer as W
 # quantized operands and partitioning
 MAX_ABS = 2e-3
 REL_L2 = 1e-3
-# beside it, an element-wise bound scaled to each output row's magnitude:
-# |got - ref| <= ROW_SCALED * max |ref row|. At long contexts an output row
-# averages many value rows and its entries shrink towards 1e-3, where the
-# absolute bound above no longer constrains anything.
-ROW_SCALED = 2e-3
+# beside it, element-wise bounds scaled to each output row's magnitude
+# (|got - ref| / max |ref row|): at long contexts an output row averages many
+# value rows and its entries shrink towards 1e-3, where the absolute bound
+# above no longer constrains anything. Every row within ROW_SCALED, and all
+# rows but row_flips_allowed(rows) (at least one, or one in 256) within
+# ROW_BULK. The few rows allowed between the two are those where the decode's
+# float32 logits (accumulated in another order) and the oracle's, rounded to
+# float32, put a p' on opposite sides of a P rounding boundary: one P code
+# one grid step apart moves its row by up to ~2e-3 of the row's largest
+# entry (measured 0.6e-3 on the full 128K layer and 1.2e-3 on the batch of
+# 16; with the P decisions taken on the decode's own logits those rows agree
+# to 2e-7 and 4e-7). Every other row agrees to 4e-7, the running-maximum P
+# variant to 2e-4 (P_hat w rounded to f16).
+ROW_SCALED = 1e-2
+ROW_BULK = 1e-3
+
+
+def row_flips_allowed(n_rows: int) -> int:
+    return max(1, n_rows // 256)
 
 _MODE = {Q.NONE: bd.SCALE_NONE, Q.AMAX6: bd.SCALE_AMAX6, Q.FOUR_SIX: bd.SCALE_FOUR_SIX,
          Q.MXFP4_SEARCH: bd.SCALE_MXFP4_SEARCH, Q.AMAX2_OR_AMAX6: bd.SCALE_AMAX2_OR_AMAX6}
@@ -72,7 +86,10 @@ def gpu_write(r: RC.Recipe, wl, cache: bd.PagedCache | None = None) -> bd.PagedC
 def oracle_write(r: RC.Recipe, wl) -> dict:
     cache = W.empty_cache(wl.num_pages, wl.num_kv_heads, r)
     k, v, ids = wl.writer_inputs()
-    if len(ids):
+    if len(ids) * wl.num_kv_heads > 512:
+        import oracle_pool
+        oracle_pool.write_pages(r, cache, k, v, ids, wl.key_shift if r.key_smoothing else None)
+    elif len(ids):
         W.write_pages(r, cache, k, v, ids, wl.key_shift if r.key_smoothing else None)
     return cache
 
@@ -120,16 +137,25 @@ def errors(got: np.ndarray, ref: np.ndarray):
     return float(np.max(np.abs(d))), float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
 
 
-def row_scaled_error(got: np.ndarray, ref: np.ndarray) -> float:
-    """max over output rows (last axis = channels) of max |got - ref| / max |ref|."""
+def row_scaled_errors(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per output row (last axis = channels): max |got - ref| / max |ref|."""
     d = np.abs(got - ref).reshape(-1, ref.shape[-1]).max(axis=1)
     m = np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=1)
-    return float(np.max(d / np.maximum(m, 1e-30)))
+    return d / np.maximum(m, 1e-30)
+
+
+def row_scaled_error(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over output rows of max |got - ref| / max |ref|."""
+    return float(np.max(row_scaled_errors(got, ref)))
 
 
 def assert_close(got, ref, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     mx, rel = errors(got, ref)
-    rs = row_scaled_error(got, ref)
-    print(f"[parity] {what}: max_abs={mx:.3e} rel_l2={rel:.3e} row_scaled={rs:.3e}", flush=True)
+    rows = row_scaled_errors(got, ref)
+    rs = float(np.max(rows))
+    above = int(np.count_nonzero(rows > ROW_BULK))
+    print(f"[parity] {what}: max_abs={mx:.3e} rel_l2={rel:.3e} row_scaled={rs:.3e} "
+          f"rows_above_{ROW_BULK:g}={above}/{rows.size}", flush=True)
     assert mx <= MAX_ABS and rel <= REL_L2 and rs <= ROW_SCALED, (what, mx, rel, rs)
+    assert above <= row_flips_allowed(rows.size), (what, above, rows.size)

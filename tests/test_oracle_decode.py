@@ -282,8 +282,8 @@ def test_p_blocks_follow_bruteforce_quantizer():
     rng = np.random.default_rng(6)
     t = rng.standard_normal((4, 64)) * 3
     p = np.exp(t - t.max(axis=1, keepdims=True))
-    ph = OD._p_hat(r, p)
     pp = (8.0 * p).astype(np.float32)
+    ph = OD._p_hat(r, pp)
     for g in range(4):
         for blk in range(4):
             x = pp[g, blk * 16:(blk + 1) * 16]
@@ -294,6 +294,31 @@ def test_p_blocks_follow_bruteforce_quantizer():
                 r_ = Fraction(float(x[j])) / s
                 m = min(range(8), key=lambda i: (abs(r_ - Fraction(GRID[i])), i % 2))
                 assert ph[g, blk * 16 + j] == float(Fraction(GRID[m]) * s / 8)
+
+
+def test_p_prime_is_c_exp_sigma_t_minus_max_in_float32():
+    """p' (the float32 probabilities the P codes are decided on): c exactly at
+    the maximum, c * exp(sigma (r - m)) to float32 rounding elsewhere (within
+    a few units in the last place: the argument is rounded twice), float32,
+    non-negative, and increasing with r; against the running maximum it is
+    c * exp(sigma (r - ref)) for the given reference."""
+    rng = np.random.default_rng(11)
+    sigma = 1.0 / np.sqrt(128.0)
+    raw = rng.standard_normal((4, 96)) * 20.0
+    for c in (1, 8):
+        r = RC.nvfp4_default().with_(tau=1.0, c=c)
+        m32 = raw.astype(np.float32).max(axis=1)
+        pp = OD.p_prime(r, sigma, raw, m32)
+        assert pp.dtype == np.float32 and np.all(pp >= 0)
+        want = c * np.exp(sigma * (raw.astype(np.float32).astype(np.float64) - m32[:, None].astype(np.float64)))
+        assert np.all(np.abs(pp - want) <= 4e-6 * want + 1e-30)
+        assert np.all(pp[np.arange(4), raw.argmax(axis=1)] == np.float32(c))
+        order = np.argsort(raw, axis=1)
+        assert np.all(np.diff(np.take_along_axis(pp, order, axis=1), axis=1) >= 0)
+        ref = np.maximum.accumulate(raw.astype(np.float32), axis=1)
+        pr = OD.p_prime(r, sigma, raw, ref)
+        assert np.all(np.abs(pr - c * np.exp(sigma * (raw.astype(np.float32) - ref).astype(np.float64)))
+                      <= 4e-6 * c)
 
 
 def test_bf16_baseline_is_textbook():
