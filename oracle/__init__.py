@@ -29,7 +29,8 @@ validation rules but no formulas; where they leave a step open the oracle
 takes one plain reading and says so in the function that implements it.
 Functions whose rule is such a reading (the four_six and mxfp4_search
 criteria, the amax2_or_amax6 branch, the sink partition, the P normaliser
-and the block shape of the channel key scale geometry) are pinned only by
+and the float32 form of p', and the block shape of the channel key scale
+geometry) are pinned only by
 invariants and brute force, not by values printed on the pages: their parity
 is "parity unpinned" with respect to the pages' own implementation.
 """
