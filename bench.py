@@ -683,7 +683,7 @@ def main():
                    "pages_per_partition": ppp, "partitions": parts, "graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": "bdfp4::decode_kernel<false,2,true,false>",
+                     "kernel": "bdfp4::decode_kernel<false,2,true,false,4,false>",
                      "bytes_per_launch": h["bytes_per_layer"], "us_per_launch": round(us_launch, 3),
                      "us_per_launch_single_events": round(h["us_kernel_events"], 3),
                      "read_ceiling": ceiling,
