@@ -227,6 +227,12 @@ __device__ __forceinline__ void page_head(const WriterArgs& a, const Rows& rows,
   }
 }
 
+// One workgroup per (input page, KV head) quantizes the K page, then the V
+// page, through the same LDS staging (the barrier between them keeps the K
+// block's copy-out ahead of the V block's first LDS writes). Measured
+// against one workgroup per page of one kind (twice the grid): 150-154 us
+// instead of 161 us (NVFP4) and 147 us instead of 158 us (MXFP4) for
+// 131,072 tokens x 8 heads, with bit-identical output.
 // At least 3 (MXFP4) / 4 (NVFP4) waves per SIMD: the MXFP4 body would take
 // 171 VGPRs (2 waves) unbounded and fits 168 without spilling; NVFP4 fits
 // 4 waves as it is (at 5 it would spill).
@@ -237,13 +243,15 @@ writer_kernel(WriterArgs a) {
   __shared__ __align__(16) uint8_t s_scales[1024];
   __shared__ __align__(16) float tbuf[kChan ? 4 * 16 * kD : 4];
   const int ph = blockIdx.x;       // input page * hkv + head
-  const bool is_v = blockIdx.y != 0;
   const int in_page = ph / a.hkv, h = ph - in_page * a.hkv;
   const int dst = a.page_ids[in_page];
   if (dst < 0 || dst >= a.num_pages) return;
-  const WriterRows rows{is_v ? a.v : a.k, in_page, a.hkv, h};
-  if (is_v) page_head<kKMode, kVMode, true, kChan>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales, tbuf);
-  else page_head<kKMode, kVMode, false, kChan>(a, rows, h, (size_t)dst * a.hkv + h, s_codes, s_scales, tbuf);
+  const size_t blk = (size_t)dst * a.hkv + h;
+  const WriterRows krows{a.k, in_page, a.hkv, h};
+  page_head<kKMode, kVMode, false, kChan>(a, krows, h, blk, s_codes, s_scales, tbuf);
+  __syncthreads();
+  const WriterRows vrows{a.v, in_page, a.hkv, h};
+  page_head<kKMode, kVMode, true, kChan>(a, vrows, h, blk, s_codes, s_scales, tbuf);
 }
 
 // Decode-time append with freeze-at-fill ("kv-landlords scripts/quant_ab.py"
@@ -458,7 +466,7 @@ static WriterArgs writer_args(const WriterLaunch& L) {
 hipError_t launch_writer(const WriterLaunch& L, hipStream_t stream) {
   if (L.n_pages == 0) return hipSuccess;
   const WriterArgs a = writer_args(L);
-  const dim3 grid((unsigned)(L.n_pages * L.hkv), 2u), block(256u);
+  const dim3 grid((unsigned)(L.n_pages * L.hkv)), block(256u);
   if (L.k_chan && L.k_mode == 2 && L.v_mode == 1)
     hipLaunchKernelGGL((writer_kernel<2, 1, true>), grid, block, 0, stream, a);
   else if (L.k_chan && L.k_mode == 1 && L.v_mode == 1)
