@@ -167,8 +167,10 @@ def build_layers(args, arms):
     rec = {"nvfp4": bd.recipe_default_nvfp4(tau=1.0), "mxfp4": bd.recipe_default_mxfp4(tau=1.0)}
     L = args.context
     ppp, parts = bd.decode_plan(1, 8, L, args.ppp)
+    # the BF16-KV arm in its own automatic plan (about 512 workgroups)
+    ppp_arm = {a: bd.bf16_decode_plan(1, 8, L, 0)[0] if a == "bf16" else ppp for a in arms}
     layers = {a: [] for a in arms}
-    ws = {a: bd.alloc_workspace(bd.decode_workspace_size(1, 32, 8, L, ppp)) for a in arms}
+    ws = {a: bd.alloc_workspace(bd.decode_workspace_size(1, 32, 8, L, ppp_arm[a])) for a in arms}
     outs = {a: torch.empty((1, 32, 128), dtype=torch.float32, device="cuda") for a in arms}
     for layer in range(args.layers):
         d = synth.torch_decode_layer(layer, seq_len=L)
@@ -183,8 +185,8 @@ def build_layers(args, arms):
             else:
                 kp = synth.bf16_pages_from_tokens(d["k"], d["block_tables"], d["num_pages"])
                 vp = synth.bf16_pages_from_tokens(d["v"], d["block_tables"], d["num_pages"])
-                call = bd.Bf16DecodeCall(d["q"], kp, vp, d["block_tables"], d["seq_lens"], L, d["sigma"], ppp,
-                                         ws[a], outs[a])
+                call = bd.Bf16DecodeCall(d["q"], kp, vp, d["block_tables"], d["seq_lens"], L, d["sigma"],
+                                         ppp_arm[a], ws[a], outs[a])
             layers[a].append(call)
         del d
         torch.cuda.synchronize()
@@ -612,6 +614,9 @@ def main():
                   "us_kernel_events_p90": LAST_PERCENTILES["p90"] * 1e3, "wall_ms_per_step": wall,
                   "bytes_per_layer": nb, "GBps": nb * args.layers / (ms * 1e-3) / 1e9,
                   "kernel_GBps": nb / (per * 1e-3) / 1e9}
+        if a == "bf16":
+            import fp4_kv_cache_nvfp4_amd as bd
+            res[a]["pages_per_partition"] = bd.bf16_decode_plan(1, 8, args.context, 0)[0]
         print(f"[bench] {a}: {ms * 1e3:.1f} us/step, {res[a]['GBps']:.0f} GB/s, kernel "
               f"{per * 1e3:.2f} us ({res[a]['kernel_GBps']:.0f} GB/s)", file=sys.stderr, flush=True)
     del layers

@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
         "bdfp4_page_errors_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_page_errors": [RP, CP, P, P, P, I32, P, P, SZ, P, P],
         "bdfp4_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
+        "bdfp4_bf16_decode_plan": [I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
         "bdfp4_decode_workspace_size": [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "bdfp4_decode_attention": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, SZ, P, P],
         "bdfp4_decode_attention_noalloc": [RP, CP, P, I32, I32, P, I32, P, I32, P, P, P, P, P, F32, I32, P, P],
@@ -319,6 +320,13 @@ def decode_plan(batch: int, num_kv_heads: int, max_seq_len: int, pages_per_parti
     ppp, parts = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().bdfp4_decode_plan(batch, num_kv_heads, max_seq_len, pages_per_partition,
                                    ctypes.byref(ppp), ctypes.byref(parts)))
+    return ppp.value, parts.value
+
+
+def bf16_decode_plan(batch: int, num_kv_heads: int, max_seq_len: int, pages_per_partition: int = 0):
+    ppp, parts = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().bdfp4_bf16_decode_plan(batch, num_kv_heads, max_seq_len, pages_per_partition,
+                                        ctypes.byref(ppp), ctypes.byref(parts)))
     return ppp.value, parts.value
 
 

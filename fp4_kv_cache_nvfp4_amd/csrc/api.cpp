@@ -164,17 +164,53 @@ int32_t auto_ppp(int32_t batch, int32_t hkv, int32_t max_seq_len) {
 
 constexpr int32_t kMaxPpp = 4;   // a partition is one wave's pages; its logits sit in LDS
 
-bdfp4_status plan(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_in, int32_t* ppp,
-                  int32_t* parts) {
+// The BF16-KV decode's plan: every page of a sequence is read (the partial
+// last one included) and a workgroup's partition is split over its 4 waves,
+// up to 16 pages (its logits sit in LDS). Measured on the MI355X for one
+// sequence x 8 KV heads, the best value is the one that gives about 512
+// workgroups (8K: 1-2 pages, 32K: 4, 64K: 8, 128K: 16; at 128K 16 pages take
+// 108 us against 129 us for 4, whose 2,048 workgroups run in 2.7 rounds and
+// merge 256 partials per head).
+constexpr int32_t kMaxPppBf16 = 16;
+
+int32_t auto_ppp_bf16(int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  const int64_t pages = ((int64_t)max_seq_len + 127) / 128;
+  const int64_t work = (int64_t)batch * hkv * pages;      // page-heads
+  int64_t ppp = (work + 511) / 512;                       // about 512 workgroups
+  if (ppp < 1) ppp = 1;
+  if (ppp > kMaxPppBf16) ppp = kMaxPppBf16;
+  return (int32_t)ppp;
+}
+
+bdfp4_status plan_checks(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_in, int32_t max_ppp) {
   if (batch < 1 || hkv < 1) return fail(BDFP4_E_INVALID, "batch and num_kv_heads must be positive");
   if (max_seq_len < 1) return fail(BDFP4_E_INVALID, "max_seq_len must be positive");
-  if (ppp_in < 0 || ppp_in > kMaxPpp)
-    return fail(BDFP4_E_INVALID, "pages_per_partition must be in [0, %d], got %d", kMaxPpp, ppp_in);
+  if (ppp_in < 0 || ppp_in > max_ppp)
+    return fail(BDFP4_E_INVALID, "pages_per_partition must be in [0, %d], got %d", max_ppp, ppp_in);
   if ((int64_t)batch * hkv > bdfp4::kMaxSeqHeads)
     return fail(BDFP4_E_UNSUPPORTED, "batch * num_kv_heads must be <= %d", bdfp4::kMaxSeqHeads);
+  return BDFP4_OK;
+}
+
+// FP4 decode plan: partitions of full pages.
+bdfp4_status plan(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_in, int32_t* ppp,
+                  int32_t* parts) {
+  const bdfp4_status s = plan_checks(batch, hkv, max_seq_len, ppp_in, kMaxPpp);
+  if (s != BDFP4_OK) return s;
   *ppp = ppp_in ? ppp_in : auto_ppp(batch, hkv, max_seq_len);
   const int32_t n_full = max_seq_len / 128;
   *parts = (n_full + *ppp - 1) / *ppp;
+  return BDFP4_OK;
+}
+
+// BF16-KV decode plan: partitions of all pages.
+bdfp4_status plan_bf16(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t ppp_in, int32_t* ppp,
+                       int32_t* parts) {
+  const bdfp4_status s = plan_checks(batch, hkv, max_seq_len, ppp_in, kMaxPppBf16);
+  if (s != BDFP4_OK) return s;
+  *ppp = ppp_in ? ppp_in : auto_ppp_bf16(batch, hkv, max_seq_len);
+  const int32_t pages = (max_seq_len + 127) / 128;
+  *parts = (pages + *ppp - 1) / *ppp;
   return BDFP4_OK;
 }
 
@@ -465,15 +501,30 @@ bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads, int32_t max_
   return s == BDFP4_OK ? ok() : s;
 }
 
+bdfp4_status bdfp4_bf16_decode_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                    int32_t pages_per_partition, int32_t* ppp_out, int32_t* parts_out) {
+  if (!ppp_out || !parts_out) return fail(BDFP4_E_INVALID, "NULL output");
+  bdfp4_status s = plan_bf16(batch, num_kv_heads, max_seq_len, pages_per_partition, ppp_out, parts_out);
+  return s == BDFP4_OK ? ok() : s;
+}
+
 bdfp4_status bdfp4_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t max_seq_len, int32_t pages_per_partition, size_t* bytes) {
   if (!bytes) return fail(BDFP4_E_INVALID, "NULL output");
   if (num_q_heads != bdfp4::kGroup * num_kv_heads)
     return fail(BDFP4_E_UNSUPPORTED, "num_q_heads must be 4 * num_kv_heads");
-  int32_t ppp, parts;
-  bdfp4_status s = plan(batch, num_kv_heads, max_seq_len, pages_per_partition, &ppp, &parts);
+  int32_t ppp, parts, ppp_b, parts_b;
+  bdfp4_status s = plan_bf16(batch, num_kv_heads, max_seq_len, pages_per_partition, &ppp_b, &parts_b);
   if (s != BDFP4_OK) return s;
-  *bytes = workspace_bytes(batch, num_kv_heads, max_seq_len, ppp);
+  size_t need = workspace_bytes(batch, num_kv_heads, max_seq_len, ppp_b);
+  if (pages_per_partition <= kMaxPpp) {
+    // 0: both decodes' automatic plans; 1 .. 4: a plan either decode accepts
+    s = plan(batch, num_kv_heads, max_seq_len, pages_per_partition, &ppp, &parts);
+    if (s != BDFP4_OK) return s;
+    const size_t fp4 = workspace_bytes(batch, num_kv_heads, max_seq_len, ppp);
+    if (fp4 > need) need = fp4;
+  }
+  *bytes = need;
   return ok();
 }
 
@@ -481,10 +532,11 @@ static bdfp4_status check_decode_common(const void* q, int32_t batch, int32_t hq
                                         const int32_t* block_tables, int32_t max_pages_per_seq,
                                         const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
                                         int32_t ppp_in, void* workspace, size_t workspace_bytes_in,
-                                        float* out, int32_t* ppp, int32_t* parts) {
+                                        float* out, int32_t* ppp, int32_t* parts, bool bf16 = false) {
   if (hq != bdfp4::kGroup * hkv)
     return fail(BDFP4_E_UNSUPPORTED, "num_q_heads must be 4 * num_kv_heads (got %d, %d)", hq, hkv);
-  bdfp4_status s = plan(batch, hkv, max_seq_len, ppp_in, ppp, parts);
+  bdfp4_status s = bf16 ? plan_bf16(batch, hkv, max_seq_len, ppp_in, ppp, parts)
+                        : plan(batch, hkv, max_seq_len, ppp_in, ppp, parts);
   if (s != BDFP4_OK) return s;
   if (!q || !block_tables || !seq_lens || !out) return fail(BDFP4_E_INVALID, "NULL input or output pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(BDFP4_E_INVALID, "q and out must be 16-byte aligned");
@@ -643,7 +695,8 @@ bdfp4_status bdfp4_bf16_decode_attention(const void* q_bf16, int32_t batch, int3
   int32_t ppp, parts;
   bdfp4_status s = check_decode_common(q_bf16, batch, num_q_heads, num_kv_heads, block_tables,
                                        max_pages_per_seq, seq_lens, max_seq_len, softmax_scale,
-                                       pages_per_partition, workspace, workspace_bytes_in, out, &ppp, &parts);
+                                       pages_per_partition, workspace, workspace_bytes_in, out, &ppp, &parts,
+                                       true);
   if (s != BDFP4_OK) return s;
   if (!k_pages || !v_pages) return fail(BDFP4_E_INVALID, "NULL page pointer");
   if (!aligned16(k_pages) || !aligned16(v_pages)) return fail(BDFP4_E_INVALID, "pages must be 16-byte aligned");

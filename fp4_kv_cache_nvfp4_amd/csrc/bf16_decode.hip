@@ -1,7 +1,8 @@
 // BF16-KV paged decode attention for gfx950: the unquantized baseline arm
 // (kv_cache_dtype "auto" in the KV_MODES of "BitDecoding-FP4
-// evaluation/config.py"), with the same split-K plan and merge as the FP4
-// decode so the two are measured under the same launch structure.
+// evaluation/config.py"), with the same split-K partials and merge as the FP4
+// decode and a plan of its own (up to 16 pages per partition, about 512
+// workgroups: a BF16 page is 4.5 times the bytes of an NVFP4 one).
 //
 // Pages are bf16 [page][KV head][128 tokens][128 channels]. One workgroup (4
 // waves) per (sequence, KV head, partition of pages_per_partition pages):

@@ -278,11 +278,26 @@ bdfp4_status bdfp4_decode_plan(int32_t batch, int32_t num_kv_heads,
                                int32_t* pages_per_partition_out,
                                int32_t* max_partitions_out);
 
+/* Split plan of bdfp4_bf16_decode_attention (host). pages_per_partition
+ * (1 .. 16) is the number of consecutive pages, the partial last one
+ * included, that one workgroup covers (its 4 waves share them); 0 picks
+ * ceil(batch * num_kv_heads * ceil(max_seq_len / 128) / 512), at most 16:
+ * about 512 workgroups, the fastest grid measured on the MI355X (one
+ * resident round). The chosen value and the number of partitions of the
+ * longest sequence are returned. */
+bdfp4_status bdfp4_bf16_decode_plan(int32_t batch, int32_t num_kv_heads,
+                                    int32_t max_seq_len, int32_t pages_per_partition,
+                                    int32_t* pages_per_partition_out,
+                                    int32_t* max_partitions_out);
+
 /* Workspace bytes for bdfp4_decode_attention / bdfp4_bf16_decode_attention
  * with these sizes (host output): a fixed ticket region of
  * 16384 * 4 bytes (the same for every call shape), then
  * batch * num_kv_heads * (P + 2) partial slots of 2080 bytes, where
- * P = ceil(ceil(max_seq_len / 128) / pages_per_partition). The workspace must
+ * P = ceil(ceil(max_seq_len / 128) / pages_per_partition).
+ * pages_per_partition 0 sizes for the larger of the two decodes' automatic
+ * plans, 1 .. 4 for that value (either decode), 5 .. 16 for the BF16 decode
+ * with that value. The workspace must
  * be zero-filled once after it is allocated; every call leaves its ticket
  * words zero again, so a buffer can be reused by calls of any shape (and
  * captured in a graph) without clearing. After a call that did not complete
@@ -373,8 +388,9 @@ bdfp4_status bdfp4_decode_attention_logits(
 
 /* BF16-KV paged decode (the unquantized baseline arm, kv_cache_dtype "auto"
  * in KV_MODES): exact softmax attention over all L tokens of BF16 pages
- * k_pages / v_pages [num_pages][num_kv_heads][128][128], same split plan and
- * workspace rules as bdfp4_decode_attention. */
+ * k_pages / v_pages [num_pages][num_kv_heads][128][128], split as
+ * bdfp4_bf16_decode_plan says (pages_per_partition 0 .. 16), with the
+ * workspace rules of bdfp4_decode_attention. */
 bdfp4_status bdfp4_bf16_decode_attention(
     const void* q_bf16, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     const void* k_pages, const void* v_pages, int32_t num_pages,

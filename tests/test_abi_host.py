@@ -125,6 +125,31 @@ def test_sizes_and_plan():
         assert ei.value.status == bd.E_INVALID
 
 
+def test_bf16_plan_and_workspace():
+    # the BF16-KV decode's own plan: about 512 workgroups, up to 16 pages
+    # (the partial last page counted) per partition
+    assert [bd.bf16_decode_plan(1, 8, L, 0) for L in (8192, 32768, 65536, 131072)] == \
+        [(1, 64), (4, 64), (8, 64), (16, 64)]
+    assert bd.bf16_decode_plan(1, 8, 131072 + 77, 0) == (16, 65)
+    assert bd.bf16_decode_plan(16, 8, 16384, 0) == (16, 8)
+    assert bd.bf16_decode_plan(5, 2, 2100, 0) == (1, 17)
+    assert bd.bf16_decode_plan(1, 1, 100, 16) == (16, 1)
+    for args in [(1, 8, 1000, 17), (1, 8, 1000, -1), (0, 8, 1000, 0)]:
+        with pytest.raises(bd.Bdfp4Error) as ei:
+            bd.bf16_decode_plan(*args)
+        assert ei.value.status == bd.E_INVALID
+    # 0 sizes for both automatic plans (the FP4 one needs more here), 5 .. 16
+    # for the BF16 decode alone
+    assert bd.decode_workspace_size(1, 32, 8, 131072, 0) == 16384 * 4 + 8 * (256 + 2) * 520 * 4
+    assert bd.decode_workspace_size(1, 32, 8, 131072, 16) == 16384 * 4 + 8 * (64 + 2) * 520 * 4
+    assert bd.decode_workspace_size(1, 32, 8, 131072 + 77, 16) == 16384 * 4 + 8 * (65 + 2) * 520 * 4
+    for L in (100, 2048, 8192, 32768 + 77, 131072):
+        for b, h in ((1, 1), (1, 8), (16, 8)):
+            auto = bd.decode_workspace_size(b, 4 * h, h, L, 0)
+            assert auto >= bd.decode_workspace_size(b, 4 * h, h, L, bd.bf16_decode_plan(b, h, L, 0)[0])
+            assert auto >= bd.decode_workspace_size(b, 4 * h, h, L, bd.decode_plan(b, h, L, 0)[0])
+
+
 def _cache(**kw):
     c = bd.Cache(FAKE, FAKE, FAKE, FAKE, 16, 1, 128, 128)
     for k, v in kw.items():

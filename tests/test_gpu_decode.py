@@ -216,7 +216,7 @@ def test_end_to_end_writer_then_decode(r):
     assert_close(gpu_decode(r, wl, cache, 4), ref, "end to end")
 
 
-@pytest.mark.parametrize("ppp", [1, 4])
+@pytest.mark.parametrize("ppp", [1, 4, 8, 16, 0])
 def test_bf16_baseline(ppp):
     wl = synth.decode_workload("b", 13, [1, 127, 128, 1000, 2100], 8, 2, "qwen", extra_pages=2)
     kp, vp = wl.bf16_pages()
@@ -250,6 +250,26 @@ def test_full_128k_layer(r):
     sk, sv, tk, tv = wl.sink_tail()
     ref = OD.decode(r, cache, wl.q, wl.block_tables, wl.seq_lens, sk, sv, tk, tv, wl.key_shift, wl.sigma, ppp)
     assert_close(got, ref, "128k layer, all 8 KV heads")
+
+
+def test_bf16_full_128k_layer():
+    """The BF16-KV arm on the benchmark's 128K layer in its own automatic
+    plan (16 pages per partition: 64 workgroups per KV head, 512 in all);
+    every one of the 32 output rows against the oracle's exact attention."""
+    L = 131072
+    print("[128k layer] bf16", flush=True)
+    wl = synth.decode_workload("full128k", 11, [L], 32, 8, "qwen")
+    ppp, parts = bd.bf16_decode_plan(1, 8, L, 0)
+    assert (ppp, parts) == (16, 64)
+    kp, vp = wl.bf16_pages()
+    ref = OD.bf16_decode(wl.q, kp, vp, wl.block_tables, wl.seq_lens, wl.sigma)
+    ws = bd.alloc_workspace(bd.decode_workspace_size(1, 32, 8, L, 0))
+    out = torch.full((1, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    bd.bf16_decode_attention(dev_bf16(wl.q), dev_bf16(kp), dev_bf16(vp), dev(wl.block_tables),
+                             dev(wl.seq_lens), L, wl.sigma, 0, ws, out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), ref, "bf16 128k layer, auto plan")
+    assert not ws[:65536].any()
 
 
 @pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
