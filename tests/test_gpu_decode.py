@@ -306,6 +306,44 @@ def test_batched_16_sequences():
     assert_close(got, ref, f"batched 16 x 2k..16k ppp={ppp}, every sequence")
 
 
+def test_max_sequence_heads():
+    """The largest call the library takes: 2,048 sequences x 8 KV heads =
+    16,384 (sequence, KV head) pairs, every ticket word in use. Most
+    sequences are shorter than a page (the BF16 partition alone), 64 hold
+    1-4 full pages, 16 hold 17-23 (two FP4 workgroups of the plan's 4 pages
+    per partition, so tickets and the merge run at the top of the ticket
+    region). The FP4 and the BF16-KV decode against the oracle on every
+    sequence, and the ticket words are zero again after each call."""
+    print("[max sequence heads] 2048 x 8", flush=True)
+    rng = np.random.Generator(np.random.PCG64(2048))
+    lens = np.concatenate([rng.integers(1, 128, 1968), rng.integers(128, 601, 64), rng.integers(2200, 3001, 16)])
+    lens = lens[rng.permutation(lens.size)].astype(np.int32)
+    wl = synth.decode_workload("max_seq_heads", 29, lens, 32, 8, "qwen")
+    assert wl.batch * wl.num_kv_heads == 16384
+    ppp, parts = bd.decode_plan(wl.batch, 8, int(lens.max()), 0)
+    assert (ppp, parts) == (4, 6)
+    ref = oracle_decode(NV, wl, oracle_write(NV, wl), ppp)
+    ws = bd.alloc_workspace(bd.decode_workspace_size(wl.batch, 32, 8, int(lens.max()), 0))
+    cache = gpu_write(NV, wl)
+    sk, sv, tk, tv = wl.sink_tail()
+    out = torch.full((wl.batch, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    bd.decode_attention(to_c(NV), cache, dev_bf16(wl.q), dev(wl.block_tables), dev(wl.seq_lens), int(lens.max()),
+                        dev_bf16(sk), dev_bf16(sv), dev_bf16(tk), dev_bf16(tv), dev(wl.key_shift), wl.sigma, ppp,
+                        ws, out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), ref, "16,384 (sequence, KV head) pairs")
+    assert not ws[:65536].any()
+    kp, vp = wl.bf16_pages()
+    ref16 = OD.bf16_decode(wl.q, kp, vp, wl.block_tables, wl.seq_lens, wl.sigma)
+    assert bd.bf16_decode_plan(wl.batch, 8, int(lens.max()), 0) == (16, 2)
+    out.fill_(float("nan"))
+    bd.bf16_decode_attention(dev_bf16(wl.q), dev_bf16(kp), dev_bf16(vp), dev(wl.block_tables), dev(wl.seq_lens),
+                             int(lens.max()), wl.sigma, 0, ws, out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), ref16, "bf16, 16,384 (sequence, KV head) pairs")
+    assert not ws[:65536].any()
+
+
 def test_p_flips_from_float32_logits():
     """P code and scale flips: the decode's own float32 logits
     (bdfp4_decode_attention_logits) and the oracle's float64 logits, both
