@@ -520,6 +520,29 @@ __device__ __forceinline__ void load_v(VPage& v, const DecodeLaunch& P, size_t b
   }
 }
 
+// Half h of an NVFP4 K page (tiles 4 h .. 4 h + 3, and the page's scales) or
+// V page (chunks 2 h, 2 h + 1 and their scales) into the page buffer, for the
+// half-page stream of fp4_wg; the other half of the buffer is never written
+// or read, so it takes no registers.
+__device__ __forceinline__ void load_k_half(KPage& k, const DecodeLaunch& P, size_t blk, int lane, int half) {
+  const uint4* kc = reinterpret_cast<const uint4*>(P.k_codes + blk * 8192) + lane;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) k.code[4 * half + t] = kc[(4 * half + t) * 64];
+  k.sc = *reinterpret_cast<const uint4*>(P.k_scales + blk * 1024 + lane * 16);
+}
+__device__ __forceinline__ void load_v_half(VPage& v, const DecodeLaunch& P, size_t blk, int lane, int half) {
+  const uint4* vc = reinterpret_cast<const uint4*>(P.v_codes + blk * 8192 + lane * 32);
+  const int kg = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    const int c = 2 * half + cc;
+    v.code[2 * c] = vc[c * 128];
+    v.code[2 * c + 1] = vc[c * 128 + 1];
+    const int sidx = ((c * 4 + kg) * 8 + (n >> 1)) * 8;
+    v.sc[c] = *reinterpret_cast<const uint2*>(P.v_scales + blk * 1024 + sidx);
+  }
+}
+
 // ------------------------------------------------------------ FP4 partitions
 
 __device__ __forceinline__ uint32_t umax_dpp8(uint32_t v) {
@@ -596,13 +619,14 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
   // The wave reads a stream of 2 kSlots slots, K pages 0..kSlots-1 then V
-  // pages 0..kSlots-1, keeping the next slot in flight while one is used:
+  // pages 0..kSlots-1 (for NVFP4 with 4 slots, kHalf: half pages, 16 slots,
+  // see there), keeping the next slot in flight while one is used:
   // K page i lands in kb[i % 2], V page j in vb[j % 2], and the load of a
   // slot is issued once the slot two before it (same buffer) has been used
   // (with one page per partition, K and V page 0 are both requested at the
-  // start). One page in flight per wave measured faster than two: with
-  // 8 waves per CU the memory pipe is already full, and deeper queues only
-  // delay the waves dispatched second. The loads are unconditional (a slot
+  // start). One page in flight per wave measured faster than two, and half
+  // a page (kHalf) faster still: with 8 waves per CU the memory pipe is
+  // already full, and deeper queues only delay the waves dispatched second. The loads are unconditional (a slot
   // of a page past npg, in the partition that ends the sequence, reads
   // physical page 0, which always exists, and is never used) so the compiler
   // can count the loads in flight exactly and wait only for the slot about
@@ -613,14 +637,19 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   // requests its first K pages, so that waiting for the partition's rows
   // does not also wait for those pages (every workgroup of the grid requests
   // its first pages at once, and they take several µs to drain)
+  constexpr bool kHalf = kSlots == 4 && !kMx && !kChan;
   Partial bfp;
   if (bf16) {
     bfp = bf16_partition(A, sm, b, h, L, n_full);
-    load_k<kMx>(kb0, P, blk_of(0), lane);
+    if constexpr (kHalf) load_k_half(kb0, P, blk_of(0), lane, 0);
+    else load_k<kMx>(kb0, P, blk_of(0), lane);
   } else {
-    load_k<kMx>(kb0, P, blk_of(0), lane);
+    if constexpr (kHalf) load_k_half(kb0, P, blk_of(0), lane, 0);
+    else load_k<kMx>(kb0, P, blk_of(0), lane);
   }
-  if constexpr (kSlots == 1)
+  if constexpr (kHalf)
+    load_k_half(kb1, P, blk_of(0), lane, 1);
+  else if constexpr (kSlots == 1)
     load_v<kMx>(vb0, P, blk_of(0), lane);
   else
     load_k<kMx>(kb1, P, blk_of(1), lane);
@@ -669,7 +698,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   // whole 16-token tiles of the sequence's first page; those tiles get -inf.
   const int sink_tiles = p0 == 0 ? P.sink / 16 : 0;
   float ma = kNegInf, mb = kNegInf;
-  auto k_page = [&](const KPage& cur, int pi) {
+  auto k_page = [&](const KPage& cur, int pi, int t_lo = 0, int t_hi = 8) {
     const int skip = pi == 0 ? sink_tiles : 0;                  // uniform
     float pa = kNegInf, pb = kNegInf;
     // channel key geometry: the page's 1 KiB of scales, [token block][channel],
@@ -677,7 +706,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     // 32 scales of its lanes' channels 32 kg .. +32 from block t
     if (kChan) reinterpret_cast<uint4*>(&sm.ksc[wave][0])[lane] = cur.sc;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = t_lo; t < t_hi; ++t) {
       const int local = pi * kPage + t * 16;                    // first token of the tile - 128 p0
       u32x4_t bk[4];
       f32x4_t acc = acc0;
@@ -744,6 +773,22 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     load_v<kMx>(vb0, P, blk_of(0), lane);
     if (npg > 1) k_page(kb1, 1);
     load_v<kMx>(vb1, P, blk_of(1), lane);
+  } else if constexpr (kHalf) {
+    // half pages: slot 2 p + h is half h of K page p (buffer kb_h), then
+    // half h of V page p (vb_h); the load of a slot follows the use of the
+    // slot two before it, in the same buffer. Against whole pages this holds
+    // one page of K and V at a time instead of two (160 against 167 VGPRs),
+    // the room the compacted grid needs, and measured 0.4-0.8 us faster at
+    // 128K (bit-identical output).
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (npg > p) k_page(kb0, p, 0, 4);
+      if (p < 3) load_k_half(kb0, P, blk_of(p + 1), lane, 0);
+      else load_v_half(vb0, P, blk_of(0), lane, 0);
+      if (npg > p) k_page(kb1, p, 4, 8);
+      if (p < 3) load_k_half(kb1, P, blk_of(p + 1), lane, 1);
+      else load_v_half(vb1, P, blk_of(0), lane, 1);
+    }
   } else {
     if (npg > 0) k_page(kb0, 0);
     load_k<kMx>(kb0, P, blk_of(2), lane);
@@ -781,9 +826,9 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   f32x4_t acco[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acco[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  auto v_page = [&](const VPage& vcur, int pi) {
+  auto v_page = [&](const VPage& vcur, int pi, int c_lo = 0, int c_hi = 4) {
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = c_lo; ch < c_hi; ++ch) {
       // p' = c exp(sigma (t - m)) of tokens 2 pj, 2 pj + 1 of the chunk, head ph
       const float2 tt = *reinterpret_cast<const float2*>(lrow + pi * kPage + ch * 32);
       // the reference maximum: the partition's, or (running-max variant) the
@@ -869,6 +914,14 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   } else if constexpr (kSlots == 2) {
     if (npg > 0) v_page(vb0, 0);
     if (npg > 1) v_page(vb1, 1);
+  } else if constexpr (kHalf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (npg > p) v_page(vb0, p, 0, 2);
+      if (p < 3) load_v_half(vb0, P, blk_of(p + 1), lane, 0);
+      if (npg > p) v_page(vb1, p, 2, 4);
+      if (p < 3) load_v_half(vb1, P, blk_of(p + 1), lane, 1);
+    }
   } else {
     if (npg > 0) v_page(vb0, 0);
     load_v<kMx>(vb0, P, blk_of(2), lane);
@@ -958,8 +1011,60 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   return r;
 }
 
+// FP4 workgroups of a sequence of length L (0 for an invalid length, whose
+// rows column 0 poisons, or for a sequence without a full page).
+__device__ __forceinline__ int seq_fp4_wgs(const DecodeLaunch& P, int L) {
+  if (L < 1 || L > P.max_seq_len || L / kPage > P.max_pages_per_seq) return 0;
+  const int n_full = L / kPage;
+  return n_full > 0 ? fp4_wgs((n_full + P.ppp - 1) / P.ppp) : 0;
+}
+// A compacted launch: the grid of every (sequence, KV head, column) is
+// larger than the chip holds at once. Workgroups are dispatched in index
+// order, and a slot that a workgroup without work frees is not taken by the
+// next one until workgroups with work end, so the columns that only the
+// longest sequences have would start late and end the launch (measured on
+// the batch of 16: columns 6-7 entered at 2-35 us). Workgroup j instead
+// serves the j-th unit with work, as the virtual index col * B Hkv + bh that
+// an uncompacted grid would give it: column 0 for every sequence (it also
+// computes the BF16 partition, or the NaN rows of an invalid sequence), then
+// column c >= 1 for each sequence with more than c FP4 workgroups, in
+// sequence order, KV head j mod Hkv (so a head's workgroups keep their place
+// in the dispatch rotation). Every wave computes the same mapping from the
+// sequence lengths (up to kCompactChunks x 64 sequences, in registers).
+// Returns -1 for a workgroup past the units with work.
+constexpr int kCompactChunks = 4;
+__device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
+  const int lane = threadIdx.x & 63;
+  const int BH = P.batch * P.hkv;
+  int u = j / P.hkv;
+  const int h = j - u * P.hkv;
+  if (u < P.batch) return j;
+  u -= P.batch;
+  int nw[kCompactChunks];
+#pragma unroll
+  for (int k = 0; k < kCompactChunks; ++k) {
+    const int b = 64 * k + lane;
+    nw[k] = b < P.batch ? seq_fp4_wgs(P, P.seq_lens[b]) : 0;
+  }
+  const int wgs = fp4_wgs(P.max_parts);
+  for (int c = 1; c < wgs; ++c) {
+#pragma unroll
+    for (int k = 0; k < kCompactChunks; ++k) {
+      const uint64_t m = __ballot(nw[k] > c);
+      const int cnt = __popcll(m);
+      if (u < cnt) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const uint64_t pick = __ballot(nw[k] > c && below == u);
+        return c * BH + (64 * k + __builtin_ctzll(pick)) * P.hkv + h;
+      }
+      u -= cnt;
+    }
+  }
+  return -1;
+}
+
 // Workgroup j works for (sequence, KV head) bh = j % (B Hkv) in grid column
-// c = j / (B Hkv). A launch whose grid has room for one more column
+// c = j / (B Hkv) (j the virtual index of compact_vj in a compacted launch). A launch whose grid has room for one more column
 // (split_bf16: it still fits the chip at two workgroups per compute unit)
 // gives every BF16 partition (sink + tail) a workgroup of its own in column
 // 0, the first B Hkv workgroups of the grid (dispatched first), which runs
@@ -981,7 +1086,12 @@ decode_kernel(DecArgs A) {
   const DecodeLaunch& P = A.L;
   const MergeCtx C = merge_ctx(A);
   const int BH = P.batch * P.hkv;
-  const int bh = (int)blockIdx.x % BH, col = (int)blockIdx.x / BH;
+  int vj = (int)blockIdx.x;                                // grid position (compacted: of the j-th unit with work)
+  if (P.compact) {
+    vj = __builtin_amdgcn_readfirstlane(compact_vj(P, vj));
+    if (vj < 0) return;
+  }
+  const int bh = vj % BH, col = vj / BH;
   const int b = bh / P.hkv, h = bh - b * P.hkv;
   const int split = P.split_bf16;                          // 0 or 1, uniform per launch
   const int sp = col - split;                              // FP4 workgroup of this column (-1: BF16)
@@ -1147,6 +1257,9 @@ static hipError_t launch_one(DecArgs A, int cus, hipStream_t stream) {
   const long long bh = (long long)A.L.batch * A.L.hkv;
   const int wgs = fp4_wgs(A.L.max_parts);
   A.L.split_bf16 = wgs >= 2 && bh * (wgs + 1) <= (long long)per_cu * cus ? 1 : 0;
+  // a grid the chip does not hold at once takes its units with work first
+  A.L.compact = !A.L.split_bf16 && wgs >= 2 && bh * wgs > (long long)per_cu * cus && A.L.batch <= 64 * kCompactChunks
+                    ? 1 : 0;
   // the FP4 workgroups of the longest sequence, after a column of BF16
   // partition workgroups when the launch has them
   const dim3 grid((unsigned)(bh * (wgs + A.L.split_bf16))), block(256u);

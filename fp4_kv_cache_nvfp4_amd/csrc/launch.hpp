@@ -89,6 +89,7 @@ struct DecodeLaunch {
   float* dbg_logits;      // debug: raw FP4-token logits [batch * hkv][4][dbg_stride], or null
   int32_t dbg_stride;
   int32_t split_bf16;     // the BF16 partitions of sequences with >= 2 FP4 workgroups get workgroups of their own
+  int32_t compact;        // a grid larger than the chip holds: workgroups take the units with work first
 };
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);

@@ -306,6 +306,37 @@ def test_batched_16_sequences():
     assert_close(got, ref, f"batched 16 x 2k..16k ppp={ppp}, every sequence")
 
 
+def test_compacted_grid():
+    """A batch whose grid of every (sequence, KV head, column) exceeds what the
+    chip holds at once (48 sequences x 8 KV heads x 3 columns against 768
+    resident workgroups), so the launch is compacted: workgroup j serves the
+    j-th unit with work. Sequences of every kind side by side: no full page
+    (the BF16 partition alone), one to three FP4 workgroups, an empty one, one
+    longer than max_seq_len and one whose block table names a page outside
+    the pool (their rows NaN); every other row against the oracle."""
+    print("[compacted grid] 48 x 8", flush=True)
+    rng = np.random.Generator(np.random.PCG64(96))
+    lens = rng.integers(1, 6000, 48).astype(np.int32)
+    lens[::11] = rng.integers(1, 128, lens[::11].size)
+    wl = synth.decode_workload("compact", 31, lens, 32, 8, "qwen", extra_pages=1)
+    ppp, parts = bd.decode_plan(48, 8, 6000, 0)
+    assert (ppp, parts) == (4, 12)                      # 3 FP4 workgroups per (sequence, KV head)
+    host = oracle_write(NV, wl)
+    ref = oracle_decode(NV, wl, host, ppp)
+    cache = cache_to_dev(NV, host, 8)
+    sl = wl.seq_lens.copy()
+    bt = wl.block_tables.copy()
+    victim = int([b for b in np.flatnonzero(sl >= 3 * 128) if b not in (5, 7)][2])
+    sl[5] = 0                                          # empty
+    sl[7] = 6500                                       # above max_seq_len
+    bt[victim, 2] = wl.num_pages + 7                   # a page outside the pool
+    got = gpu_decode(NV, wl, cache, ppp, max_seq_len=6000, seq_lens=sl, block_tables=bt)
+    bad = [5, 7, victim]
+    assert all(np.all(np.isnan(got[b])) for b in bad)
+    good = np.setdiff1d(np.arange(48), bad)
+    assert_close(got[good], ref[good], "compacted grid, 45 valid sequences")
+
+
 def test_max_sequence_heads():
     """The largest call the library takes: 2,048 sequences x 8 KV heads =
     16,384 (sequence, KV head) pairs, every ticket word in use. Most
