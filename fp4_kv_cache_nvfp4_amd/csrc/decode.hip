@@ -520,16 +520,23 @@ __device__ __forceinline__ void load_v(VPage& v, const DecodeLaunch& P, size_t b
   }
 }
 
-// Half h of an NVFP4 K page (tiles 4 h .. 4 h + 3, and the page's scales) or
-// V page (chunks 2 h, 2 h + 1 and their scales) into the page buffer, for the
+// Half h of a K page (tiles 4 h .. 4 h + 3, and the page's scales) or V page
+// (chunks 2 h, 2 h + 1 and their scales) into the page buffer, for the
 // half-page stream of fp4_wg; the other half of the buffer is never written
 // or read, so it takes no registers.
+template <bool kMx>
 __device__ __forceinline__ void load_k_half(KPage& k, const DecodeLaunch& P, size_t blk, int lane, int half) {
   const uint4* kc = reinterpret_cast<const uint4*>(P.k_codes + blk * 8192) + lane;
 #pragma unroll
   for (int t = 0; t < 4; ++t) k.code[4 * half + t] = kc[(4 * half + t) * 64];
-  k.sc = *reinterpret_cast<const uint4*>(P.k_scales + blk * 1024 + lane * 16);
+  if (kMx) {
+    const uint2 t2 = *reinterpret_cast<const uint2*>(P.k_scales + blk * 512 + lane * 8);
+    k.sc = make_uint4(t2.x, t2.y, 0u, 0u);
+  } else {
+    k.sc = *reinterpret_cast<const uint4*>(P.k_scales + blk * 1024 + lane * 16);
+  }
 }
+template <bool kMx>
 __device__ __forceinline__ void load_v_half(VPage& v, const DecodeLaunch& P, size_t blk, int lane, int half) {
   const uint4* vc = reinterpret_cast<const uint4*>(P.v_codes + blk * 8192 + lane * 32);
   const int kg = lane >> 4, n = lane & 15;
@@ -538,8 +545,8 @@ __device__ __forceinline__ void load_v_half(VPage& v, const DecodeLaunch& P, siz
     const int c = 2 * half + cc;
     v.code[2 * c] = vc[c * 128];
     v.code[2 * c + 1] = vc[c * 128 + 1];
-    const int sidx = ((c * 4 + kg) * 8 + (n >> 1)) * 8;
-    v.sc[c] = *reinterpret_cast<const uint2*>(P.v_scales + blk * 1024 + sidx);
+    const int sidx = kMx ? ((c * 4 + kg) * 4 + (n >> 2)) * 8 : ((c * 4 + kg) * 8 + (n >> 1)) * 8;
+    v.sc[c] = *reinterpret_cast<const uint2*>(P.v_scales + blk * (kMx ? 512 : 1024) + sidx);
   }
 }
 
@@ -619,8 +626,8 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
   // The wave reads a stream of 2 kSlots slots, K pages 0..kSlots-1 then V
-  // pages 0..kSlots-1 (for NVFP4 with 4 slots, kHalf: half pages, 16 slots,
-  // see there), keeping the next slot in flight while one is used:
+  // pages 0..kSlots-1 (with 4 slots, kHalf: half pages, 16 slots, see
+  // there), keeping the next slot in flight while one is used:
   // K page i lands in kb[i % 2], V page j in vb[j % 2], and the load of a
   // slot is issued once the slot two before it (same buffer) has been used
   // (with one page per partition, K and V page 0 are both requested at the
@@ -637,18 +644,18 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   // requests its first K pages, so that waiting for the partition's rows
   // does not also wait for those pages (every workgroup of the grid requests
   // its first pages at once, and they take several µs to drain)
-  constexpr bool kHalf = kSlots == 4 && !kMx && !kChan;
+  constexpr bool kHalf = kSlots == 4 && !kChan;           // half pages (see the stream below)
   Partial bfp;
   if (bf16) {
     bfp = bf16_partition(A, sm, b, h, L, n_full);
-    if constexpr (kHalf) load_k_half(kb0, P, blk_of(0), lane, 0);
+    if constexpr (kHalf) load_k_half<kMx>(kb0, P, blk_of(0), lane, 0);
     else load_k<kMx>(kb0, P, blk_of(0), lane);
   } else {
-    if constexpr (kHalf) load_k_half(kb0, P, blk_of(0), lane, 0);
+    if constexpr (kHalf) load_k_half<kMx>(kb0, P, blk_of(0), lane, 0);
     else load_k<kMx>(kb0, P, blk_of(0), lane);
   }
   if constexpr (kHalf)
-    load_k_half(kb1, P, blk_of(0), lane, 1);
+    load_k_half<kMx>(kb1, P, blk_of(0), lane, 1);
   else if constexpr (kSlots == 1)
     load_v<kMx>(vb0, P, blk_of(0), lane);
   else
@@ -777,17 +784,18 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     // half pages: slot 2 p + h is half h of K page p (buffer kb_h), then
     // half h of V page p (vb_h); the load of a slot follows the use of the
     // slot two before it, in the same buffer. Against whole pages this holds
-    // one page of K and V at a time instead of two (160 against 167 VGPRs),
-    // the room the compacted grid needs, and measured 0.4-0.8 us faster at
-    // 128K (bit-identical output).
+    // one page of K and V at a time instead of two (NVFP4 160 against 167
+    // VGPRs: the room the compacted grid needs; MXFP4 157 against 184: 3
+    // waves per SIMD instead of 2), and measured faster at 128K (NVFP4
+    // 0.4-0.8 us with bit-identical output, MXFP4 1.4-1.7 us).
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if (npg > p) k_page(kb0, p, 0, 4);
-      if (p < 3) load_k_half(kb0, P, blk_of(p + 1), lane, 0);
-      else load_v_half(vb0, P, blk_of(0), lane, 0);
+      if (p < 3) load_k_half<kMx>(kb0, P, blk_of(p + 1), lane, 0);
+      else load_v_half<kMx>(vb0, P, blk_of(0), lane, 0);
       if (npg > p) k_page(kb1, p, 4, 8);
-      if (p < 3) load_k_half(kb1, P, blk_of(p + 1), lane, 1);
-      else load_v_half(vb1, P, blk_of(0), lane, 1);
+      if (p < 3) load_k_half<kMx>(kb1, P, blk_of(p + 1), lane, 1);
+      else load_v_half<kMx>(vb1, P, blk_of(0), lane, 1);
     }
   } else {
     if (npg > 0) k_page(kb0, 0);
@@ -918,9 +926,9 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if (npg > p) v_page(vb0, p, 0, 2);
-      if (p < 3) load_v_half(vb0, P, blk_of(p + 1), lane, 0);
+      if (p < 3) load_v_half<kMx>(vb0, P, blk_of(p + 1), lane, 0);
       if (npg > p) v_page(vb1, p, 2, 4);
-      if (p < 3) load_v_half(vb1, P, blk_of(p + 1), lane, 1);
+      if (p < 3) load_v_half<kMx>(vb1, P, blk_of(p + 1), lane, 1);
     }
   } else {
     if (npg > 0) v_page(vb0, 0);
@@ -1079,8 +1087,12 @@ __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
 // partial, ticket or merge: the merge of a single partial is that quotient).
 // A sequence without a full page has only the BF16 partition, written
 // straight to the output by column 0.
+// At least 3 waves per SIMD (at most 168 VGPRs) for the kernels that fit
+// without spilling: every 4-slot kernel but the channel-scale one (half
+// pages) and the NVFP4 ones with 1 or 2 slots.
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMx || kChan || kRunMax ? 2 : 3)))
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(kChan || (kSlots != 4 && (kMx || kRunMax)) ? 2 : 3)))
 decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
