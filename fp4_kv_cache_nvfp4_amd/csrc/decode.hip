@@ -626,8 +626,9 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
   // The wave reads a stream of 2 kSlots slots, K pages 0..kSlots-1 then V
-  // pages 0..kSlots-1 (with 4 slots, kHalf: half pages, 16 slots, see
-  // there), keeping the next slot in flight while one is used:
+  // pages 0..kSlots-1 (kHalf, every kernel without channel key scales:
+  // half pages, 4 kSlots slots, see there), keeping the next slot in
+  // flight while one is used:
   // K page i lands in kb[i % 2], V page j in vb[j % 2], and the load of a
   // slot is issued once the slot two before it (same buffer) has been used
   // (with one page per partition, K and V page 0 are both requested at the
@@ -644,7 +645,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   // requests its first K pages, so that waiting for the partition's rows
   // does not also wait for those pages (every workgroup of the grid requests
   // its first pages at once, and they take several µs to drain)
-  constexpr bool kHalf = kSlots == 4 && !kChan;           // half pages (see the stream below)
+  constexpr bool kHalf = !kChan;                          // half pages (see the stream below)
   Partial bfp;
   if (bf16) {
     bfp = bf16_partition(A, sm, b, h, L, n_full);
@@ -773,30 +774,31 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   };
   static_assert(kMaxPpw == 4 && (kSlots == 1 || kSlots == 2 || kSlots == 4),
                 "the stream below is unrolled for 1, 2 or 4 pages");
-  if constexpr (kSlots == 1) {
-    if (npg > 0) k_page(kb0, 0);
-  } else if constexpr (kSlots == 2) {
-    if (npg > 0) k_page(kb0, 0);
-    load_v<kMx>(vb0, P, blk_of(0), lane);
-    if (npg > 1) k_page(kb1, 1);
-    load_v<kMx>(vb1, P, blk_of(1), lane);
-  } else if constexpr (kHalf) {
+  if constexpr (kHalf) {
     // half pages: slot 2 p + h is half h of K page p (buffer kb_h), then
     // half h of V page p (vb_h); the load of a slot follows the use of the
     // slot two before it, in the same buffer. Against whole pages this holds
     // one page of K and V at a time instead of two (NVFP4 160 against 167
     // VGPRs: the room the compacted grid needs; MXFP4 157 against 184: 3
     // waves per SIMD instead of 2), and measured faster at 128K (NVFP4
-    // 0.4-0.8 us with bit-identical output, MXFP4 1.4-1.7 us).
+    // 0.4-0.8 us with bit-identical output, MXFP4 1.4-1.7 us) and for the
+    // 32K layer's 2 pages per partition (0.3-0.9 us, bit-identical).
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < kSlots; ++p) {
       if (npg > p) k_page(kb0, p, 0, 4);
-      if (p < 3) load_k_half<kMx>(kb0, P, blk_of(p + 1), lane, 0);
+      if (p < kSlots - 1) load_k_half<kMx>(kb0, P, blk_of(p + 1), lane, 0);
       else load_v_half<kMx>(vb0, P, blk_of(0), lane, 0);
       if (npg > p) k_page(kb1, p, 4, 8);
-      if (p < 3) load_k_half<kMx>(kb1, P, blk_of(p + 1), lane, 1);
+      if (p < kSlots - 1) load_k_half<kMx>(kb1, P, blk_of(p + 1), lane, 1);
       else load_v_half<kMx>(vb1, P, blk_of(0), lane, 1);
     }
+  } else if constexpr (kSlots == 1) {
+    if (npg > 0) k_page(kb0, 0);
+  } else if constexpr (kSlots == 2) {
+    if (npg > 0) k_page(kb0, 0);
+    load_v<kMx>(vb0, P, blk_of(0), lane);
+    if (npg > 1) k_page(kb1, 1);
+    load_v<kMx>(vb1, P, blk_of(1), lane);
   } else {
     if (npg > 0) k_page(kb0, 0);
     load_k<kMx>(kb0, P, blk_of(2), lane);
@@ -917,19 +919,19 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
       }
     }
   };
-  if constexpr (kSlots == 1) {
+  if constexpr (kHalf) {
+#pragma unroll
+    for (int p = 0; p < kSlots; ++p) {
+      if (npg > p) v_page(vb0, p, 0, 2);
+      if (p < kSlots - 1) load_v_half<kMx>(vb0, P, blk_of(p + 1), lane, 0);
+      if (npg > p) v_page(vb1, p, 2, 4);
+      if (p < kSlots - 1) load_v_half<kMx>(vb1, P, blk_of(p + 1), lane, 1);
+    }
+  } else if constexpr (kSlots == 1) {
     if (npg > 0) v_page(vb0, 0);
   } else if constexpr (kSlots == 2) {
     if (npg > 0) v_page(vb0, 0);
     if (npg > 1) v_page(vb1, 1);
-  } else if constexpr (kHalf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (npg > p) v_page(vb0, p, 0, 2);
-      if (p < 3) load_v_half<kMx>(vb0, P, blk_of(p + 1), lane, 0);
-      if (npg > p) v_page(vb1, p, 2, 4);
-      if (p < 3) load_v_half<kMx>(vb1, P, blk_of(p + 1), lane, 1);
-    }
   } else {
     if (npg > 0) v_page(vb0, 0);
     load_v<kMx>(vb0, P, blk_of(2), lane);
@@ -1087,12 +1089,10 @@ __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
 // partial, ticket or merge: the merge of a single partial is that quotient).
 // A sequence without a full page has only the BF16 partition, written
 // straight to the output by column 0.
-// At least 3 waves per SIMD (at most 168 VGPRs) for the kernels that fit
-// without spilling: every 4-slot kernel but the channel-scale one (half
-// pages) and the NVFP4 ones with 1 or 2 slots.
+// At least 3 waves per SIMD (at most 168 VGPRs; with half pages every kernel
+// but the channel-scale ones fits without spilling).
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
-__global__ void __launch_bounds__(256)
-    __attribute__((amdgpu_waves_per_eu(kChan || (kSlots != 4 && (kMx || kRunMax)) ? 2 : 3)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kChan ? 2 : 3)))
 decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
