@@ -626,9 +626,9 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     for (int i = tid; i < 4 * 192; i += 256) pz[(i / 192) * 256 + 64 + (i % 192)] = 0u;
   }
   // The wave reads a stream of 2 kSlots slots, K pages 0..kSlots-1 then V
-  // pages 0..kSlots-1 (kHalf, every kernel without channel key scales:
-  // half pages, 4 kSlots slots, see there), keeping the next slot in
-  // flight while one is used:
+  // pages 0..kSlots-1 (kHalf, every kernel but the channel-scale ones with 1
+  // or 2 slots: half pages, 4 kSlots slots, see there), keeping the next
+  // slot in flight while one is used:
   // K page i lands in kb[i % 2], V page j in vb[j % 2], and the load of a
   // slot is issued once the slot two before it (same buffer) has been used
   // (with one page per partition, K and V page 0 are both requested at the
@@ -645,7 +645,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
   // requests its first K pages, so that waiting for the partition's rows
   // does not also wait for those pages (every workgroup of the grid requests
   // its first pages at once, and they take several µs to drain)
-  constexpr bool kHalf = !kChan;                          // half pages (see the stream below)
+  constexpr bool kHalf = !kChan || kSlots == 4;          // half pages (see the stream below)
   Partial bfp;
   if (bf16) {
     bfp = bf16_partition(A, sm, b, h, L, n_full);
@@ -712,7 +712,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     // channel key geometry: the page's 1 KiB of scales, [token block][channel],
     // in this wave's LDS (the wave reads it back in order); tile t takes the
     // 32 scales of its lanes' channels 32 kg .. +32 from block t
-    if (kChan) reinterpret_cast<uint4*>(&sm.ksc[wave][0])[lane] = cur.sc;
+    if (kChan && t_lo == 0) reinterpret_cast<uint4*>(&sm.ksc[wave][0])[lane] = cur.sc;
 #pragma unroll
     for (int t = t_lo; t < t_hi; ++t) {
       const int local = pi * kPage + t * 16;                    // first token of the tile - 128 p0
@@ -782,7 +782,10 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     // VGPRs: the room the compacted grid needs; MXFP4 157 against 184: 3
     // waves per SIMD instead of 2), and measured faster at 128K (NVFP4
     // 0.4-0.8 us with bit-identical output, MXFP4 1.4-1.7 us) and for the
-    // 32K layer's 2 pages per partition (0.3-0.9 us, bit-identical).
+    // 32K layer's 2 pages per partition (0.3-0.9 us, bit-identical). With
+    // channel key scales (the page's scales staged in LDS by the first half)
+    // it gains with 4 slots (the batch of 16: 57.6 -> 55.2 us) and loses with
+    // 2 (32K: +0.8 us), so those kernels keep whole pages.
 #pragma unroll
     for (int p = 0; p < kSlots; ++p) {
       if (npg > p) k_page(kb0, p, 0, 4);
@@ -1089,10 +1092,10 @@ __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
 // partial, ticket or merge: the merge of a single partial is that quotient).
 // A sequence without a full page has only the BF16 partition, written
 // straight to the output by column 0.
-// At least 3 waves per SIMD (at most 168 VGPRs; with half pages every kernel
-// but the channel-scale ones fits without spilling).
+// At least 3 waves per SIMD (at most 168 VGPRs; every kernel that streams
+// half pages fits without spilling).
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kChan ? 2 : 3)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kChan && kSlots != 4 ? 2 : 3)))
 decode_kernel(DecArgs A) {
   __shared__ __align__(16) Smem sm;
   const DecodeLaunch& P = A.L;
