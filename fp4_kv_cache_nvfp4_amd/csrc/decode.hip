@@ -12,17 +12,24 @@
 //
 // Grid: one workgroup (256 threads, 4 waves) per 4 FP4 partitions of a
 // (sequence, KV head); each wave owns one partition of pages_per_partition
-// (1..4) consecutive full pages. The BF16 partition (sink + tail tokens,
-// exact float32 attention of the raw query) of (sequence, KV head) j is
-// computed by workgroup j, among the first dispatched, before it requests
-// its first K pages. Every partition computes, for the 4 query heads of its KV
-// head, m = max logit, l = sum exp(t - m) and o = sum P_hat v_hat; a
-// workgroup merges its four waves in LDS, stores one partial and takes a
-// ticket; the last of a (sequence, KV head) merges all of them (merge.hpp).
+// (1..4) consecutive full pages. Workgroup j serves (sequence, KV head)
+// j mod (batch * KV heads) in column j / (batch * KV heads), so column 0 is
+// dispatched first. The BF16 partition (sink + tail tokens, exact float32
+// attention of the raw query) runs in a workgroup of its own in column 0 when
+// one more column still fits the chip at the kernel's occupancy, and is
+// otherwise folded into the first FP4 workgroup, computed before that
+// workgroup requests its first K pages. A grid larger than the chip holds is
+// compacted: workgroup j takes the j-th (column, sequence) unit that has
+// pages (compact_vj), so that no resident slot goes to a unit without work.
+// Every partition computes, for the 4 query heads of its KV head,
+// m = max logit, l = sum exp(t - m) and o = sum P_hat v_hat; a workgroup
+// merges its four waves in LDS, stores one partial and takes a ticket; the
+// last of a (sequence, KV head) merges all of them (merge.hpp).
 //
 // FP4 partition, per wave:
 //  * page ids: lane i reads page i of the partition's block-table run; the
-//    wave then issues its first two K page loads;
+//    wave then fills both K buffers (the two halves of its first page, or
+//    its first two whole pages);
 //  * prologue: wave g rotates (128-point Hadamard, float32) and quantizes
 //    query row g as Q1 + Q2 (amax6 per 16 or mxfp4_search per 32), two
 //    elements per lane. NVFP4: the dequantized terms are exact in 16 bits
@@ -31,9 +38,13 @@
 //    MFMA. Row 2g + t holds term t of head g and rows 8..15 repeat rows
 //    0..7. q . mu (raw float32 query, key means) seeds the term-1 rows of the
 //    accumulator.
-//  * pass 1 (QK^T): the wave streams its K pages with two pages in flight;
-//    per 16-token tile a lane holds 16 code bytes (one coalesced 1 KiB run
-//    per wave) and the page's scales come in one 16-byte load per lane. Four
+//  * pass 1 (QK^T): the wave streams its K pages, then its V pages, through
+//    two buffers per kind: half pages (K tiles 0-3 / 4-7, V chunks 0-1 / 2-3)
+//    in all kernels but the 1- and 2-slot channel-key-scale ones, which hold
+//    whole pages; a buffer is refilled as soon as its contents are used, so
+//    one buffer is in flight while the other is consumed. Per 16-token tile a
+//    lane holds 16 code bytes (one coalesced 1 KiB run per wave) and the
+//    page's scales come in one 16-byte load per lane. Four
 //    f16 MFMAs (NVFP4) or one v_mfma_scale_f32_16x16x128_f8f6f4 (MXFP4: the
 //    page's code bytes and E8M0 scales used as they are) give both terms of
 //    all four heads; their sum, the raw logit
@@ -779,7 +790,7 @@ __device__ Partial fp4_wg(const DecArgs& A, Smem& sm, int b, int h, int sp, int 
     // half h of V page p (vb_h); the load of a slot follows the use of the
     // slot two before it, in the same buffer. Against whole pages this holds
     // one page of K and V at a time instead of two (NVFP4 160 against 167
-    // VGPRs: the room the compacted grid needs; MXFP4 157 against 184: 3
+    // VGPRs: the room the compacted grid needs; MXFP4 163 against 184: 3
     // waves per SIMD instead of 2), and measured faster at 128K (NVFP4
     // 0.4-0.8 us with bit-identical output, MXFP4 1.4-1.7 us) and for the
     // 32K layer's 2 pages per partition (0.3-0.9 us, bit-identical). With
