@@ -1051,11 +1051,16 @@ __device__ __forceinline__ int seq_fp4_wgs(const DecodeLaunch& P, int L) {
 // serves the j-th unit with work, as the virtual index col * B Hkv + bh that
 // an uncompacted grid would give it: column 0 for every sequence (it also
 // computes the BF16 partition, or the NaN rows of an invalid sequence), then
-// column c >= 1 for each sequence with more than c FP4 workgroups, in
-// sequence order, KV head j mod Hkv (so a head's workgroups keep their place
-// in the dispatch rotation). Every wave computes the same mapping from the
-// sequence lengths (up to kCompactChunks x 64 sequences, in registers).
-// Returns -1 for a workgroup past the units with work.
+// by column the columns c >= 1 that are not a sequence's last, then by
+// column each sequence's last column (c >= 1), all in sequence order, KV
+// head j mod Hkv (so a head's workgroups keep their place in the dispatch
+// rotation). The last columns hold 1..ppp x 4 pages, the others all of
+// them: dispatched last, the lighter units are the ones a compute unit
+// takes as its third workgroup (the batch of 16: 46.0-47.8 against
+// 48.1-49.7 us with the last columns in column order). Every wave computes
+// the same mapping from the sequence lengths (up to kCompactChunks x 64
+// sequences, in registers). Returns -1 for a workgroup past the units with
+// work.
 constexpr int kCompactChunks = 4;
 __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
   const int lane = threadIdx.x & 63;
@@ -1071,17 +1076,21 @@ __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
     nw[k] = b < P.batch ? seq_fp4_wgs(P, P.seq_lens[b]) : 0;
   }
   const int wgs = fp4_wgs(P.max_parts);
-  for (int c = 1; c < wgs; ++c) {
+  for (int last = 0; last < 2; ++last) {
+    for (int c = 1; c < wgs; ++c) {
 #pragma unroll
-    for (int k = 0; k < kCompactChunks; ++k) {
-      const uint64_t m = __ballot(nw[k] > c);
-      const int cnt = __popcll(m);
-      if (u < cnt) {
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        const uint64_t pick = __ballot(nw[k] > c && below == u);
-        return c * BH + (64 * k + __builtin_ctzll(pick)) * P.hkv + h;
+      for (int k = 0; k < kCompactChunks; ++k) {
+        const bool has = last ? nw[k] == c + 1 : nw[k] > c + 1;   // column c is (not) the sequence's last
+        const uint64_t m = __ballot(has);
+        const int cnt = __popcll(m);
+        if (u < cnt) {
+          const int below =
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          const uint64_t pick = __ballot(has && below == u);
+          return c * BH + (64 * k + __builtin_ctzll(pick)) * P.hkv + h;
+        }
+        u -= cnt;
       }
-      u -= cnt;
     }
   }
   return -1;
