@@ -13,10 +13,11 @@
 // Grid: one workgroup (256 threads, 4 waves) per 4 FP4 partitions of a
 // (sequence, KV head); each wave owns one partition of pages_per_partition
 // (1..4) consecutive full pages. Workgroup j serves (sequence, KV head)
-// j mod (batch * KV heads) in column j / (batch * KV heads), so column 0 is
-// dispatched first. The BF16 partition (sink + tail tokens, exact float32
-// attention of the raw query) runs in a workgroup of its own in column 0 when
-// one more column still fits the chip at the kernel's occupancy, and is
+// j mod (batch * KV heads) in column j / (batch * KV heads). The BF16
+// partition (sink + tail tokens, exact float32 attention of the raw query)
+// runs in a workgroup of its own in column 0 when one more column still fits
+// the chip at the kernel's occupancy (that column is dispatched first, or
+// last when the FP4 workgroups outnumber the compute units), and is
 // otherwise folded into the first FP4 workgroup, computed before that
 // workgroup requests its first K pages. A grid larger than the chip holds is
 // compacted: workgroup j takes the j-th (column, sequence) unit that has
@@ -1097,11 +1098,13 @@ __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
 }
 
 // Workgroup j works for (sequence, KV head) bh = j % (B Hkv) in grid column
-// c = j / (B Hkv) (j the virtual index of compact_vj in a compacted launch). A launch whose grid has room for one more column
-// (split_bf16: it still fits the chip at two workgroups per compute unit)
-// gives every BF16 partition (sink + tail) a workgroup of its own in column
-// 0, the first B Hkv workgroups of the grid (dispatched first), which runs
-// beside the FP4 workgroups instead of delaying one of them; FP4 workgroup
+// c = j / (B Hkv) (j the virtual index: of compact_vj in a compacted launch,
+// rotated by one column under bf16_last). A launch whose grid has room for
+// one more column (split_bf16: it still fits the chip at the kernel's
+// occupancy) gives every BF16 partition (sink + tail) a workgroup of its own
+// in column 0 (the first B Hkv workgroups of the grid, or under bf16_last the
+// last), which runs beside the FP4 workgroups instead of delaying one of
+// them; FP4 workgroup
 // sp then sits in column sp + 1. Otherwise FP4 workgroup sp sits in column
 // sp, and workgroup 0 also computes the BF16 partition, before it requests
 // its first K pages, and folds it into its partial. FP4 workgroup sp stores
@@ -1112,8 +1115,8 @@ __device__ __forceinline__ int compact_vj(const DecodeLaunch& P, int j) {
 // partial, ticket or merge: the merge of a single partial is that quotient).
 // A sequence without a full page has only the BF16 partition, written
 // straight to the output by column 0.
-// At least 3 waves per SIMD (at most 168 VGPRs; every kernel that streams
-// half pages fits without spilling).
+// 3 waves per SIMD (at most 168 VGPRs) for every kernel that streams half
+// pages, without spilling; 2 for the whole-page channel-key-scale kernels.
 template <bool kMx, int kTerms, bool kUnder, bool kRunMax, int kSlots, bool kChan>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kChan && kSlots != 4 ? 2 : 3)))
 decode_kernel(DecArgs A) {
@@ -1122,6 +1125,11 @@ decode_kernel(DecArgs A) {
   const MergeCtx C = merge_ctx(A);
   const int BH = P.batch * P.hkv;
   int vj = (int)blockIdx.x;                                // grid position (compacted: of the j-th unit with work)
+  if (P.bf16_last) {
+    // the FP4 columns take workgroups 0 .. nfp - 1, the BF16 column the rest
+    const int nfp = (int)gridDim.x - BH;
+    vj = vj < nfp ? vj + BH : vj - nfp;
+  }
   if (P.compact) {
     vj = __builtin_amdgcn_readfirstlane(compact_vj(P, vj));
     if (vj < 0) return;
@@ -1295,6 +1303,12 @@ static hipError_t launch_one(DecArgs A, int cus, hipStream_t stream) {
   // a grid the chip does not hold at once takes its units with work first
   A.L.compact = !A.L.split_bf16 && wgs >= 2 && bh * wgs > (long long)per_cu * cus && A.L.batch <= 64 * kCompactChunks
                     ? 1 : 0;
+  // With more FP4 workgroups than compute units, a BF16 workgroup shares its
+  // compute unit with two FP4 workgroups; dispatched last it is the youngest
+  // there, so its issue comes after theirs rather than before (the 128K
+  // layer: 34.9-35.0 against 35.4-35.6 us). With one FP4 workgroup per
+  // compute unit it stays first (the 32K layer: 0.15-0.3 us faster so).
+  A.L.bf16_last = A.L.split_bf16 && bh * wgs > cus ? 1 : 0;
   // the FP4 workgroups of the longest sequence, after a column of BF16
   // partition workgroups when the launch has them
   const dim3 grid((unsigned)(bh * (wgs + A.L.split_bf16))), block(256u);

@@ -90,6 +90,7 @@ struct DecodeLaunch {
   int32_t dbg_stride;
   int32_t split_bf16;     // the BF16 partitions of sequences with >= 2 FP4 workgroups get workgroups of their own
   int32_t compact;        // a grid larger than the chip holds: workgroups take the units with work first
+  int32_t bf16_last;      // split_bf16 with more FP4 workgroups than compute units: the BF16 column is dispatched last
 };
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
