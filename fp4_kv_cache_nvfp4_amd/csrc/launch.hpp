@@ -125,7 +125,11 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
 constexpr int kGroup = 4;                         // query heads per KV head
 constexpr int kPartialFloats = kGroup * 130;      // o[4][128], m[4], l[4] (+pad)
 constexpr int kMaxSeqHeads = 16384;               // (sequence, KV head) pairs per call
-constexpr int kTicketStride = 1;                  // one completion ticket per (sequence, KV head)
+// One completion ticket per (sequence, KV head), each on a 128-byte line of
+// its own: every workgroup of a launch takes a device-scope ticket, and with
+// the tickets of all heads on one line those atomics queue on it (the 32K
+// layer's 264 workgroups finish within about 1.5 us: 17.33 -> 16.98 us apart).
+constexpr int kTicketStride = 32;
 
 // FP4 workgroups of a sequence with `parts` FP4 partitions (four per
 // workgroup, at least one).
@@ -135,7 +139,7 @@ __host__ __device__ inline int fp4_wgs(int parts) {
 }
 
 // Workspace shared by both decodes. A fixed ticket region,
-// [kMaxSeqHeads][kTicketStride] uint32 (the same for every call, so one
+// [kMaxSeqHeads][kTicketStride] uint32, 2 MiB (the same for every call, so one
 // zero-filled workspace serves calls of any shape), then partials
 // [batch * hkv][slot_stride][kPartialFloats] float32, slot_stride = parts + 2
 // for parts = partitions of the longest sequence counting its partial last

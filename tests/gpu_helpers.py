@@ -16,6 +16,7 @@ from oracle import writer as W
 
 # tolerance for attention outputs against the float64 oracle on the same
 # quantized operands and partitioning
+TICKET_BYTES = 16384 * 128      # the workspace's ticket region (one 128-byte line per ticket)
 MAX_ABS = 2e-3
 REL_L2 = 1e-3
 # beside it, element-wise bounds scaled to each output row's magnitude

@@ -20,6 +20,7 @@ import fp4_kv_cache_nvfp4_amd as bd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 FAKE = 0x7F0000000000          # 16-byte aligned stand-in device address (never dereferenced)
+TICKETS = 16384 * 128          # the workspace's ticket region: 16,384 tickets, one 128-byte line each
 
 
 def _golden(name):
@@ -113,9 +114,9 @@ def test_sizes_and_plan():
     assert bd.decode_plan(16, 8, 16384, 0) == (4, 32)
     assert bd.decode_plan(1, 1, 2048, 0) == (1, 16)
     ws = bd.decode_workspace_size(1, 32, 8, 131072, 4)
-    assert ws == 16384 * 4 + 8 * (256 + 2) * 520 * 4
+    assert ws == TICKETS + 8 * (256 + 2) * 520 * 4
     # a partial last page adds a BF16-decode partition
-    assert bd.decode_workspace_size(2, 8, 2, 1000, 3) == 16384 * 4 + 4 * (3 + 2) * 520 * 4
+    assert bd.decode_workspace_size(2, 8, 2, 1000, 3) == TICKETS + 4 * (3 + 2) * 520 * 4
     with pytest.raises(bd.Bdfp4Error) as ei:
         bd.decode_workspace_size(1, 24, 8, 1000, 0)
     assert ei.value.status == bd.E_UNSUPPORTED
@@ -140,9 +141,9 @@ def test_bf16_plan_and_workspace():
         assert ei.value.status == bd.E_INVALID
     # 0 sizes for both automatic plans (the FP4 one needs more here), 5 .. 16
     # for the BF16 decode alone
-    assert bd.decode_workspace_size(1, 32, 8, 131072, 0) == 16384 * 4 + 8 * (256 + 2) * 520 * 4
-    assert bd.decode_workspace_size(1, 32, 8, 131072, 16) == 16384 * 4 + 8 * (64 + 2) * 520 * 4
-    assert bd.decode_workspace_size(1, 32, 8, 131072 + 77, 16) == 16384 * 4 + 8 * (65 + 2) * 520 * 4
+    assert bd.decode_workspace_size(1, 32, 8, 131072, 0) == TICKETS + 8 * (256 + 2) * 520 * 4
+    assert bd.decode_workspace_size(1, 32, 8, 131072, 16) == TICKETS + 8 * (64 + 2) * 520 * 4
+    assert bd.decode_workspace_size(1, 32, 8, 131072 + 77, 16) == TICKETS + 8 * (65 + 2) * 520 * 4
     for L in (100, 2048, 8192, 32768 + 77, 131072):
         for b, h in ((1, 1), (1, 8), (16, 8)):
             auto = bd.decode_workspace_size(b, 4 * h, h, L, 0)

@@ -26,7 +26,7 @@ from oracle import writer as OW
 
 import oracle_pool as OP
 from gpu_helpers import (assert_close, cache_to_dev, dev, dev_bf16, gpu_decode, gpu_write,
-                         oracle_decode, oracle_write, to_c)
+                         oracle_decode, oracle_write, to_c, TICKET_BYTES)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,7 +205,7 @@ def test_workspace_reuse_across_shapes():
                             dev_bf16(tv), dev(wl.key_shift), wl.sigma, 1, ws, out)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy().astype(np.float64), ref, f"reuse {wl.name}")
-    assert not ws[:65536].any()
+    assert not ws[:TICKET_BYTES].any()
 
 
 @pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
@@ -269,7 +269,7 @@ def test_bf16_full_128k_layer():
                              dev(wl.seq_lens), L, wl.sigma, 0, ws, out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy().astype(np.float64), ref, "bf16 128k layer, auto plan")
-    assert not ws[:65536].any()
+    assert not ws[:TICKET_BYTES].any()
 
 
 @pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
@@ -363,7 +363,7 @@ def test_max_sequence_heads():
                         ws, out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy().astype(np.float64), ref, "16,384 (sequence, KV head) pairs")
-    assert not ws[:65536].any()
+    assert not ws[:TICKET_BYTES].any()
     kp, vp = wl.bf16_pages()
     ref16 = OD.bf16_decode(wl.q, kp, vp, wl.block_tables, wl.seq_lens, wl.sigma)
     assert bd.bf16_decode_plan(wl.batch, 8, int(lens.max()), 0) == (16, 2)
@@ -372,7 +372,7 @@ def test_max_sequence_heads():
                              int(lens.max()), wl.sigma, 0, ws, out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy().astype(np.float64), ref16, "bf16, 16,384 (sequence, KV head) pairs")
-    assert not ws[:65536].any()
+    assert not ws[:TICKET_BYTES].any()
 
 
 def test_p_flips_from_float32_logits():
