@@ -170,7 +170,7 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 
 // Merges the n partials of (sequence b, KV head h) and writes out = o / L.
 // Each wave merges its own query head (wave g, head g) with no workgroup
-// barrier: per batch of 64 partials, lane i loads (m, l) of partial i and
+// barrier: per batch of 64 (or 32) partials, lane i loads (m, l) of partial i and
 // every lane loads its two channels of o of all 64 (one memory round trip,
 // the (m, l) loads first so the maximum and the weights are formed while o
 // lands); a batch after the first rescales what came before. The merging
@@ -185,7 +185,46 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 // issued ahead of the first batch's, so they share that round trip, and it
 // is combined after the last batch. With rotate_back (values stored
 // rotated), the merged o is rotated back before the division.
-constexpr int kMergeBatch = 64;
+// Partials are taken in batches of kB = 32 or 64 slots: lane i loads (m, l) of
+// slot i0 + i (lanes past a batch of 32 weigh 0 there; they belong to the
+// next) and every lane loads its two channels of o of each slot. A batch of
+// 64 covers the 64 partials of a 128K head in one round trip; with at most
+// 32 partials a batch of 32 halves the loads (34 per wave instead of 66, under
+// the 63 loads a wave's counter tracks: the 32K layer 16.9-17.1 -> 16.0-16.2
+// us, the tiny case 11.2 -> 10.2 us, bit-identical: the slots past n weigh 0
+// either way).
+template <int kB>
+__device__ __forceinline__ void merge_batches(__amdgpu_buffer_rsrc_t R, int ns, int g, int lane, int o_off,
+                                              float& M, float& Ls, float& o0, float& o1) {
+  constexpr int kSlotBytes = kPartialFloats * 4;
+  const float ninf = -__builtin_inff();
+  for (int i0 = 0; i0 < ns; i0 += kB) {
+    const int i = i0 + lane;
+    const int ml_off = i * kSlotBytes + (512 + g) * 4;
+    const float mr = cload1(R, ml_off);
+    const float lr = cload1(R, ml_off + 16);
+    float2 ov[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) ov[k] = cload2(R, (i0 + k) * kSlotBytes + o_off);
+    const float ms = (i < ns && lane < kB) ? mr : ninf;
+    const float Mn = fmaxf(M, wave_max(ms));
+    const float f = M == ninf ? 0.0f : __expf(M - Mn);     // rescale of the partials before
+    const float w = ms == ninf ? 0.0f : __expf(ms - Mn);
+    Ls = fmaf(Ls, f, wave_sum(w * lr));
+    // the batch's weighted sum in four independent FMA chains (slots k with
+    // k mod 4 = c), added in a fixed tree: a quarter of the dependent latency
+    float c0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const float wk = lane_f32(w, k);
+      c0[k & 3] = fmaf(wk, ov[k].x, c0[k & 3]);
+      c1[k & 3] = fmaf(wk, ov[k].y, c1[k & 3]);
+    }
+    o0 = fmaf(o0, f, (c0[0] + c0[1]) + (c0[2] + c0[3]));
+    o1 = fmaf(o1, f, (c1[0] + c1[1]) + (c1[2] + c1[3]));
+    M = Mn;
+  }
+}
 
 __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n, bool rotate_back,
                                           int extra = -1) {
@@ -212,32 +251,9 @@ __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n
     ox = cload2(RX, xs * kSlotBytes + o_off);
   }
   float M = ninf, Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int i0 = 0; i0 < ns; i0 += kMergeBatch) {
-    const int i = i0 + lane;
-    const int ml_off = i * kSlotBytes + (512 + g) * 4;
-    const float mr = cload1(R, ml_off);
-    const float lr = cload1(R, ml_off + 16);
-    float2 ov[kMergeBatch];
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) ov[k] = cload2(R, (i0 + k) * kSlotBytes + o_off);
-    const float ms = i < ns ? mr : ninf;
-    const float Mn = fmaxf(M, wave_max(ms));
-    const float f = M == ninf ? 0.0f : __expf(M - Mn);     // rescale of the partials before
-    const float w = ms == ninf ? 0.0f : __expf(ms - Mn);
-    Ls = fmaf(Ls, f, wave_sum(w * lr));
-    // the batch's weighted sum in four independent FMA chains (slots k with
-    // k mod 4 = c), added in a fixed tree: a quarter of the dependent latency
-    float c0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const float wk = lane_f32(w, k);
-      c0[k & 3] = fmaf(wk, ov[k].x, c0[k & 3]);
-      c1[k & 3] = fmaf(wk, ov[k].y, c1[k & 3]);
-    }
-    o0 = fmaf(o0, f, (c0[0] + c0[1]) + (c0[2] + c0[3]));
-    o1 = fmaf(o1, f, (c1[0] + c1[1]) + (c1[2] + c1[3]));
-    M = Mn;
-  }
+  // up to 64 partials in one round trip; up to 32 with half the loads
+  if (ns <= 32) merge_batches<32>(R, ns, g, lane, o_off, M, Ls, o0, o1);
+  else merge_batches<64>(R, ns, g, lane, o_off, M, Ls, o0, o1);
   if (xs >= 0) {
     const float Mn = fmaxf(M, mx);
     const float f = M == ninf ? 0.0f : __expf(M - Mn);
