@@ -141,7 +141,7 @@ __host__ __device__ inline int fp4_wgs(int parts) {
 // Workspace shared by both decodes. A fixed ticket region,
 // [kMaxSeqHeads][kTicketStride] uint32, 2 MiB (the same for every call, so one
 // zero-filled workspace serves calls of any shape), then partials
-// [batch * hkv][slot_stride][kPartialFloats] float32, slot_stride = parts + 2
+// [batch * hkv][slot_stride][kPartialFloats] float32 (slots in pairs), slot_stride = parts + 2 rounded up to even
 // for parts = partitions of the longest sequence counting its partial last
 // page (ceil(ceil(max_seq_len / 128) / pages_per_partition)). An FP4 decode
 // of a sequence with w FP4 workgroups uses slots 0 .. w-1, one per
@@ -149,7 +149,8 @@ __host__ __device__ inline int fp4_wgs(int parts) {
 // one slot per partition.
 constexpr size_t kTicketBytes = (size_t)kMaxSeqHeads * kTicketStride * sizeof(uint32_t);
 
-inline int32_t workspace_slot_stride(int32_t parts) { return parts + 2; }
+// parts + 2 slots, rounded up to even: the slots are stored in pairs
+inline int32_t workspace_slot_stride(int32_t parts) { return (parts + 3) & ~1; }
 
 // The allocation-free decode's workspace: a device array of this many bytes
 // (tickets, then partials) that the library keeps per GPU. noalloc_scratch

@@ -42,6 +42,19 @@ __device__ __forceinline__ float* partial_slot(const MergeCtx& C, int bh, int s)
   return C.partials + ((size_t)bh * C.slot_stride + s) * kPartialFloats;
 }
 
+// Slots are stored in pairs (2p, 2p + 1), a block of 2 kPartialFloats floats
+// (slot_stride is even): o of both slots interleaved first, the 16 bytes at
+// float (head * 64 + c) * 4 holding channels 2c, 2c + 1 of slot 2p, then of
+// slot 2p + 1; then m[4], l[4] of slot 2p at float 1024 and of slot 2p + 1 at
+// 1032. One 16-byte load thus gives a lane its two channels of two slots.
+constexpr int kPairBytes = 2 * kPartialFloats * 4;
+__device__ __forceinline__ int o_byte(int s, int head, int c) {
+  return (s >> 1) * kPairBytes + ((head * 64 + c) * 4 + (s & 1) * 2) * 4;
+}
+__device__ __forceinline__ int ml_byte(int s) {      // m[4] here, l[4] 16 bytes on
+  return (s >> 1) * kPairBytes + (1024 + (s & 1) * 8) * 4;
+}
+
 constexpr int kCachePolicySc1 = 16;
 constexpr int kRawBufferWord3 = 0x00020000;   // 32-bit data format, untyped access
 
@@ -56,6 +69,11 @@ __device__ __forceinline__ float4 cload4(__amdgpu_buffer_rsrc_t r, int byte_off)
   const f4 v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicySc1));
   return make_float4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ void cstore2(__amdgpu_buffer_rsrc_t r, int byte_off, float2 v) {
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  const u2 w = {__float_as_uint(v.x), __float_as_uint(v.y)};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, byte_off, 0, kCachePolicySc1);
+}
 __device__ __forceinline__ void cstore4(__amdgpu_buffer_rsrc_t r, int byte_off, float4 v) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   const u4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
@@ -64,29 +82,26 @@ __device__ __forceinline__ void cstore4(__amdgpu_buffer_rsrc_t r, int byte_off, 
 
 struct PartialWriter {
   __amdgpu_buffer_rsrc_t r;
-  int slot_off;   // byte offset of the slot
+  int slot;
 };
 
 __device__ __forceinline__ PartialWriter partial_writer(const MergeCtx& C, int bh, int s) {
   PartialWriter w;
   w.r = partial_rsrc(C, bh);
-  w.slot_off = s * kPartialFloats * 4;
+  w.slot = s;
   return w;
 }
 
-// Stores one partial. Thread t (of 256) holds o[t >> 6][2 (t & 63) .. +2];
-// pairs of lanes combine into 16-byte stores; thread 0 stores m[4] and l[4].
+// Stores one partial. Thread t (of 256) holds o[t >> 6][2 (t & 63) .. +2] and
+// stores it as 8 bytes into the slot pair's interleaved o; thread 0 stores
+// m[4] and l[4].
 __device__ __forceinline__ void write_partial(const PartialWriter& W, float o0, float o1, const float* m4,
                                               const float* l4) {
   const int t = threadIdx.x;
-  const float p0 = __shfl_xor(o0, 1, 64), p1 = __shfl_xor(o1, 1, 64);
-  if ((t & 1) == 0) {
-    const int head = t >> 6, d = 2 * (t & 63);
-    cstore4(W.r, W.slot_off + (head * kD + d) * 4, make_float4(o0, o1, p0, p1));
-  }
+  cstore2(W.r, o_byte(W.slot, t >> 6, t & 63), make_float2(o0, o1));
   if (t == 0) {
-    cstore4(W.r, W.slot_off + 512 * 4, make_float4(m4[0], m4[1], m4[2], m4[3]));
-    cstore4(W.r, W.slot_off + 516 * 4, make_float4(l4[0], l4[1], l4[2], l4[3]));
+    cstore4(W.r, ml_byte(W.slot), make_float4(m4[0], m4[1], m4[2], m4[3]));
+    cstore4(W.r, ml_byte(W.slot) + 16, make_float4(l4[0], l4[1], l4[2], l4[3]));
   }
 }
 
@@ -175,8 +190,9 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 // the (m, l) loads first so the maximum and the weights are formed while o
 // lands); a batch after the first rescales what came before. The merging
 // workgroup reads its own partial back like the others (its stores completed
-// before it took the ticket). The resource covers exactly the n slots, so a
-// slot past them reads 0 and needs no address select; its weight is 0. The
+// before it took the ticket). The resource covers the pairs of the n slots,
+// so a pair past them reads 0 and needs no address select; a slot n in the
+// last pair (odd n) is zeroed; either weighs 0. The
 // partials are always combined in slot order (lane order for l, a fixed
 // tree over slot-ordered chains for o), so the result does not depend on
 // which workgroup merges: the
@@ -194,18 +210,29 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 // us, the tiny case 11.2 -> 10.2 us, bit-identical: the slots past n weigh 0
 // either way).
 template <int kB>
-__device__ __forceinline__ void merge_batches(__amdgpu_buffer_rsrc_t R, int ns, int g, int lane, int o_off,
-                                              float& M, float& Ls, float& o0, float& o1) {
-  constexpr int kSlotBytes = kPartialFloats * 4;
+__device__ __forceinline__ void merge_batches(__amdgpu_buffer_rsrc_t R, int ns, int g, int lane, float& M,
+                                              float& Ls, float& o0, float& o1) {
   const float ninf = -__builtin_inff();
   for (int i0 = 0; i0 < ns; i0 += kB) {
     const int i = i0 + lane;
-    const int ml_off = i * kSlotBytes + (512 + g) * 4;
-    const float mr = cload1(R, ml_off);
-    const float lr = cload1(R, ml_off + 16);
+    const float mr = cload1(R, ml_byte(i) + g * 4);
+    float lr = cload1(R, ml_byte(i) + 16 + g * 4);
     float2 ov[kB];
 #pragma unroll
-    for (int k = 0; k < kB; ++k) ov[k] = cload2(R, (i0 + k) * kSlotBytes + o_off);
+    for (int k = 0; k < kB; k += 2) {
+      const float4 v = cload4(R, o_byte(i0 + k, g, lane));
+      ov[k] = make_float2(v.x, v.y);
+      ov[k + 1] = make_float2(v.z, v.w);
+    }
+    // with an odd n, slot n shares the last pair and lies inside the
+    // resource: whatever it holds (another call's partial, or a NaN one)
+    // weighs 0 and is zeroed (0 x NaN would not vanish)
+    if ((ns & 1) && ns >= i0 && ns < i0 + kB) {
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (i0 + k == ns) ov[k] = make_float2(0.0f, 0.0f);
+    }
+    lr = i < ns ? lr : 0.0f;
     const float ms = (i < ns && lane < kB) ? mr : ninf;
     const float Mn = fmaxf(M, wave_max(ms));
     const float f = M == ninf ? 0.0f : __expf(M - Mn);     // rescale of the partials before
@@ -234,26 +261,24 @@ __device__ __forceinline__ void merge_out(const MergeCtx& C, int b, int h, int n
   const int ns = __builtin_amdgcn_readfirstlane(n);
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const float ninf = -__builtin_inff();
-  constexpr int kSlotBytes = kPartialFloats * 4;
-  const __amdgpu_buffer_rsrc_t R =
-      __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0, ns * kSlotBytes, kRawBufferWord3);
-  const int o_off = (g * kD + 2 * lane) * 4;
-  // the extra partial, through a resource that covers its slot as well (the
-  // batches keep theirs: a slot past the n reads 0)
+  // the pair blocks that hold slots 0 .. n-1 (a pair past them reads 0)
+  const __amdgpu_buffer_rsrc_t R = __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0,
+                                                                     ((ns + 1) >> 1) * kPairBytes, kRawBufferWord3);
+  // the extra partial, through a resource that covers its pair as well
   const int xs = __builtin_amdgcn_readfirstlane(extra);
   float mx = ninf, lx = 0.0f;
   float2 ox = make_float2(0.0f, 0.0f);
   if (xs >= 0) {
-    const __amdgpu_buffer_rsrc_t RX =
-        __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0, (xs + 1) * kSlotBytes, kRawBufferWord3);
-    mx = cload1(RX, xs * kSlotBytes + (512 + g) * 4);
-    lx = cload1(RX, xs * kSlotBytes + (516 + g) * 4);
-    ox = cload2(RX, xs * kSlotBytes + o_off);
+    const __amdgpu_buffer_rsrc_t RX = __builtin_amdgcn_make_buffer_rsrc(partial_slot(C, bh, 0), (short)0,
+                                                                        ((xs >> 1) + 1) * kPairBytes, kRawBufferWord3);
+    mx = cload1(RX, ml_byte(xs) + g * 4);
+    lx = cload1(RX, ml_byte(xs) + 16 + g * 4);
+    ox = cload2(RX, o_byte(xs, g, lane));
   }
   float M = ninf, Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
   // up to 64 partials in one round trip; up to 32 with half the loads
-  if (ns <= 32) merge_batches<32>(R, ns, g, lane, o_off, M, Ls, o0, o1);
-  else merge_batches<64>(R, ns, g, lane, o_off, M, Ls, o0, o1);
+  if (ns <= 32) merge_batches<32>(R, ns, g, lane, M, Ls, o0, o1);
+  else merge_batches<64>(R, ns, g, lane, M, Ls, o0, o1);
   if (xs >= 0) {
     const float Mn = fmaxf(M, mx);
     const float f = M == ninf ? 0.0f : __expf(M - Mn);

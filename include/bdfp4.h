@@ -294,7 +294,8 @@ bdfp4_status bdfp4_bf16_decode_plan(int32_t batch, int32_t num_kv_heads,
  * with these sizes (host output): a fixed ticket region of
  * 16384 * 128 bytes (one 128-byte line per ticket; the same for every call
  * shape), then
- * batch * num_kv_heads * (P + 2) partial slots of 2080 bytes, where
+ * batch * num_kv_heads * S partial slots of 2080 bytes, S = P + 2 rounded up
+ * to even (the slots are stored in pairs), where
  * P = ceil(ceil(max_seq_len / 128) / pages_per_partition).
  * pages_per_partition 0 sizes for the larger of the two decodes' automatic
  * plans, 1 .. 4 for that value (either decode), 5 .. 16 for the BF16 decode
