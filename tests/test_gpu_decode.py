@@ -208,6 +208,43 @@ def test_workspace_reuse_across_shapes():
     assert not ws[:TICKET_BYTES].any()
 
 
+def test_odd_partial_count_after_poisoned_call():
+    """Partials are stored in slot pairs, so with an odd count n the merge's
+    loads of the last pair also bring slot n, which still holds whatever an
+    earlier call left there. Here an earlier call on the same workspace left
+    a NaN partial in slot 3 of sequence 0 (an invalid page in its fourth FP4
+    workgroup; a grid larger than the chip holds, so the BF16 partition is
+    folded and slot 3 is no BF16 slot); the next call merges 3 partials for
+    that sequence, and every row must match the oracle."""
+    print("[odd partial count after a poisoned call] 48 x 8, ppp 1", flush=True)
+    lens1 = [16 * 128] + [200] * 47
+    lens2 = [12 * 128 + 50] + [200] * 47
+    wl1 = synth.decode_workload("odd1", 41, lens1, 32, 8, "qwen", extra_pages=1)
+    wl2 = synth.decode_workload("odd2", 42, lens2, 32, 8, "qwen")
+    msl = 16 * 128
+    ws = bd.alloc_workspace(bd.decode_workspace_size(48, 32, 8, msl, 1))
+    rc = to_c(NV)
+    outs = []
+    for wl, poison in ((wl1, True), (wl2, False)):
+        host = oracle_write(NV, wl)
+        bt = np.zeros((48, 16), dtype=np.int32)          # both calls: 16 block-table columns
+        bt[:, :wl.block_tables.shape[1]] = wl.block_tables
+        if poison:
+            bt[0, 13] = wl.num_pages + 7                 # a page outside the pool, FP4 workgroup 3's
+        sk, sv, tk, tv = wl.sink_tail()
+        out = torch.empty((48, 32, 128), dtype=torch.float32, device="cuda")
+        bd.decode_attention(rc, cache_to_dev(NV, host, 8), dev_bf16(wl.q), dev(bt), dev(wl.seq_lens), msl,
+                            dev_bf16(sk), dev_bf16(sv), dev_bf16(tk), dev_bf16(tv), dev(wl.key_shift), wl.sigma, 1,
+                            ws, out)
+        torch.cuda.synchronize()
+        outs.append((wl, host, out.cpu().numpy().astype(np.float64)))
+    wl, host, got = outs[0]
+    assert np.all(np.isnan(got[0]))
+    wl, host, got = outs[1]
+    assert_close(got, oracle_decode(NV, wl, host, 1), "3 partials after a NaN partial in slot 3")
+    assert not ws[:TICKET_BYTES].any()
+
+
 @pytest.mark.parametrize("r", [NV, MX], ids=["nvfp4", "mxfp4"])
 def test_end_to_end_writer_then_decode(r):
     wl = synth.decode_workload("e", 12, [5000, 2300], 16, 4, "qwen", extra_pages=2)
