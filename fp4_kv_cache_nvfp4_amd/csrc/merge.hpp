@@ -1,9 +1,10 @@
 // Split-K partials and their log-sum-exp merge, shared by the FP4 and BF16
 // decodes.
 //
-// A partial (kPartialFloats floats) holds, for the 4 query heads of a KV
-// head, o[4][128] (unnormalized: sum over its tokens of p v) at 0, m[4] (the
-// maximum logit, sigma included) at 512 and l[4] = sum p at 516. Merging
+// A partial holds, for the 4 query heads of a KV head, o[4][128]
+// (unnormalized: sum over its tokens of p v), m[4] (the maximum logit, sigma
+// included) and l[4] = sum p: kPartialFloats floats, stored in pairs of
+// slots (o_byte, ml_byte). Merging
 // partials s gives
 //   M = max m_s, L = sum l_s e^(m_s - M), o = sum o_s e^(m_s - M)
 // (partials with m_s = -inf are empty and weigh 0), and the output is o / L.
@@ -17,7 +18,7 @@
 // store, ticket, loads, output.
 //
 // Visibility without cache flushes: partials are written and read with
-// 16-byte buffer accesses carrying the SC1 cache policy (coherent at device
+// buffer accesses carrying the SC1 cache policy (coherent at device
 // scope: the stores are written through to the device coherence point
 // instead of being held in one XCD's L2, and the merging workgroup's loads
 // are not served from a possibly stale L2 line). Every thread waits for its
@@ -185,10 +186,11 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 
 // Merges the n partials of (sequence b, KV head h) and writes out = o / L.
 // Each wave merges its own query head (wave g, head g) with no workgroup
-// barrier: per batch of 64 (or 32) partials, lane i loads (m, l) of partial i and
-// every lane loads its two channels of o of all 64 (one memory round trip,
-// the (m, l) loads first so the maximum and the weights are formed while o
-// lands); a batch after the first rescales what came before. The merging
+// barrier: per batch of 64 (or 32) partials, lane i loads (m, l) of partial i
+// and every lane loads its two channels of o of every slot of the batch, two
+// slots per 16-byte load (one memory round trip, the (m, l) loads first so
+// the maximum and the weights are formed while o lands); a batch after the
+// first rescales what came before. The merging
 // workgroup reads its own partial back like the others (its stores completed
 // before it took the ticket). The resource covers the pairs of the n slots,
 // so a pair past them reads 0 and needs no address select; a slot n in the
@@ -203,9 +205,10 @@ __device__ __forceinline__ void wave_rotate2(float& x0, float& x1) {
 // rotated), the merged o is rotated back before the division.
 // Partials are taken in batches of kB = 32 or 64 slots: lane i loads (m, l) of
 // slot i0 + i (lanes past a batch of 32 weigh 0 there; they belong to the
-// next) and every lane loads its two channels of o of each slot. A batch of
-// 64 covers the 64 partials of a 128K head in one round trip; with at most
-// 32 partials a batch of 32 halves the loads (34 per wave instead of 66, under
+// next) and every lane loads its two channels of o of each slot, a slot pair
+// per 16-byte load. A batch of 64 covers the 64 partials of a 128K head in
+// one round trip; with at most 32 partials a batch of 32 halves the loads
+// (measured with one slot per 8-byte load: 34 per wave instead of 66, under
 // the 63 loads a wave's counter tracks: the 32K layer 16.9-17.1 -> 16.0-16.2
 // us, the tiny case 11.2 -> 10.2 us, bit-identical: the slots past n weigh 0
 // either way).
