@@ -114,6 +114,35 @@ def test_random_shapes(seed):
     assert_close(got, ref, what)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_large_random_grids(seed):
+    """Seeded batches whose grids leave the small-launch paths, 4 KV heads:
+    even seeds 6-11 sequences of 3K-8K tokens at one page per partition
+    (13-16 FP4 workgroups per head, 312-640 in all: BF16 workgroups of their
+    own, dispatched after the FP4 columns, and heads of up to 64 partials);
+    odd seeds 40-63 sequences of 1-6000 tokens at two pages per partition (a
+    grid of 1,000-1,400 workgroups: compacted, last columns last, the BF16
+    partition folded, odd partial counts). Random recipe (NVFP4 / MXFP4,
+    sink, query terms, tau); every output row against the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    if seed % 2 == 0:
+        B, ppp = int(rng.integers(6, 12)), 1
+        lens = [int(x) for x in rng.integers(3000, 8192, size=B)]
+    else:
+        B, ppp = int(rng.integers(40, 64)), 2
+        lens = [int(x) for x in rng.integers(1, 6000, size=B)]
+    sink = int(rng.choice([0, 16, 48]))
+    base = MX if rng.random() < 0.4 else NV
+    r = base.with_(sink_tokens=sink, query_terms=int(rng.choice([1, 2])), tau=float(rng.choice([0.5, 1.0, 4.0])))
+    wl = synth.decode_workload("large", 6000 + seed, lens, 16, 4, "qwen", extra_pages=1, sink_tokens=sink)
+    what = f"large grid seed={seed}: B={B} max L={max(lens)} ppp={ppp} sink={sink} {'mx' if base is MX else 'nv'}"
+    print(f"[decode] {what}", flush=True)
+    host = oracle_write(r, wl)
+    ref = oracle_decode(r, wl, host, ppp)
+    got = gpu_decode(r, wl, cache_to_dev(r, host, 4), ppp)
+    assert_close(got, ref, what)
+
+
 @pytest.mark.parametrize("ppp", [1, 2, 3])
 def test_ragged_batch_channel_geometry(ppp):
     # the channel key scale geometry over ragged lengths, every page-slot count
