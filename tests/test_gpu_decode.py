@@ -122,8 +122,9 @@ def test_large_random_grids(seed):
     own, dispatched after the FP4 columns, and heads of up to 64 partials);
     odd seeds 40-63 sequences of 1-6000 tokens at two pages per partition (a
     grid of 1,000-1,400 workgroups: compacted, last columns last, the BF16
-    partition folded, odd partial counts). Random recipe (NVFP4 / MXFP4,
-    sink, query terms, tau); every output row against the oracle."""
+    partition folded, odd partial counts). NVFP4, MXFP4 or NVFP4 with
+    channel key scales by seed; random sink, query terms and tau; every
+    output row against the oracle."""
     rng = np.random.default_rng(5000 + seed)
     if seed % 2 == 0:
         B, ppp = int(rng.integers(6, 12)), 1
@@ -132,10 +133,11 @@ def test_large_random_grids(seed):
         B, ppp = int(rng.integers(40, 64)), 2
         lens = [int(x) for x in rng.integers(1, 6000, size=B)]
     sink = int(rng.choice([0, 16, 48]))
-    base = MX if rng.random() < 0.4 else NV
+    kind = ["nv", "mx", "chan"][seed % 3]
+    base = MX if kind == "mx" else (NV.with_(key_scale_geometry=RC.CHANNEL) if kind == "chan" else NV)
     r = base.with_(sink_tokens=sink, query_terms=int(rng.choice([1, 2])), tau=float(rng.choice([0.5, 1.0, 4.0])))
     wl = synth.decode_workload("large", 6000 + seed, lens, 16, 4, "qwen", extra_pages=1, sink_tokens=sink)
-    what = f"large grid seed={seed}: B={B} max L={max(lens)} ppp={ppp} sink={sink} {'mx' if base is MX else 'nv'}"
+    what = f"large grid seed={seed}: B={B} max L={max(lens)} ppp={ppp} sink={sink} {kind}"
     print(f"[decode] {what}", flush=True)
     host = oracle_write(r, wl)
     ref = oracle_decode(r, wl, host, ppp)
