@@ -116,32 +116,34 @@ def test_random_shapes(seed):
 
 @pytest.mark.parametrize("seed", range(8))
 def test_large_random_grids(seed):
-    """Seeded batches whose grids leave the small-launch paths, 4 KV heads:
-    even seeds 6-11 sequences of 3K-8K tokens at one page per partition
-    (13-16 FP4 workgroups per head, 312-640 in all: BF16 workgroups of their
-    own, dispatched after the FP4 columns, and heads of up to 64 partials);
-    odd seeds 40-63 sequences of 1-6000 tokens at two pages per partition (a
-    grid of 1,000-1,400 workgroups: compacted, last columns last, the BF16
-    partition folded, odd partial counts). NVFP4, MXFP4 or NVFP4 with
+    """Seeded batches whose grids leave the small-launch paths, 4, 8 or 3 KV
+    heads by seed (with 3, a head's workgroups span XCDs): even seeds
+    sequences of 3K-8K tokens at one page per partition (13-16 FP4
+    workgroups per head, 312-640 in all: BF16 workgroups of their own,
+    dispatched after the FP4 columns, and heads of up to 64 partials); odd
+    seeds 160-250 (sequence, KV head) pairs of 1-6000 tokens at two pages per
+    partition (a grid of 1,000-1,400 workgroups: compacted, last columns
+    last, the BF16 partition folded, odd partial counts). NVFP4, MXFP4 or NVFP4 with
     channel key scales by seed; random sink, query terms and tau; every
     output row against the oracle."""
+    hkv = [4, 8, 3][seed % 3]
     rng = np.random.default_rng(5000 + seed)
     if seed % 2 == 0:
-        B, ppp = int(rng.integers(6, 12)), 1
+        B, ppp = int(rng.integers(max(1, 24 // hkv), max(2, 44 // hkv))), 1
         lens = [int(x) for x in rng.integers(3000, 8192, size=B)]
     else:
-        B, ppp = int(rng.integers(40, 64)), 2
+        B, ppp = int(rng.integers(160 // hkv, 252 // hkv)), 2
         lens = [int(x) for x in rng.integers(1, 6000, size=B)]
     sink = int(rng.choice([0, 16, 48]))
     kind = ["nv", "mx", "chan"][seed % 3]
     base = MX if kind == "mx" else (NV.with_(key_scale_geometry=RC.CHANNEL) if kind == "chan" else NV)
     r = base.with_(sink_tokens=sink, query_terms=int(rng.choice([1, 2])), tau=float(rng.choice([0.5, 1.0, 4.0])))
-    wl = synth.decode_workload("large", 6000 + seed, lens, 16, 4, "qwen", extra_pages=1, sink_tokens=sink)
-    what = f"large grid seed={seed}: B={B} max L={max(lens)} ppp={ppp} sink={sink} {kind}"
+    wl = synth.decode_workload("large", 6000 + seed, lens, 4 * hkv, hkv, "qwen", extra_pages=1, sink_tokens=sink)
+    what = f"large grid seed={seed}: B={B} hkv={hkv} max L={max(lens)} ppp={ppp} sink={sink} {kind}"
     print(f"[decode] {what}", flush=True)
     host = oracle_write(r, wl)
     ref = oracle_decode(r, wl, host, ppp)
-    got = gpu_decode(r, wl, cache_to_dev(r, host, 4), ppp)
+    got = gpu_decode(r, wl, cache_to_dev(r, host, hkv), ppp)
     assert_close(got, ref, what)
 
 
